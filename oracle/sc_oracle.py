@@ -1,0 +1,273 @@
+"""Plain float64 CPU oracle for the score-centering (SC) correction.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it, to check and to time the HIP
+library.  It shares no code, table or constant generator with the HIP path.
+
+Source of the method: "Score Centering" example page of Agent Lightning
+(microsoft.github.io/agent-lightning, section "Score Centering").  That section
+states, for one generated position:
+
+* the rollout records the top-K behaviour probabilities q over an id set H from
+  the sampling call, plus the sampled token a and its log-probability
+  separately; the recorded q may sum to less than one and a may lie outside H;
+* the trainer scores its own policy p over the whole vocabulary at the rollout
+  temperature and gathers p at H and at a;
+* with P_H = sum_H p_v, Q_H = sum_H q_v and
+  rho = max(1 - Q_H, 1e-6) / max(1 - P_H, 1e-6), the token loss is
+  -sg(A) * [log p_a - sum_H sg(q_v - rho p_v) log p_v];
+* the unrecorded behaviour tail is taken to be proportional to p;
+* the objective is unclipped, reduced over all generated tokens of the step,
+  with padding masked; group standard-deviation normalisation gives A
+  (same page, "Training" section);
+* rollout_corr/k3_kl is the masked mean of exp(d) - 1 - d with
+  d = train logprob - rollout logprob of the sampled token.
+
+Readings taken where the page is silent (each is listed in the design notes):
+
+* p is the trainer policy and q the recorded behaviour probabilities (the
+  gradient flows through log p_a; the tail is proportional to the "current
+  policy").
+* 1 - P_H is evaluated as the direct off-head sum tau = sum_{v not in H} p_v,
+  equal in exact arithmetic and free of cancellation.
+* The behaviour estimate is mu_hat_v = q_k on H and rho * p_v off H.
+* The centered score is the exact gradient of the bracket of the loss with
+  respect to the tempered logits u = z / T:
+  g = e_a - mu_hat - (1 - S) p, with S = sum_v mu_hat_v = Q_H + rho * tau.
+  It equals e_a - mu_hat whenever S = 1 (no clamp binds).
+* dLogits (gradient of the step loss sum_i loss_i / N_valid with respect to the
+  raw logits z) is -A / (T * N_valid) * g.
+* The correction is mu_hat - p.  TV is 1/2 sum_v |mu_hat_v - p_v| and KL is
+  KL(mu_hat || p) = sum_v mu_hat_v log(mu_hat_v / p_v), over the full
+  vocabulary, with 0 log 0 = 0.
+* The argmax is taken on the raw logits; ties go to the lowest index.
+* Data errors (id outside [0, V), duplicate id, sampled id outside [0, V),
+  a NaN or +inf logit, a -inf logit at a recorded or sampled id) make every
+  float output of the row NaN and its integer outputs -1.
+
+Group normalisation (same page, "Training" section: "group standard deviation
+normalization"; Agent Lightning v1.0.3 release note, section 4: rewards are not
+rounded to bf16 first and the denominator must not overflow): rewards are
+widened to float64; mode 0 divides by the unbiased standard deviation plus eps,
+mode 1 by the population standard deviation plus eps, mode 2 only subtracts the
+mean (the paper's mean-only setup the release note mentions).
+
+bf16 rounding: round to nearest, ties to even (lecture notes "RL systems for
+agents", section 4, where the cast is described).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# Clamp constant printed in the rho definition (Score Centering section).
+CLAMP = 1e-6
+
+# Data-error bits; same meaning as the library's device status bits.
+DEV_BAD_ID = 1
+DEV_DUP_ID = 2
+DEV_BAD_SAMPLED = 4
+DEV_NONFINITE = 8
+DEV_BAD_RESP = 16
+
+# Row output modes for the full-vocabulary row.
+MODE_DLOGITS = 0      # -A / (T * N_valid) * g
+MODE_SCORE = 1        # g, the centered score
+MODE_CORRECTION = 2   # mu_hat - p
+
+
+def trainer_log_softmax(z, temperature):
+    """log p over the full vocabulary at the rollout temperature.
+
+    Score Centering section: the trainer scores the current policy over the
+    full model vocabulary at the rollout temperature.  Returns (log p, lse)
+    with lse = logsumexp(z / T) in float64.
+    """
+    u = np.asarray(z, dtype=np.float64) / float(temperature)
+    m = np.max(u)
+    s = np.sum(np.exp(u - m))
+    lse = m + math.log(s)
+    return u - lse, lse
+
+
+def _row_flags(z, head_ids, sampled):
+    """Data-error bits of one row (see the module docstring)."""
+    V = z.shape[0]
+    flags = 0
+    ids = np.asarray(head_ids, dtype=np.int64)
+    in_range = (ids >= 0) & (ids < V)
+    if not np.all(in_range):
+        flags |= DEV_BAD_ID
+    good = ids[in_range]
+    if np.unique(good).size != good.size:
+        flags |= DEV_DUP_ID
+    a_ok = 0 <= int(sampled) < V
+    if not a_ok:
+        flags |= DEV_BAD_SAMPLED
+    if np.any(np.isnan(z)) or np.any(np.isposinf(z)):
+        flags |= DEV_NONFINITE
+    elif np.all(np.isneginf(z)):
+        flags |= DEV_NONFINITE
+    else:
+        if np.any(np.isneginf(z[good])):
+            flags |= DEV_NONFINITE
+        if a_ok and np.isneginf(z[int(sampled)]):
+            flags |= DEV_NONFINITE
+    return flags
+
+
+def sc_row(z, temperature, head_ids, head_probs, sampled, rollout_logp=None,
+           advantage=1.0, n_valid=1, row_mode=MODE_DLOGITS):
+    """All per-position SC outputs of one valid row, by definition, in float64.
+
+    Arguments: z (V,) logits (any float dtype, widened exactly), temperature T,
+    head_ids (K,) recorded ids H, head_probs (K,) recorded probabilities q,
+    sampled id a, rollout_logp = log mu(a) recorded by the rollout (or None),
+    advantage A of the row's response, n_valid = number of valid positions of
+    the whole step, row_mode selecting the full-vocabulary row to return.
+
+    Returns a dict; see the keys at the end.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    V = z.shape[0]
+    ids = np.asarray(head_ids, dtype=np.int64)
+    q = np.asarray(head_probs, dtype=np.float64)
+    K = ids.shape[0]
+    a = int(sampled)
+    T = float(temperature)
+
+    flags = _row_flags(z, ids, a)
+    if flags:
+        nan = float("nan")
+        return dict(flags=flags, lse=nan, logp_a=nan, argmax=-1, a_slot=-1,
+                    head_logp=np.full(K, nan), P_H=nan, Q_H=nan, tau=nan,
+                    rho=nan, coef=np.full(K, nan), S=nan, loss=nan, tv=nan,
+                    kl=nan, k3=nan, row=np.full(V, nan))
+
+    # Trainer softmax at the rollout temperature; gather at H and at a.
+    logp, lse = trainer_log_softmax(z, T)
+    p = np.exp(logp)
+    argmax = int(np.argmax(z))          # numpy returns the first maximum
+    logp_a = logp[a]
+    head_logp = logp[ids]
+    p_H = p[ids]
+    hits = np.nonzero(ids == a)[0]
+    a_slot = int(hits[0]) if hits.size else -1
+
+    # Masses: P_H, Q_H and the off-head trainer mass tau (= 1 - P_H exactly).
+    in_H = np.zeros(V, dtype=bool)
+    in_H[ids] = True
+    P_H = float(np.sum(p_H))
+    Q_H = float(np.sum(q))
+    tau = float(np.sum(p[~in_H]))
+
+    # rho with both clamps, as printed.
+    rho = max(1.0 - Q_H, CLAMP) / max(tau, CLAMP)
+
+    # Stop-gradient coefficients and the token loss.
+    coef = q - rho * p_H
+    loss = -float(advantage) * (logp_a - float(np.sum(coef * head_logp)))
+
+    # Behaviour estimate mu_hat: recorded head, tail proportional to p.
+    mu_hat = rho * p
+    mu_hat[ids] = q
+    S = float(np.sum(mu_hat))
+
+    # Centered score: gradient of the bracket with respect to u = z / T.
+    g = -mu_hat - (1.0 - S) * p
+    g[a] += 1.0
+
+    if row_mode == MODE_DLOGITS:
+        row = (-float(advantage) / (T * float(n_valid))) * g
+    elif row_mode == MODE_SCORE:
+        row = g
+    elif row_mode == MODE_CORRECTION:
+        row = mu_hat - p
+    else:
+        raise ValueError("row_mode")
+
+    # Diagnostics over the full vocabulary.
+    tv = 0.5 * float(np.sum(np.abs(mu_hat - p)))
+    pos = mu_hat > 0
+    kl = float(np.sum(mu_hat[pos] * (np.log(mu_hat[pos]) - logp[pos])))
+    if rollout_logp is None:
+        k3 = float("nan")
+    else:
+        d = logp_a - float(rollout_logp)
+        k3 = math.expm1(d) - d
+
+    return dict(flags=0, lse=lse, logp_a=logp_a, argmax=argmax, a_slot=a_slot,
+                head_logp=head_logp, P_H=P_H, Q_H=Q_H, tau=tau, rho=rho,
+                coef=coef, S=S, loss=loss, tv=tv, kl=kl, k3=k3, row=row)
+
+
+def masked_row(V, K):
+    """Outputs of a padding row: nothing read, zero loss and gradient."""
+    return dict(flags=0, lse=0.0, logp_a=0.0, argmax=-1, a_slot=-1,
+                head_logp=np.zeros(K), P_H=0.0, Q_H=0.0, tau=0.0, rho=0.0,
+                coef=np.zeros(K), S=0.0, loss=0.0, tv=0.0, kl=0.0, k3=0.0,
+                row=np.zeros(V))
+
+
+def group_norm(rewards, group_size, mode=0, eps=1e-6):
+    """Rollout-level advantages by group normalisation, in float64.
+
+    Groups are consecutive runs of group_size responses.  mode 0: unbiased
+    standard deviation, mode 1: population standard deviation, mode 2: mean
+    only.  A group of one response gets advantage 0.
+    """
+    r = np.asarray(rewards, dtype=np.float64).reshape(-1, group_size)
+    out = np.zeros_like(r)
+    G = group_size
+    for j in range(r.shape[0]):
+        mean = sum(float(x) for x in r[j]) / G
+        dev = [float(x) - mean for x in r[j]]
+        if mode == 2:
+            out[j] = dev
+            continue
+        if G == 1:
+            out[j] = 0.0
+            continue
+        ss = sum(d * d for d in dev)
+        std = math.sqrt(ss / (G - 1 if mode == 0 else G))
+        out[j] = [d / (std + eps) for d in dev]
+    return out.reshape(-1)
+
+
+def batch_sums(rows, n_valid):
+    """Step-level reductions over valid rows (global generated-token mean).
+
+    rows: iterable of sc_row() dicts of the valid rows.  Returns the sums and
+    the means over n_valid, in float64: loss, k3, tv, kl, Q_H, P_H.
+    """
+    keys = ("loss", "k3", "tv", "kl", "Q_H", "P_H")
+    sums = {k: 0.0 for k in keys}
+    for r in rows:
+        for k in keys:
+            sums[k] += float(r[k])
+    means = {k: sums[k] / float(n_valid) for k in keys}
+    return sums, means
+
+
+def bf16_rne(x):
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bf16 keeps 8 significant bits and float32's exponent range (subnormal
+    spacing 2^-133).  Values beyond the largest finite bf16 after rounding
+    become infinities.  Returned as float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, copy=True)
+    fin = np.isfinite(x) & (x != 0)
+    xf = x[fin]
+    m, e = np.frexp(np.abs(xf))                 # |x| = m * 2^e, m in [0.5, 1)
+    ulp_exp = np.maximum(e - 8, -133)           # spacing of 8 significant bits
+    scaled = np.ldexp(np.abs(xf), -ulp_exp)     # exact (power-of-two scaling)
+    r = np.rint(scaled)                         # round half to even
+    mag = np.ldexp(r, ulp_exp)
+    max_bf16 = float(np.ldexp(255.0, 127 - 7))  # (2 - 2^-7) * 2^127
+    mag = np.where(mag > max_bf16, np.inf, mag)
+    out[fin] = np.sign(xf) * mag
+    return out

@@ -1,0 +1,426 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Each test fixes the oracle to something independent of its own code: values
+derived by hand in closed form, autograd of the printed loss, brute force over
+tiny vocabularies, library routines in special cases, invariants, and the
+numbers printed on the pages (bf16 facts, the 1.0 vs 1.001 reward case).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sc_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+LN = math.log
+P4 = np.array([0.1, 0.2, 0.3, 0.4])
+Z4 = np.log(np.array([1.0, 2.0, 3.0, 4.0]))   # softmax(Z4) = P4, lse = ln 10
+
+
+# --------------------------------------------------------------------------
+# Hand-derived cases (V = 4, p = [0.1, 0.2, 0.3, 0.4]).  Derivations follow
+# the Score Centering section: P_H, Q_H, rho with clamps, c = q - rho p,
+# loss = -A [log p_a - sum_H c log p], tail proportional to p.
+# --------------------------------------------------------------------------
+def _close(a, b, tol=1e-12):
+    np.testing.assert_allclose(np.asarray(a, float), np.asarray(b, float),
+                               rtol=0, atol=tol)
+
+
+def test_hand_case_rho_one():
+    # H = [3, 1], q = [0.5, 0.1], a = 2 (outside H).
+    # P_H = 0.4 + 0.2 = 0.6, Q_H = 0.6, tau = 0.4, rho = 0.4 / 0.4 = 1.
+    # c = [0.5 - 0.4, 0.1 - 0.2] = [0.1, -0.1];  mu_hat = [0.1, 0.1, 0.3, 0.5].
+    # loss = -[ln .3 - (0.1 ln .4 - 0.1 ln .2)] = -ln .3 + 0.1 ln 2.
+    # g = e_2 - mu_hat = [-0.1, -0.1, 0.7, -0.5];  dlogits(A=1,T=1,N=1) = -g.
+    # TV = (0.1 + 0.1) / 2 = 0.1;  KL = 0.5 ln(0.5/0.4) + 0.1 ln(0.1/0.2).
+    r = O.sc_row(Z4, 1.0, [3, 1], [0.5, 0.1], 2, rollout_logp=LN(0.15))
+    _close(r["lse"], LN(10.0))
+    _close(r["logp_a"], LN(0.3))
+    _close(r["head_logp"], [LN(0.4), LN(0.2)])
+    assert r["argmax"] == 3 and r["a_slot"] == -1
+    _close([r["P_H"], r["Q_H"], r["tau"], r["rho"], r["S"]],
+           [0.6, 0.6, 0.4, 1.0, 1.0])
+    _close(r["coef"], [0.1, -0.1])
+    _close(r["loss"], -LN(0.3) + 0.1 * LN(2.0))
+    _close(r["row"], [0.1, 0.1, -0.7, 0.5])
+    _close(r["tv"], 0.1)
+    _close(r["kl"], 0.5 * LN(1.25) - 0.1 * LN(2.0))
+    # K3 with d = ln .3 - ln .15 = ln 2:  e^d - 1 - d = 1 - ln 2.
+    _close(r["k3"], 1.0 - LN(2.0))
+    corr = O.sc_row(Z4, 1.0, [3, 1], [0.5, 0.1], 2,
+                    row_mode=O.MODE_CORRECTION)["row"]
+    _close(corr, [0.0, -0.1, 0.0, 0.1])
+
+
+def test_hand_case_rho_half():
+    # q = [0.6, 0.2]: Q_H = 0.8, rho = 0.2 / 0.4 = 0.5,
+    # c = [0.6 - 0.2, 0.2 - 0.1] = [0.4, 0.1], mu_hat = [.05, .2, .15, .6].
+    # loss = -[ln .3 - 0.4 ln .4 - 0.1 ln .2];  g = [-.05, -.2, .85, -.6].
+    # TV = (0.2 + 0 + |0.5 - 1| * 0.4) / 2 = 0.2;
+    # KL = 0.6 ln 1.5 + 0.2 ln 1 + 0.05 ln 0.5 + 0.15 ln 0.5.
+    r = O.sc_row(Z4, 1.0, [3, 1], [0.6, 0.2], 2, row_mode=O.MODE_SCORE)
+    _close(r["rho"], 0.5)
+    _close(r["coef"], [0.4, 0.1])
+    _close(r["loss"], -(LN(0.3) - 0.4 * LN(0.4) - 0.1 * LN(0.2)))
+    _close(r["row"], [-0.05, -0.2, 0.85, -0.6])
+    _close(r["tv"], 0.2)
+    _close(r["kl"], 0.6 * LN(1.5) - 0.2 * LN(2.0))
+
+
+def test_hand_case_sampled_in_head():
+    # a = 1 = H[1]: a_slot = 1, logp_a = ln .2,
+    # loss = -[ln .2 - 0.1 ln .4 + 0.1 ln .2];  g = e_1 - [.1, .1, .3, .5].
+    r = O.sc_row(Z4, 1.0, [3, 1], [0.5, 0.1], 1, row_mode=O.MODE_SCORE)
+    assert r["a_slot"] == 1
+    _close(r["loss"], -(LN(0.2) - 0.1 * LN(0.4) + 0.1 * LN(0.2)))
+    _close(r["row"], [-0.1, 0.9, -0.3, -0.5])
+
+
+def test_hand_case_numerator_clamp():
+    # q = [0.7, 0.3] sums to 1: max(1 - Q_H, 1e-6) = 1e-6, tau = 0.4,
+    # rho = 2.5e-6, S = Q_H + rho tau = 1 + 1e-6.
+    # g = e_a - mu_hat - (1 - S) p = e_2 - [2.5e-7, .3, 7.5e-7, .7] + 1e-6 p.
+    r = O.sc_row(Z4, 1.0, [3, 1], [0.7, 0.3], 2, row_mode=O.MODE_SCORE)
+    _close(r["rho"], 2.5e-6, 1e-18)
+    _close(r["S"], 1.0 + 1e-6, 1e-15)
+    _close(r["coef"], [0.7 - 1e-6, 0.3 - 5e-7], 1e-15)
+    _close(r["row"], [-2.5e-7 + 1e-7, -0.3 + 2e-7, 1 - 7.5e-7 + 3e-7,
+                      -0.7 + 4e-7], 1e-15)
+
+
+def test_hand_case_full_head_matching():
+    # K = V with q = p: 1 - Q_H = 0 and tau = 0, both clamp to 1e-6, rho = 1,
+    # c = 0, mu_hat = p, correction 0, g = e_a - p, TV = KL = 0.
+    r = O.sc_row(Z4, 1.0, [0, 1, 2, 3], P4, 0, row_mode=O.MODE_SCORE)
+    _close(r["rho"], 1.0, 1e-9)
+    _close(r["coef"], np.zeros(4), 1e-15)
+    _close(r["row"], [0.9, -0.2, -0.3, -0.4], 1e-15)
+    _close([r["tv"], r["kl"]], [0.0, 0.0], 1e-15)
+    corr = O.sc_row(Z4, 1.0, [0, 1, 2, 3], P4, 0,
+                    row_mode=O.MODE_CORRECTION)["row"]
+    _close(corr, np.zeros(4), 1e-15)
+
+
+def test_hand_case_temperature_and_scaling():
+    # z = 0.5 ln k at T = 0.5 gives the same p.  With A = -1, N_valid = 4:
+    # dlogits = -A / (T N) g = 0.5 g, g as in the rho = 0.5 case; loss flips.
+    r = O.sc_row(0.5 * Z4, 0.5, [3, 1], [0.6, 0.2], 2, advantage=-1.0,
+                 n_valid=4)
+    _close(r["lse"], LN(10.0))
+    _close(r["loss"], LN(0.3) - 0.4 * LN(0.4) - 0.1 * LN(0.2))
+    _close(r["row"], 0.5 * np.array([-0.05, -0.2, 0.85, -0.6]))
+
+
+# --------------------------------------------------------------------------
+# Autograd of the printed token loss (torch, float64)
+# --------------------------------------------------------------------------
+def _printed_loss(z, T, ids, q, a, A, n_valid):
+    """-sg(A) [log p_a - sum_H sg(q - rho p) log p] / N_valid at temperature T,
+    written from the Score Centering section with detach() as sg."""
+    logp = torch.log_softmax(z / T, dim=0)
+    p = logp.exp()
+    P_H = p[ids].sum()
+    Q_H = q.sum()
+    rho = torch.clamp(1 - Q_H, min=1e-6) / torch.clamp(1 - P_H, min=1e-6)
+    c = (q - rho * p[ids]).detach()
+    return -A * (logp[a] - (c * logp[ids]).sum()) / n_valid
+
+
+def _rand_case(rng, V, K, clamp=None):
+    z = rng.normal(0, 2.0, V)
+    ids = rng.choice(V, K, replace=False)
+    p = np.exp(z - z.max()); p /= p.sum()
+    if clamp == "tail":          # trainer tail below 1e-6, recorded head short
+        z = rng.normal(0, 1.0, V)
+        z[ids] += 30.0
+        q = rng.dirichlet(np.ones(K)) * 0.9
+    elif clamp == "head":        # recorded head sums to >= 1
+        q = rng.dirichlet(np.ones(K)) * (1 + 1e-7)
+    else:
+        q = rng.dirichlet(np.ones(K)) * rng.uniform(0.3, 0.99)
+    a = int(rng.integers(V))
+    return z, ids, q, a
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7])
+@pytest.mark.parametrize("clamp", [None, "tail", "head"])
+def test_dlogits_equal_autograd_of_printed_loss(T, clamp):
+    rng = np.random.default_rng(123)
+    for V in (8, 16, 32):
+        for trial in range(20):
+            K = int(rng.integers(1, V))
+            z, ids, q, a = _rand_case(rng, V, K, clamp)
+            A = float(rng.normal())
+            n_valid = int(rng.integers(1, 50))
+            zt = torch.tensor(z, dtype=torch.float64, requires_grad=True)
+            loss = _printed_loss(zt, T, torch.tensor(ids), torch.tensor(q), a,
+                                 A, n_valid)
+            loss.backward()
+            r = O.sc_row(z, T, ids, q, a, advantage=A, n_valid=n_valid)
+            np.testing.assert_allclose(r["row"], zt.grad.numpy(), rtol=1e-9,
+                                       atol=1e-11)
+            np.testing.assert_allclose(r["loss"] / n_valid, loss.item(),
+                                       rtol=1e-10, atol=1e-10)
+
+
+def test_clamp_reading_differs_from_plain_centering():
+    # When tau < 1e-6 and 1 - Q_H >> 1e-6, S != 1 and the exact gradient
+    # e_a - mu_hat - (1 - S) p differs from e_a - mu_hat by (1 - S) p.
+    rng = np.random.default_rng(5)
+    z, ids, q, a = _rand_case(rng, 16, 4, "tail")
+    r = O.sc_row(z, 1.0, ids, q, a, row_mode=O.MODE_SCORE)
+    assert r["tau"] < 1e-6 and r["S"] < 0.95
+    logp, _ = O.trainer_log_softmax(z, 1.0)
+    p = np.exp(logp)
+    corr = O.sc_row(z, 1.0, ids, q, a, row_mode=O.MODE_CORRECTION)["row"]
+    plain = np.eye(16)[a] - (corr + p)
+    np.testing.assert_allclose(plain - r["row"], (1 - r["S"]) * p, atol=1e-12)
+    assert np.abs(plain - r["row"]).max() > 0.01
+
+
+# --------------------------------------------------------------------------
+# Brute force: centering removes the mean update when the tail really is
+# proportional to p (release note, section 1: "removes average update bias")
+# --------------------------------------------------------------------------
+def test_centering_identity_brute_force():
+    rng = np.random.default_rng(7)
+    for V in (4, 8, 16):
+        for trial in range(50):
+            K = int(rng.integers(1, V))
+            z = rng.normal(0, 1.5, V)
+            p = np.exp(z - z.max()); p /= p.sum()
+            ids = rng.choice(V, K, replace=False)
+            in_H = np.zeros(V, bool); in_H[ids] = True
+            # a behaviour policy: arbitrary head mass, tail exactly prop. to p
+            q = rng.dirichlet(np.ones(K)) * rng.uniform(0.2, 0.95)
+            mu = np.zeros(V)
+            mu[ids] = q
+            mu[~in_H] = (1 - q.sum()) * p[~in_H] / p[~in_H].sum()
+            assert abs(mu.sum() - 1) < 1e-12
+            expected = np.zeros(V)
+            for a in range(V):
+                r = O.sc_row(z, 1.0, ids, q, a, row_mode=O.MODE_SCORE)
+                expected += mu[a] * r["row"]
+                corr = O.sc_row(z, 1.0, ids, q, a,
+                                row_mode=O.MODE_CORRECTION)["row"]
+                np.testing.assert_allclose(corr, mu - p, atol=1e-13)
+            np.testing.assert_allclose(expected, 0.0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Special cases that reduce to library routines
+# --------------------------------------------------------------------------
+def test_log_softmax_and_lse_match_torch():
+    rng = np.random.default_rng(1)
+    for T in (1.0, 0.7, 2.5):
+        z = rng.normal(0, 3, 1000)
+        logp, lse = O.trainer_log_softmax(z, T)
+        zt = torch.tensor(z, dtype=torch.float64) / T
+        np.testing.assert_allclose(logp, torch.log_softmax(zt, 0).numpy(),
+                                   atol=1e-12)
+        assert abs(lse - torch.logsumexp(zt, 0).item()) < 1e-12
+
+
+def test_identical_distributions_give_cross_entropy_gradient():
+    # q = p on H: rho = 1, mu_hat = p, correction 0 and the SC gradient is
+    # A / N_valid times the cross-entropy gradient (torch autograd).
+    rng = np.random.default_rng(2)
+    V, K, T = 64, 10, 0.8
+    for trial in range(10):
+        z = rng.normal(0, 2, V)
+        logp, _ = O.trainer_log_softmax(z, T)
+        ids = rng.choice(V, K, replace=False)
+        q = np.exp(logp[ids])
+        a = int(rng.integers(V))
+        A, n_valid = float(rng.normal()), 7
+        r = O.sc_row(z, T, ids, q, a, advantage=A, n_valid=n_valid)
+        assert abs(r["rho"] - 1) < 1e-12
+        _close(r["coef"], np.zeros(K), 1e-13)
+        zt = torch.tensor(z, dtype=torch.float64, requires_grad=True)
+        torch.nn.functional.cross_entropy((zt / T)[None], torch.tensor([a])
+                                          ).backward()
+        np.testing.assert_allclose(r["row"], A / n_valid * zt.grad.numpy(),
+                                   atol=1e-13)
+        corr = O.sc_row(z, T, ids, q, a, row_mode=O.MODE_CORRECTION)["row"]
+        _close(corr, np.zeros(V), 1e-13)
+        assert r["tv"] < 1e-13 and abs(r["kl"]) < 1e-13
+
+
+def test_argmax_lowest_index_on_ties():
+    z = np.array([0.0, 3.0, -1.0, 3.0, 3.0, 2.0])
+    r = O.sc_row(z, 1.0, [5], [0.1], 0)
+    assert r["argmax"] == 1
+
+
+# --------------------------------------------------------------------------
+# Invariants
+# --------------------------------------------------------------------------
+def test_invariants_random_rows():
+    rng = np.random.default_rng(3)
+    for trial in range(200):
+        V = int(rng.integers(2, 300))
+        K = int(rng.integers(1, V + 1))
+        clamp = rng.choice([None, "tail", "head"])
+        z, ids, q, a = _rand_case(rng, V, K, clamp)
+        r = O.sc_row(z, 1.0, ids, q, a, row_mode=O.MODE_SCORE)
+        logp, _ = O.trainer_log_softmax(z, 1.0)
+        p = np.exp(logp)
+        assert abs(r["P_H"] + r["tau"] - 1) < 1e-12
+        assert abs(r["P_H"] - p[ids].sum()) < 1e-12
+        # the gradient of any log-softmax loss sums to zero over the vocabulary
+        assert abs(r["row"].sum()) < 1e-12
+        # S = Q_H + rho tau, and S = 1 when no clamp binds
+        assert abs(r["S"] - (r["Q_H"] + r["rho"] * r["tau"])) < 1e-12
+        if 1 - r["Q_H"] >= 1e-6 and r["tau"] >= 1e-6:
+            assert abs(r["S"] - 1) < 1e-12
+        # TV in [0, 1] when S = 1; equals sum max(0, p - mu_hat) then
+        # (lecture notes, exercise 2 and its solution)
+        corr = O.sc_row(z, 1.0, ids, q, a, row_mode=O.MODE_CORRECTION)["row"]
+        mu_hat = corr + p
+        if abs(r["S"] - 1) < 1e-12:
+            assert abs(r["tv"] - np.maximum(0, p - mu_hat).sum()) < 1e-12
+        # closed forms of TV and KL(mu_hat || p): the tail is prop. to p
+        in_H = np.zeros(V, bool); in_H[ids] = True
+        tv_cf = 0.5 * (np.abs(q - p[ids]).sum() + abs(r["rho"] - 1) * r["tau"])
+        qpos = q > 0
+        kl_cf = (q[qpos] * (np.log(q[qpos]) - logp[ids][qpos])).sum()
+        if r["rho"] * r["tau"] > 0:
+            kl_cf += r["rho"] * r["tau"] * math.log(r["rho"])
+        assert abs(r["tv"] - tv_cf) < 1e-12
+        assert abs(r["kl"] - kl_cf) < 1e-10 * max(1, abs(kl_cf))
+
+
+def test_k3_properties():
+    # rollout_corr/k3_kl term exp(d) - 1 - d (Score Centering section):
+    # >= 0, zero iff d = 0, e - 2 at d = 1, ~ d^2 / 2 for small d.
+    z = np.log(np.array([1.0, 2.0, 3.0, 4.0]))
+    for d in (-3.0, -0.5, 1e-4, 0.0, 1.0, 2.0):
+        r = O.sc_row(z, 1.0, [3], [0.4], 2, rollout_logp=LN(0.3) - d)
+        assert r["k3"] >= 0
+        if d == 0:
+            assert r["k3"] == 0
+        if d == 1.0:
+            _close(r["k3"], math.e - 2)
+        if d == 1e-4:
+            _close(r["k3"], d * d / 2, 1e-12)
+
+
+# --------------------------------------------------------------------------
+# Data errors and padding
+# --------------------------------------------------------------------------
+def test_data_error_flags():
+    z = np.zeros(8)
+    assert O.sc_row(z, 1.0, [1, 9], [.1, .1], 0)["flags"] == O.DEV_BAD_ID
+    assert O.sc_row(z, 1.0, [1, 1], [.1, .1], 0)["flags"] == O.DEV_DUP_ID
+    assert O.sc_row(z, 1.0, [1, 2], [.1, .1], 8)["flags"] == O.DEV_BAD_SAMPLED
+    zn = z.copy(); zn[5] = np.nan
+    r = O.sc_row(zn, 1.0, [1, 2], [.1, .1], 0)
+    assert r["flags"] == O.DEV_NONFINITE and np.isnan(r["loss"])
+    zi = z.copy(); zi[2] = -np.inf
+    assert O.sc_row(zi, 1.0, [1, 2], [.1, .1], 0)["flags"] == O.DEV_NONFINITE
+    # -inf outside H and a is a legal masked vocabulary entry (p = 0)
+    r = O.sc_row(zi, 1.0, [1, 3], [.1, .1], 0)
+    assert r["flags"] == 0 and np.isfinite(r["loss"]) and r["row"][2] == 0
+
+
+# --------------------------------------------------------------------------
+# Group normalisation
+# --------------------------------------------------------------------------
+def test_group_norm_hand_cases():
+    # R = [1, 0, 0, 0]: mean 0.25, unbiased std sqrt(0.75 / 3) = 0.5.
+    A = O.group_norm([1, 0, 0, 0], 4, mode=0, eps=0.0)
+    _close(A, [1.5, -0.5, -0.5, -0.5])
+    # population std sqrt(0.75 / 4) = sqrt(3) / 4: A_1 = 0.75 / (sqrt 3 / 4).
+    A = O.group_norm([1, 0, 0, 0], 4, mode=1, eps=0.0)
+    _close(A[0], math.sqrt(3.0))
+    _close(O.group_norm([1, 0, 0, 0], 4, mode=2), [0.75, -.25, -.25, -.25])
+    # zero-variance groups and single-response groups give exactly 0
+    assert np.all(O.group_norm([0.3] * 8, 4) == 0)
+    assert np.all(O.group_norm([1.0, 0.0, 5.0], 1) == 0)
+
+
+def test_group_norm_matches_statistics_module():
+    import statistics
+    rng = np.random.default_rng(4)
+    for G in (2, 4, 8):
+        r = rng.random(G * 6).astype(np.float32)
+        A = O.group_norm(r, G, mode=0, eps=1e-6)
+        for j in range(6):
+            g = [float(x) for x in r[j * G:(j + 1) * G]]
+            m, s = statistics.fmean(g), statistics.stdev(g)
+            _close(A[j * G:(j + 1) * G], [(x - m) / (s + 1e-6) for x in g],
+                   1e-12)
+
+
+def test_group_norm_keeps_fractional_rewards_and_large_values():
+    # Release note, section 4: 1.0 and 1.001 stay distinct (no bf16 cast);
+    # the normaliser must not overflow for large rewards.
+    A = O.group_norm(np.array([1.0, 1.001, 1.0, 1.001], np.float32), 4)
+    assert A[0] < 0 < A[1] and abs(A[0] + A[1]) < 1e-9
+    big = np.array([1e30, -1e30, 3e29, 0.0], np.float32)
+    A = O.group_norm(big, 4)
+    assert np.all(np.isfinite(A)) and abs(A.sum()) < 1e-9
+
+
+def test_batch_sums_global_token_mean():
+    rows = [dict(loss=1.0, k3=0.1, tv=0.2, kl=0.3, Q_H=0.9, P_H=0.8),
+            dict(loss=3.0, k3=0.3, tv=0.4, kl=0.5, Q_H=0.7, P_H=0.6)]
+    sums, means = O.batch_sums(rows, 4)
+    _close([sums["loss"], means["loss"], means["Q_H"]], [4.0, 1.0, 0.4])
+
+
+# --------------------------------------------------------------------------
+# bf16 round-to-nearest-even
+# --------------------------------------------------------------------------
+def test_bf16_page_facts():
+    with open(os.path.join(GOLDEN, "bf16_page_facts.json")) as f:
+        facts = json.load(f)
+    for fact in facts["facts"]:
+        got = O.bf16_rne(fact["x"])
+        if "expect" in fact:
+            assert got == fact["expect"], fact["what"]
+        else:
+            assert got == O.bf16_rne(fact["same_as"]), fact["what"]
+    for case in facts["step_counts"]:
+        v = O.bf16_rne(case["start"])
+        master, steps = case["start"], 0
+        while O.bf16_rne(master) == v:
+            master += case["step"]
+            steps += 1
+        assert steps == case["steps"], case["what"]
+
+
+def test_bf16_matches_torch_rne_on_float32_values():
+    rng = np.random.default_rng(9)
+    x = np.concatenate([
+        rng.normal(0, 1, 20000), rng.normal(0, 1e-30, 2000),
+        np.ldexp(rng.normal(0, 1, 2000), -130),   # bf16 subnormal range
+        [1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 3.3e38, 3.4e38, 0.0],
+    ]).astype(np.float32)
+    ref = torch.tensor(x).to(torch.bfloat16).double().numpy()
+    got = O.bf16_rne(x.astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
+    # ties go to the even neighbour
+    assert O.bf16_rne(1 + 2 ** -8) == 1.0
+    assert O.bf16_rne(1 + 3 * 2 ** -8) == 1 + 2 ** -6
+
+
+# --------------------------------------------------------------------------
+# Generator sanity (the inputs the oracle is fed look like the pages' record)
+# --------------------------------------------------------------------------
+def test_tiny_generator_shapes_and_record():
+    from synthetic import tiny
+    d = tiny(seed=0)
+    n, V = d["logits"].shape
+    assert (n, V) == (256, 4096) and d["head_ids"].shape == (256, 128)
+    for i in range(0, 256, 37):
+        assert len(set(d["head_ids"][i])) == 128
+        assert 0.0 < d["head_probs"][i].sum() <= 1.0 + 1e-6
+        assert np.all(np.diff(d["head_probs"][i]) <= 0)
+    assert d["rewards"].shape == (32,)
