@@ -1,0 +1,240 @@
+/*
+ * sc.h -- C ABI of the score-centering (SC) correction library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method: "Score Centering" example page of Agent Lightning
+ * (microsoft.github.io/agent-lightning), section "Score Centering".  For each
+ * generated position the rollout recorded the top-K candidate ids H with their
+ * behaviour probabilities q, plus the sampled token a and its log-probability.
+ * The trainer scores its policy p over the full vocabulary at the rollout
+ * temperature T, gathers p at H and at a, sets P_H = sum_H p, Q_H = sum_H q,
+ * rho = max(1 - Q_H, 1e-6) / max(1 - P_H, 1e-6), and trains on the token loss
+ * -sg(A) [log p_a - sum_H sg(q_v - rho p_v) log p_v], the unrecorded tail of
+ * the behaviour policy being taken proportional to p.  Advantages come from
+ * group standard-deviation normalisation of the rewards (same page, section
+ * "Training"), the loss is reduced over all generated tokens of the step with
+ * padding masked, and rollout_corr/k3_kl is the masked mean of
+ * exp(d) - 1 - d with d = train logprob - rollout logprob.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named as device pointers address GPU memory owned by the caller.
+ *   The library allocates nothing and keeps no state besides a cached query of
+ *   the device's compute-unit count.
+ * - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
+ *   stream) and never synchronises.  Calls are thread-safe.
+ * - Argument errors are returned as a negative sc_status BEFORE any HIP call is
+ *   made, so they can be exercised on a host without a GPU.  A failed kernel
+ *   launch returns SC_ERR_HIP.  No exception crosses the ABI.
+ * - Data errors found on the device (see SC_DEV_*) are OR-ed into the optional
+ *   `dev_status` word; every float output of the affected row is then NaN,
+ *   its integer outputs are -1 and its full-vocabulary output row is NaN.
+ * - Padding rows (resp_idx < 0) are never read: their outputs are 0, their
+ *   integer outputs -1 and their full-vocabulary output row is all zero.
+ * - Per-id outputs keep the caller's slot order of head_ids.
+ * - Logits rows: `row_stride` elements apart, row_stride >= vocab.  The
+ *   16-byte vector path is taken when the logits pointer is 16-byte aligned
+ *   and row_stride * element size is a multiple of 16; otherwise a scalar path
+ *   gives the same results.
+ * - Preconditions checked on the host: 1 <= k <= min(vocab, 1024),
+ *   1 <= vocab < 2^31, 0 <= n_rows < 2^31, temperature finite and > 0.
+ */
+#ifndef SC_H
+#define SC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+enum sc_status {
+  SC_OK = 0,
+  SC_ERR_ARG = -1,          /* invalid argument (checked before any HIP call) */
+  SC_ERR_UNSUPPORTED = -2,  /* valid but outside what this build supports      */
+  SC_ERR_HIP = -3           /* a HIP runtime call or kernel launch failed       */
+};
+
+/* Element types of logits and of the full-vocabulary output row. */
+enum sc_dtype { SC_F32 = 0, SC_BF16 = 1 };
+
+/* Device data-error bits OR-ed into *dev_status. */
+enum sc_dev_flag {
+  SC_DEV_BAD_ID = 1,       /* a head id outside [0, vocab)                     */
+  SC_DEV_DUP_ID = 2,       /* the same id recorded twice in one row            */
+  SC_DEV_BAD_SAMPLED = 4,  /* sampled id outside [0, vocab)                    */
+  SC_DEV_NONFINITE = 8,    /* NaN or +inf logit, -inf at a head or sampled id  */
+  SC_DEV_BAD_RESP = 16     /* resp_idx >= n_responses                          */
+};
+
+/* Full-vocabulary output row selected by `row_mode`. */
+enum sc_row_mode {
+  SC_ROW_DLOGITS = 0,    /* d(step loss)/dz = -A / (T * N_valid) * g          */
+  SC_ROW_SCORE = 1,      /* centered score g = e_a - mu_hat - (1 - S) p       */
+  SC_ROW_CORRECTION = 2  /* correction mu_hat - p                             */
+};
+
+/* Columns of the per-row statistics array row_stats[n_rows][SC_NSTATS]. */
+enum sc_stat {
+  SC_STAT_LSE = 0,     /* log sum_v exp(z_v / T)                               */
+  SC_STAT_LOGP_A = 1,  /* log p(a) of the sampled token                        */
+  SC_STAT_TAIL = 2,    /* tau = sum of p over ids outside H (= 1 - P_H)        */
+  SC_STAT_P_H = 3,     /* trainer mass on the recorded ids                     */
+  SC_STAT_Q_H = 4,     /* recorded behaviour mass (coverage)                   */
+  SC_STAT_RHO = 5,     /* tail scale rho, both clamps applied                  */
+  SC_STAT_S = 6,       /* sum of mu_hat = Q_H + rho * tau                      */
+  SC_STAT_LOSS = 7,    /* token loss -A [log p_a - sum_H c log p]              */
+  SC_STAT_TV = 8,      /* 1/2 sum_v |mu_hat_v - p_v|                           */
+  SC_STAT_KL = 9,      /* KL(mu_hat || p)                                      */
+  SC_STAT_K3 = 10,     /* exp(d) - 1 - d, d = log p(a) - rollout log mu(a)     */
+  SC_STAT_RESERVED = 11,
+  SC_NSTATS = 12
+};
+
+/* Columns of the per-row integer array row_idx[n_rows][2]. */
+enum sc_idx { SC_IDX_ARGMAX = 0, SC_IDX_A_SLOT = 1, SC_NIDX = 2 };
+
+/* Sums and means written by sc_batch_sums, batch[SC_NBATCH] (float64). */
+enum sc_batch {
+  SC_SUM_LOSS = 0, SC_SUM_K3 = 1, SC_SUM_TV = 2, SC_SUM_KL = 3,
+  SC_SUM_Q_H = 4, SC_SUM_P_H = 5, SC_SUM_ROWS = 6, SC_SUM_FLAGGED = 7,
+  SC_MEAN_LOSS = 8, SC_MEAN_K3 = 9, SC_MEAN_TV = 10, SC_MEAN_KL = 11,
+  SC_MEAN_Q_H = 12, SC_MEAN_P_H = 13,
+  SC_NBATCH = 14
+};
+
+/*
+ * sc_logprobs -- trainer log-probabilities at the recorded and sampled ids.
+ *
+ * Score Centering section: "scores the current policy over the full model
+ * vocabulary at the rollout temperature, then gathers candidate and sampled
+ * logprobs".  One HBM pass over each valid row of logits.
+ *
+ *   logits        device, [n_rows, row_stride] of logits_dtype (SC_F32/SC_BF16)
+ *   head_ids      device int32 [n_rows, k]: recorded ids H, distinct, in [0,V)
+ *   sampled       device int32 [n_rows]: sampled token a
+ *   resp_idx      device int32 [n_rows] or NULL: response of each row, < 0 for
+ *                 padding; NULL means every row is valid
+ *   temperature   T > 0; p = softmax(z / T)
+ * Outputs (device, written for every row):
+ *   row_stats     float [n_rows, SC_NSTATS]: columns LSE, LOGP_A, TAIL, P_H
+ *                 (the other columns are left untouched)
+ *   row_idx       int32 [n_rows, SC_NIDX]: argmax of the raw logits (lowest
+ *                 index among equal maxima) and the slot k with H_k = a (-1 if
+ *                 a is not recorded)
+ *   head_logp     float [n_rows, k]: log p at H, in slot order
+ *   dev_status    uint32 or NULL: data-error bits OR-ed in
+ */
+int sc_logprobs(const void* logits, int logits_dtype, int64_t n_rows,
+                int64_t vocab, int64_t row_stride, const int32_t* head_ids,
+                int32_t k, const int32_t* sampled, const int32_t* resp_idx,
+                float temperature, float* row_stats, int32_t* row_idx,
+                float* head_logp, uint32_t* dev_status, void* stream);
+
+/*
+ * sc_center -- the SC token loss, rho, coefficients, diagnostics and
+ * (optionally) one full-vocabulary row per position, from sc_logprobs' output.
+ *
+ * Score Centering section: P_H, Q_H, rho, the token loss with stop-gradient
+ * coefficients c = q - rho p on H, the tail proportional to p, global
+ * generated-token reduction with padding masked; rollout_corr/k3_kl.
+ * Reads row_stats columns LSE, LOGP_A, TAIL and row_idx / head_logp as written
+ * by sc_logprobs on the same rows; writes row_stats columns P_H .. K3.
+ * When row_out is not NULL the logits are streamed once more to write it.
+ *
+ *   logits, logits_dtype, row_stride   as for sc_logprobs; may be NULL when
+ *                 row_out is NULL
+ *   head_ids      device int32 [n_rows, k]
+ *   head_probs    device float [n_rows, k]: recorded q (their sum may be < 1)
+ *   sampled       device int32 [n_rows]
+ *   rollout_logp  device float [n_rows] or NULL: recorded log mu(a); NULL
+ *                 leaves the K3 column NaN
+ *   resp_idx      device int32 [n_rows]: response of each row, < 0 = padding
+ *   advantages    device float [n_responses]: A of each response
+ *   n_valid       device int64 [1]: valid positions of the WHOLE step (all
+ *                 chunks); read only for SC_ROW_DLOGITS with row_out
+ *   row_out       device [n_rows, out_stride] of out_dtype, or NULL
+ *   row_mode      sc_row_mode
+ *   coef          device float [n_rows, k]: c_k = q_k - rho p_k, or NULL
+ */
+int sc_center(const void* logits, int logits_dtype, int64_t n_rows,
+              int64_t vocab, int64_t row_stride, const int32_t* head_ids,
+              const float* head_probs, int32_t k, const int32_t* sampled,
+              const float* rollout_logp, const int32_t* resp_idx,
+              const float* advantages, int32_t n_responses, float temperature,
+              const int64_t* n_valid, float* row_stats, int32_t* row_idx,
+              const float* head_logp, float* coef, void* row_out,
+              int out_dtype, int64_t out_stride, int row_mode,
+              uint32_t* dev_status, void* stream);
+
+/*
+ * sc_correct -- sc_logprobs followed by sc_center in one kernel: every output
+ * of both, with each logits row brought from HBM once for the statistics and
+ * re-read from the on-chip caches for row_out.  Same arguments and outputs as
+ * the two calls together; row_stats, row_idx and head_logp are written, not
+ * read.  head_logp and coef may be NULL.
+ */
+int sc_correct(const void* logits, int logits_dtype, int64_t n_rows,
+               int64_t vocab, int64_t row_stride, const int32_t* head_ids,
+               const float* head_probs, int32_t k, const int32_t* sampled,
+               const float* rollout_logp, const int32_t* resp_idx,
+               const float* advantages, int32_t n_responses, float temperature,
+               const int64_t* n_valid, float* row_stats, int32_t* row_idx,
+               float* head_logp, float* coef, void* row_out, int out_dtype,
+               int64_t out_stride, int row_mode, uint32_t* dev_status,
+               void* stream);
+
+/*
+ * sc_group_norm -- rollout-level advantages by group normalisation.
+ *
+ * Score Centering page, section "Training": both algorithms use "group
+ * standard deviation normalization"; Agent Lightning v1.0.3 release note,
+ * section 4: rewards stay fractional (no bf16 cast first) and the normaliser
+ * must not overflow -- the kernel accumulates in float64.
+ *
+ *   rewards     device float [n_groups * group_size]; group j holds entries
+ *               j*group_size .. j*group_size + group_size - 1
+ *   mode        0: (R - mean) / (unbiased std + eps); 1: population std;
+ *               2: R - mean (mean only).  A group of one gets 0 in modes 0-1.
+ *   advantages  device float [n_groups * group_size] (output)
+ * Preconditions: n_groups >= 0, 1 <= group_size <= 4096, eps >= 0 finite.
+ */
+int sc_group_norm(const float* rewards, int32_t n_groups, int32_t group_size,
+                  int32_t mode, float eps, float* advantages, void* stream);
+
+/*
+ * sc_count_valid -- the exact number of non-padding positions (resp_idx >= 0)
+ * as int64 (release note, section 4: token counts are not rounded).
+ *   out         device int64 [1]; overwritten, or incremented when
+ *               accumulate != 0 (for steps processed in chunks)
+ */
+int sc_count_valid(const int32_t* resp_idx, int64_t n_rows, int64_t* out,
+                   int32_t accumulate, void* stream);
+
+/*
+ * sc_batch_sums -- step-level reductions in a fixed order (deterministic):
+ * float64 sums over the valid rows of loss, K3, TV, KL, Q_H and P_H, the
+ * number of valid rows and of rows whose statistics are NaN, then the means
+ * over n_valid (global generated-token reduction, Score Centering section).
+ *   row_stats   device float [n_rows, SC_NSTATS] from sc_center / sc_correct
+ *   resp_idx    device int32 [n_rows]
+ *   n_valid     device int64 [1]
+ *   batch       device double [SC_NBATCH]; sums overwritten, or added to when
+ *               accumulate != 0; means recomputed from the sums every call
+ */
+int sc_batch_sums(const float* row_stats, const int32_t* resp_idx,
+                  int64_t n_rows, const int64_t* n_valid, double* batch,
+                  int32_t accumulate, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* sc_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int sc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SC_H */

@@ -1,0 +1,268 @@
+// C ABI of the SC library: argument validation (before any HIP call), LDS
+// layout, persistent-grid sizing and kernel dispatch.  See include/sc.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+
+#include "sc.h"
+#include "sc_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxI32 = 2147483647;
+constexpr int kMaxK = 1024;
+constexpr size_t kMaxLds = 64 * 1024;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t esize(int dtype) { return dtype == SC_BF16 ? 2 : 4; }
+bool dtype_ok(int d) { return d == SC_F32 || d == SC_BF16; }
+
+// Compute units of the current device, cached per device id.
+int cu_count(int* out) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SC_ERR_HIP;
+  if (dev >= 0 && dev < 64) {
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) { *out = c; return SC_OK; }
+  }
+  int c = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+    return SC_ERR_HIP;
+  if (dev >= 0 && dev < 64) cache[dev].store(c, std::memory_order_relaxed);
+  *out = c;
+  return SC_OK;
+}
+
+// Workgroups per compute unit for the row kernels (tuning knob, read once).
+int row_wgs_per_cu() {
+  static int v = [] {
+    const char* e = std::getenv("SC_ROW_WGS_PER_CU");
+    int x = e ? std::atoi(e) : 0;
+    return (x >= 1 && x <= 8) ? x : 2;
+  }();
+  return v;
+}
+
+// Shared row-kernel argument checks; fills the geometry part of RowParams.
+int check_rows(sc::RowParams& P, const void* logits, bool logits_needed, int logits_dtype,
+               int64_t n_rows, int64_t vocab, int64_t row_stride,
+               const int32_t* head_ids, int32_t k, const int32_t* sampled,
+               float temperature, float* row_stats, int32_t* row_idx) {
+  if (!dtype_ok(logits_dtype)) return SC_ERR_ARG;
+  if (n_rows < 0 || n_rows > kMaxI32) return SC_ERR_ARG;
+  if (vocab < 1 || vocab > kMaxI32 - 64) return SC_ERR_ARG;
+  if (row_stride < vocab) return SC_ERR_ARG;
+  if (k < 1 || k > kMaxK || (int64_t)k > vocab) return SC_ERR_ARG;
+  if (!(std::isfinite(temperature) && temperature > 0.f)) return SC_ERR_ARG;
+  if (!head_ids || !sampled || !row_stats || !row_idx) return SC_ERR_ARG;
+  if (logits_needed && !logits) return SC_ERR_ARG;
+  if (logits && !aligned(logits, esize(logits_dtype))) return SC_ERR_ARG;
+  if (!aligned(head_ids, 4) || !aligned(sampled, 4) || !aligned(row_stats, 4) ||
+      !aligned(row_idx, 4))
+    return SC_ERR_ARG;
+  P.logits = logits;
+  P.in_dtype = logits_dtype;
+  P.n_rows = n_rows;
+  P.vocab = vocab;
+  P.row_stride = row_stride;
+  P.head_ids = head_ids;
+  P.k = k;
+  P.sampled = sampled;
+  P.temperature = temperature;
+  P.c = (float)(1.4426950408889634 / (double)temperature);
+  P.row_stats = row_stats;
+  P.row_idx = row_idx;
+  return SC_OK;
+}
+
+// LDS layout of a row kernel; needs P.vector, P.vocab, P.k set.
+int layout(sc::RowParams& P) {
+  const int B = sc::kRowBlock;
+  const int64_t N = P.vector ? 16 / (int64_t)esize(P.in_dtype) : 1;
+  const int64_t n_full = P.vocab / N;
+  const int64_t jmax = (n_full + B - 1) / B;
+  P.bm_wpt = (int)std::max<int64_t>(1, (jmax + 31) / 32);
+  int hs = 2, hbits = 1;
+  while (hs < 2 * P.k) { hs <<= 1; ++hbits; }
+  P.hs = hs;
+  P.hshift = 32 - hbits;
+  P.ke = P.k + 2;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = (off + bytes + 15) & ~size_t(15); return (int)o; };
+  P.off_bitmap = take((size_t)P.bm_wpt * B * 4);
+  P.off_hkey = take((size_t)hs * 4);
+  P.off_hval = take((size_t)hs * 4);
+  P.off_headz = take((size_t)P.k * 4);
+  P.off_headp = take((size_t)P.k * 4);
+  P.off_hout = take((size_t)P.k * 4);
+  P.off_entvec = take((size_t)P.ke * 4);
+  P.off_entval = take((size_t)P.ke * N * 4);
+  P.off_entperm = take((size_t)P.ke * 4);
+  P.lds_bytes = off;
+  return off <= kMaxLds ? SC_OK : SC_ERR_UNSUPPORTED;
+}
+
+bool vector_ok(const void* p, int dtype, int64_t stride) {
+  return p == nullptr || (aligned(p, 16) && ((size_t)stride * esize(dtype)) % 16 == 0);
+}
+
+int run_rows(sc::RowParams& P, int kind, void* stream) {
+  int st = layout(P);
+  if (st != SC_OK) return st;
+  if (P.n_rows == 0) return SC_OK;
+  int cus = 0;
+  st = cu_count(&cus);
+  if (st != SC_OK) return st;
+  int64_t grid = std::min<int64_t>(P.n_rows, (int64_t)cus * row_wgs_per_cu());
+  hipError_t e = sc::launch_row(P, kind, (int)grid, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SC_OK : SC_ERR_HIP;
+}
+
+int check_center(sc::RowParams& P, const float* head_probs, const float* rollout_logp,
+                 const int32_t* resp_idx, const float* advantages, int32_t n_responses,
+                 const int64_t* n_valid, float* coef, void* row_out, int out_dtype,
+                 int64_t out_stride, int row_mode, uint32_t* dev_status) {
+  if (!head_probs || !resp_idx || !advantages) return SC_ERR_ARG;
+  if (n_responses < 0) return SC_ERR_ARG;
+  if (row_mode < SC_ROW_DLOGITS || row_mode > SC_ROW_CORRECTION) return SC_ERR_ARG;
+  if (row_out) {
+    if (!dtype_ok(out_dtype) || out_stride < P.vocab) return SC_ERR_ARG;
+    if (!aligned(row_out, esize(out_dtype))) return SC_ERR_ARG;
+    if (row_mode == SC_ROW_DLOGITS && !n_valid) return SC_ERR_ARG;
+  }
+  if (!aligned(head_probs, 4) || !aligned(resp_idx, 4) || !aligned(advantages, 4) ||
+      (rollout_logp && !aligned(rollout_logp, 4)) || (coef && !aligned(coef, 4)) ||
+      (n_valid && !aligned(n_valid, 8)) || (dev_status && !aligned(dev_status, 4)))
+    return SC_ERR_ARG;
+  P.head_probs = head_probs;
+  P.rollout_logp = rollout_logp;
+  P.resp_idx = resp_idx;
+  P.advantages = advantages;
+  P.n_responses = n_responses;
+  P.n_valid = n_valid;
+  P.coef = coef;
+  P.row_out = row_out;
+  P.out_dtype = row_out ? out_dtype : SC_F32;
+  P.out_stride = row_out ? out_stride : 0;
+  P.row_mode = row_mode;
+  P.dev_status = dev_status;
+  P.vector = (vector_ok(P.logits, P.in_dtype, P.row_stride) &&
+              vector_ok(row_out, P.out_dtype, P.out_stride)) ? 1 : 0;
+  return SC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sc_logprobs(const void* logits, int logits_dtype, int64_t n_rows, int64_t vocab,
+                int64_t row_stride, const int32_t* head_ids, int32_t k,
+                const int32_t* sampled, const int32_t* resp_idx, float temperature,
+                float* row_stats, int32_t* row_idx, float* head_logp,
+                uint32_t* dev_status, void* stream) {
+  sc::RowParams P{};
+  int st = check_rows(P, logits, true, logits_dtype, n_rows, vocab, row_stride, head_ids, k,
+                      sampled, temperature, row_stats, row_idx);
+  if (st != SC_OK) return st;
+  if ((resp_idx && !aligned(resp_idx, 4)) || (head_logp && !aligned(head_logp, 4)) ||
+      (dev_status && !aligned(dev_status, 4)))
+    return SC_ERR_ARG;
+  P.resp_idx = resp_idx;
+  P.head_logp = head_logp;
+  P.dev_status = dev_status;
+  P.out_dtype = SC_F32;
+  P.vector = vector_ok(logits, logits_dtype, row_stride) ? 1 : 0;
+  return run_rows(P, 0, stream);
+}
+
+int sc_center(const void* logits, int logits_dtype, int64_t n_rows, int64_t vocab,
+              int64_t row_stride, const int32_t* head_ids, const float* head_probs,
+              int32_t k, const int32_t* sampled, const float* rollout_logp,
+              const int32_t* resp_idx, const float* advantages, int32_t n_responses,
+              float temperature, const int64_t* n_valid, float* row_stats,
+              int32_t* row_idx, const float* head_logp, float* coef, void* row_out,
+              int out_dtype, int64_t out_stride, int row_mode, uint32_t* dev_status,
+              void* stream) {
+  sc::RowParams P{};
+  int st = check_rows(P, logits, row_out != nullptr, logits_dtype, n_rows, vocab, row_stride,
+                      head_ids, k, sampled, temperature, row_stats, row_idx);
+  if (st != SC_OK) return st;
+  if (!head_logp || !aligned(head_logp, 4)) return SC_ERR_ARG;
+  st = check_center(P, head_probs, rollout_logp, resp_idx, advantages, n_responses, n_valid,
+                    coef, row_out, out_dtype, out_stride, row_mode, dev_status);
+  if (st != SC_OK) return st;
+  P.head_logp = const_cast<float*>(head_logp);
+  return run_rows(P, 1, stream);
+}
+
+int sc_correct(const void* logits, int logits_dtype, int64_t n_rows, int64_t vocab,
+               int64_t row_stride, const int32_t* head_ids, const float* head_probs,
+               int32_t k, const int32_t* sampled, const float* rollout_logp,
+               const int32_t* resp_idx, const float* advantages, int32_t n_responses,
+               float temperature, const int64_t* n_valid, float* row_stats,
+               int32_t* row_idx, float* head_logp, float* coef, void* row_out,
+               int out_dtype, int64_t out_stride, int row_mode, uint32_t* dev_status,
+               void* stream) {
+  sc::RowParams P{};
+  int st = check_rows(P, logits, true, logits_dtype, n_rows, vocab, row_stride, head_ids, k,
+                      sampled, temperature, row_stats, row_idx);
+  if (st != SC_OK) return st;
+  if (head_logp && !aligned(head_logp, 4)) return SC_ERR_ARG;
+  st = check_center(P, head_probs, rollout_logp, resp_idx, advantages, n_responses, n_valid,
+                    coef, row_out, out_dtype, out_stride, row_mode, dev_status);
+  if (st != SC_OK) return st;
+  P.head_logp = head_logp;
+  return run_rows(P, 2, stream);
+}
+
+int sc_group_norm(const float* rewards, int32_t n_groups, int32_t group_size, int32_t mode,
+                  float eps, float* advantages, void* stream) {
+  if (!rewards || !advantages || n_groups < 0 || group_size < 1 || group_size > 4096)
+    return SC_ERR_ARG;
+  if (mode < 0 || mode > 2 || !(std::isfinite(eps) && eps >= 0.f)) return SC_ERR_ARG;
+  if ((int64_t)n_groups * group_size > kMaxI32) return SC_ERR_ARG;
+  if (!aligned(rewards, 4) || !aligned(advantages, 4)) return SC_ERR_ARG;
+  if (n_groups == 0) return SC_OK;
+  hipError_t e = sc::launch_group_norm(rewards, n_groups, group_size, mode, eps, advantages,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SC_OK : SC_ERR_HIP;
+}
+
+int sc_count_valid(const int32_t* resp_idx, int64_t n_rows, int64_t* out, int32_t accumulate,
+                   void* stream) {
+  if (!out || n_rows < 0 || n_rows > kMaxI32 || (n_rows > 0 && !resp_idx)) return SC_ERR_ARG;
+  if (!aligned(out, 8) || (resp_idx && !aligned(resp_idx, 4))) return SC_ERR_ARG;
+  hipError_t e = sc::launch_count_valid(resp_idx, n_rows, out, accumulate ? 1 : 0,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SC_OK : SC_ERR_HIP;
+}
+
+int sc_batch_sums(const float* row_stats, const int32_t* resp_idx, int64_t n_rows,
+                  const int64_t* n_valid, double* batch, int32_t accumulate, void* stream) {
+  if (!batch || !n_valid || n_rows < 0 || n_rows > kMaxI32) return SC_ERR_ARG;
+  if (n_rows > 0 && (!row_stats || !resp_idx)) return SC_ERR_ARG;
+  if (!aligned(batch, 8) || !aligned(n_valid, 8) || (row_stats && !aligned(row_stats, 4)) ||
+      (resp_idx && !aligned(resp_idx, 4)))
+    return SC_ERR_ARG;
+  hipError_t e = sc::launch_batch_sums(row_stats, resp_idx, n_rows, n_valid, batch,
+                                       accumulate ? 1 : 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SC_OK : SC_ERR_HIP;
+}
+
+const char* sc_status_string(int status) {
+  switch (status) {
+    case SC_OK: return "SC_OK";
+    case SC_ERR_ARG: return "SC_ERR_ARG: invalid argument";
+    case SC_ERR_UNSUPPORTED: return "SC_ERR_UNSUPPORTED: outside what this build supports";
+    case SC_ERR_HIP: return "SC_ERR_HIP: HIP runtime call or kernel launch failed";
+    default: return "unknown sc_status";
+  }
+}
+
+int sc_version(void) { return 100; }
+
+}  // extern "C"

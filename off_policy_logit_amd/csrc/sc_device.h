@@ -1,0 +1,224 @@
+// Device-side building blocks of the SC kernels for gfx950 (wave64).
+//
+// Wave and workgroup reductions, 16-byte vector access to bf16 / fp32 rows,
+// the per-row set of recorded ids kept in LDS, and fp32 -> bf16 rounding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sc {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr double kClamp = 1e-6;  // clamp constant of rho (Score Centering)
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define SC_DEV __device__ __forceinline__
+
+SC_DEV float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Wave reductions (64 lanes, butterfly over __shfl_xor)
+// ---------------------------------------------------------------------------
+SC_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+template <typename F>
+SC_DEV F wave_sum(F v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+SC_DEV uint32_t wave_or(uint32_t v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v |= __shfl_xor(v, o);
+  return v;
+}
+// (value, index) maximum; equal values keep the lower index.
+SC_DEV void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    float ov = __shfl_xor(v, o);
+    int oi = __shfl_xor(i, o);
+    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+  }
+}
+
+// Workgroup reductions through a small LDS scratch.  Every thread of the
+// block must call them (they contain barriers); the result is returned to all
+// threads.  `red` needs B / 64 slots of the element type.
+template <int B>
+SC_DEV void block_argmax(float& v, int& i, float* redf, int* redi) {
+  wave_argmax(v, i);
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  __syncthreads();
+  if (l == 0) { redf[w] = v; redi[w] = i; }
+  __syncthreads();
+  v = redf[0]; i = redi[0];
+#pragma unroll
+  for (int k = 1; k < B / kWave; ++k) {
+    float ov = redf[k]; int oi = redi[k];
+    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+  }
+}
+
+// Sum of N values per thread; fixed order (deterministic for a fixed B).
+template <int B, int N, typename F>
+SC_DEV void block_sum(F (&v)[N], F* red) {
+#pragma unroll
+  for (int n = 0; n < N; ++n) v[n] = wave_sum(v[n]);
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  __syncthreads();
+  if (l == 0) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) red[n * (B / kWave) + w] = v[n];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    F s = red[n * (B / kWave)];
+#pragma unroll
+    for (int k = 1; k < B / kWave; ++k) s += red[n * (B / kWave) + k];
+    v[n] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row element access.  A row is read as "vectors" of N consecutive elements:
+// 16 bytes (N = 8 bf16 or 4 fp32) on the vector path, N = 1 on the scalar
+// path.  bf16 is carried as its raw 16 bits.
+// ---------------------------------------------------------------------------
+SC_DEV float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+SC_DEV uint32_t f32_to_bf16(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+template <typename T, bool VECTOR> struct RowIO;
+
+template <> struct RowIO<uint16_t, true> {   // bf16, 16-byte vectors
+  static constexpr int N = 8;
+  template <bool NT>
+  static SC_DEV void load(const uint16_t* row, int64_t n, float (&v)[N]) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(row) + n;
+    u32x4 w = NT ? __builtin_nontemporal_load(p) : *p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct RowIO<float, true> {      // fp32, 16-byte vectors
+  static constexpr int N = 4;
+  template <bool NT>
+  static SC_DEV void load(const float* row, int64_t n, float (&v)[N]) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(row) + n;
+    f32x4 w = NT ? __builtin_nontemporal_load(p) : *p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = w[i];
+  }
+};
+template <> struct RowIO<uint16_t, false> {  // bf16, one element at a time
+  static constexpr int N = 1;
+  template <bool NT>
+  static SC_DEV void load(const uint16_t* row, int64_t n, float (&v)[N]) {
+    v[0] = bf16_to_f32(row[n]);
+  }
+};
+template <> struct RowIO<float, false> {     // fp32, one element at a time
+  static constexpr int N = 1;
+  template <bool NT>
+  static SC_DEV void load(const float* row, int64_t n, float (&v)[N]) {
+    v[0] = row[n];
+  }
+};
+
+SC_DEV float load_elem(const uint16_t* row, int64_t i) { return bf16_to_f32(row[i]); }
+SC_DEV float load_elem(const float* row, int64_t i) { return row[i]; }
+
+// Store N output values of one vector (bf16 bits or fp32), nontemporal.
+template <typename O, int N> struct RowOut;
+template <> struct RowOut<uint16_t, 8> {
+  static SC_DEV void store(uint16_t* row, int64_t n, const float (&v)[8]) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = f32_to_bf16(v[2 * i]) | (f32_to_bf16(v[2 * i + 1]) << 16);
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(row) + n);
+  }
+};
+template <> struct RowOut<uint16_t, 4> {
+  static SC_DEV void store(uint16_t* row, int64_t n, const float (&v)[4]) {
+    u32x2 w;
+    w[0] = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+    w[1] = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(row) + n);
+  }
+};
+template <> struct RowOut<float, 8> {
+  static SC_DEV void store(float* row, int64_t n, const float (&v)[8]) {
+    f32x4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+    f32x4* p = reinterpret_cast<f32x4*>(row) + 2 * n;
+    __builtin_nontemporal_store(a, p);
+    __builtin_nontemporal_store(b, p + 1);
+  }
+};
+template <> struct RowOut<float, 4> {
+  static SC_DEV void store(float* row, int64_t n, const float (&v)[4]) {
+    f32x4 a = {v[0], v[1], v[2], v[3]};
+    __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(row) + n);
+  }
+};
+template <> struct RowOut<uint16_t, 1> {
+  static SC_DEV void store(uint16_t* row, int64_t n, const float (&v)[1]) {
+    row[n] = (uint16_t)f32_to_bf16(v[0]);
+  }
+};
+template <> struct RowOut<float, 1> {
+  static SC_DEV void store(float* row, int64_t n, const float (&v)[1]) { row[n] = v[0]; }
+};
+
+SC_DEV void store_elem(uint16_t* row, int64_t i, float v) { row[i] = (uint16_t)f32_to_bf16(v); }
+SC_DEV void store_elem(float* row, int64_t i, float v) { row[i] = v; }
+
+// ---------------------------------------------------------------------------
+// Recorded-id set in LDS: open addressing with linear probing, id -> slot.
+// Capacity is a power of two >= 2K, so probes always reach an empty key.
+// ---------------------------------------------------------------------------
+SC_DEV uint32_t id_hash(int32_t id, int shift) {
+  return ((uint32_t)id * 0x9E3779B1u) >> shift;
+}
+// Returns false when `id` is already present (a duplicate record).
+SC_DEV bool idset_insert(int* keys, int* vals, uint32_t mask, int shift,
+                         int32_t id, int slot) {
+  uint32_t h = id_hash(id, shift);
+  for (;;) {
+    int prev = atomicCAS(&keys[h], -1, id);
+    if (prev == -1) { vals[h] = slot; return true; }
+    if (prev == id) return false;
+    h = (h + 1) & mask;
+  }
+}
+SC_DEV int idset_find(const int* keys, const int* vals, uint32_t mask,
+                      int shift, int32_t id) {
+  uint32_t h = id_hash(id, shift);
+  for (;;) {
+    int key = keys[h];
+    if (key == id) return vals[h];
+    if (key == -1) return -1;
+    h = (h + 1) & mask;
+  }
+}
+
+}  // namespace sc

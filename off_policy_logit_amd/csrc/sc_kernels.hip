@@ -1,0 +1,596 @@
+// HIP kernels of the score-centering (SC) correction for gfx950.
+//
+// Method: "Score Centering" example page of Agent Lightning, section
+// "Score Centering" (token loss, P_H, Q_H, rho with 1e-6 clamps, tail
+// proportional to the trainer policy), section "Training" (group standard
+// deviation normalisation), and the rollout_corr/k3_kl diagnostic.
+//
+// One workgroup owns one logits row at a time (persistent grid over rows).
+// Per row:
+//   stage     recorded ids -> LDS id set (id -> slot) and a bitmap over the
+//             row's 16-byte vectors marking those that hold a recorded id or
+//             the sampled id; range and duplicate checks.
+//   pass 1    one coalesced stream of the row: per-thread running max of the
+//             raw logits (with its lowest index), and the sum of
+//             2^((z - m) log2(e) / T) over unmarked vectors (the off-head tail,
+//             summed directly, never as 1 - P_H).  Marked vectors are copied
+//             to a short LDS list instead.
+//   finalize  workgroup max / argmax / tail sum, the marked vectors resolved
+//             element by element (recorded logits, the sampled logit, their
+//             tail members), lse, log p at H and at a, P_H, tau; then Q_H,
+//             rho, c, S, loss, TV, KL(mu_hat || p), K3 in float64.
+//   pass 2    (optional) the row streamed again to write one output element
+//             per vocabulary id: off-head ids get alpha * p_v (a single exp2 of
+//             a fused multiply-add), marked vectors take the exact per-id value.
+#include "sc_device.h"
+#include "sc_internal.h"
+
+namespace sc {
+
+enum KernelKind { KIND_LOGPROBS = 0, KIND_CENTER = 1, KIND_CORRECT = 2 };
+
+// Stats columns (mirror of sc.h; duplicated here so device code needs no C header)
+enum {
+  C_LSE = 0, C_LOGP_A = 1, C_TAIL = 2, C_P_H = 3, C_Q_H = 4, C_RHO = 5,
+  C_S = 6, C_LOSS = 7, C_TV = 8, C_KL = 9, C_K3 = 10, C_RES = 11, C_N = 12
+};
+enum { F_BAD_ID = 1, F_DUP_ID = 2, F_BAD_SAMPLED = 4, F_NONFINITE = 8, F_BAD_RESP = 16 };
+enum { M_DLOGITS = 0, M_SCORE = 1, M_CORRECTION = 2 };
+
+constexpr int kU = 4;  // vectors per thread per tile (divides 32)
+
+template <typename TI, typename TO, bool VECTOR, int B, int KIND>
+__global__ __launch_bounds__(B) void k_row(RowParams P) {
+  using IO = RowIO<TI, VECTOR>;
+  constexpr int N = IO::N;
+  constexpr int NW = B / kWave;
+  const bool has_out = (KIND != KIND_LOGPROBS) && P.row_out != nullptr;
+  const int t = threadIdx.x;
+  const int K = P.k;
+  const int64_t V = P.vocab;
+  const int64_t n_full = V / N;                 // full vectors per row
+  const int rem = (int)(V - n_full * N);        // elements of the partial vector
+  const int64_t J = n_full > t ? (n_full - 1 - t) / B + 1 : 0;  // my vectors
+  const float c = P.c;                          // log2(e) / T
+
+  extern __shared__ __align__(16) unsigned char lds[];
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(lds + P.off_bitmap);
+  int* hkey = reinterpret_cast<int*>(lds + P.off_hkey);
+  int* hval = reinterpret_cast<int*>(lds + P.off_hval);
+  float* headz = reinterpret_cast<float*>(lds + P.off_headz);  // logits at H
+  float* headp = reinterpret_cast<float*>(lds + P.off_headp);  // p at H
+  float* hout = reinterpret_cast<float*>(lds + P.off_hout);    // pass-2 value at H
+  int* ent_vec = reinterpret_cast<int*>(lds + P.off_entvec);
+  float* ent_val = reinterpret_cast<float*>(lds + P.off_entval);
+  int* ent_perm = reinterpret_cast<int*>(lds + P.off_entperm);
+
+  __shared__ float redf[4 * NW];
+  __shared__ int redi[NW];
+  __shared__ double redd[4 * NW];
+  __shared__ int sh_ent;
+  __shared__ uint32_t sh_flags;
+  __shared__ float sh_za;
+  __shared__ uint32_t sh_status;
+
+  const uint32_t hmask = (uint32_t)P.hs - 1;
+  const int hshift = P.hshift;
+  const float qnan = __builtin_nanf("");
+
+  if (t == 0) sh_status = 0;
+
+  for (int64_t row = blockIdx.x; row < P.n_rows; row += gridDim.x) {
+    const int resp = P.resp_idx ? P.resp_idx[row] : 0;
+    float* stats = P.row_stats + row * C_N;
+    int32_t* ridx = P.row_idx + row * 2;
+
+    __syncthreads();  // LDS of the previous row is no longer read
+
+    // ------------------------------------------------------------ padding
+    if (resp < 0) {
+      if (t == 0) {
+        if (KIND != KIND_CENTER) {
+          stats[C_LSE] = 0.f; stats[C_LOGP_A] = 0.f; stats[C_TAIL] = 0.f;
+          ridx[0] = -1; ridx[1] = -1;
+        }
+        if (KIND == KIND_LOGPROBS) stats[C_P_H] = 0.f;
+        if (KIND != KIND_LOGPROBS)
+          for (int col = C_P_H; col <= C_RES; ++col) stats[col] = 0.f;
+      }
+      for (int k = t; k < K; k += B) {
+        if (KIND != KIND_CENTER && P.head_logp) P.head_logp[row * K + k] = 0.f;
+        if (KIND != KIND_LOGPROBS && P.coef) P.coef[row * K + k] = 0.f;
+      }
+      if (has_out) {
+        TO* orow = reinterpret_cast<TO*>(P.row_out) + row * P.out_stride;
+        for (int64_t i = t; i < V; i += B) store_elem(orow, i, 0.f);
+      }
+      continue;
+    }
+
+    const TI* zrow = reinterpret_cast<const TI*>(P.logits) + row * P.row_stride;
+    const int32_t a = P.sampled[row];
+    const bool a_ok = a >= 0 && (int64_t)a < V;
+    const bool need_stage = (KIND != KIND_CENTER) || has_out;
+
+    // ------------------------------------------------------------ stage
+    if (need_stage) {
+      for (int w = 0; w < P.bm_wpt; ++w) bitmap[w * B + t] = 0u;
+      for (int i = t; i < P.hs; i += B) hkey[i] = -1;
+      for (int k = t; k < K; k += B) headz[k] = qnan;
+    }
+    if (t == 0) { sh_ent = 0; sh_flags = 0; sh_za = qnan; }
+    __syncthreads();
+    if (need_stage) {
+      uint32_t fl = 0;
+      auto mark = [&](int64_t v) {
+        int64_t n = v / N;
+        if (n < n_full) {
+          int64_t j = n / B;
+          int tt = (int)(n - j * B);
+          atomicOr(&bitmap[(j >> 5) * B + tt], 1u << (j & 31));
+        }
+      };
+      for (int k = t; k < K; k += B) {
+        int32_t id = P.head_ids[row * K + k];
+        if (id < 0 || (int64_t)id >= V) {
+          fl |= F_BAD_ID;
+        } else {
+          if (!idset_insert(hkey, hval, hmask, hshift, id, k)) fl |= F_DUP_ID;
+          mark(id);
+        }
+      }
+      if (t == 0) {
+        if (!a_ok) fl |= F_BAD_SAMPLED; else mark(a);
+      }
+      if (fl) atomicOr(&sh_flags, fl);
+      __syncthreads();
+    }
+
+    // Quantities shared by the finalize and pass 2.
+    float m = 0.f;        // row max of raw logits (pass-1 kernels)
+    float log2s = 0.f;    // log2 sum_v 2^((z_v - m) c)
+    float lse = 0.f, logp_a = 0.f, tau = 0.f;
+    int argmax = -1, a_slot = -1;
+
+    if (KIND != KIND_CENTER) {
+      // ---------------------------------------------------------- pass 1
+      float m_t = -INFINITY, s_t = 0.f;
+      int am_t = 0x7fffffff;
+      for (int64_t j0 = 0; j0 < J; j0 += kU) {
+        float v[kU][N];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          if (j0 + u < J) {
+            IO::template load<KIND == KIND_LOGPROBS>(zrow, (j0 + u) * B + t, v[u]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < N; ++i) v[u][i] = -INFINITY;
+          }
+        }
+        const uint32_t bits = (bitmap[(j0 >> 5) * B + t] >> (j0 & 31)) & ((1u << kU) - 1u);
+        float tm = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+#pragma unroll
+          for (int i = 0; i < N; ++i) tm = fmaxf(tm, v[u][i]);
+        if (tm > m_t) {
+          s_t *= exp2_fast((m_t - tm) * c);
+          int idx = 0x7fffffff;
+#pragma unroll
+          for (int u = kU - 1; u >= 0; --u)
+#pragma unroll
+            for (int i = N - 1; i >= 0; --i)
+              if (v[u][i] == tm) idx = (int)(((j0 + u) * B + t) * N + i);
+          am_t = idx;
+          m_t = tm;
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          if (j0 + u >= J) continue;
+          if ((bits >> u) & 1u) {
+            int e = atomicAdd(&sh_ent, 1);
+            if (e < P.ke) {
+              ent_vec[e] = (int)((j0 + u) * B + t);
+#pragma unroll
+              for (int i = 0; i < N; ++i) ent_val[e * N + i] = v[u][i];
+            }
+          } else {
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < N; ++i) acc += exp2_fast((v[u][i] - m_t) * c);
+            s_t += acc;
+          }
+        }
+      }
+      // The partial last vector (vocab not a multiple of N) always goes to the
+      // LDS list; its thread is the owner of vector index n_full.
+      if (rem > 0 && t == (int)(n_full % B)) {
+        float v[N];
+        float tm = -INFINITY;
+        int idx = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          v[i] = i < rem ? load_elem(zrow, n_full * N + i) : -INFINITY;
+          if (v[i] > tm) { tm = v[i]; idx = (int)(n_full * N + i); }
+        }
+        if (tm > m_t) {
+          s_t *= exp2_fast((m_t - tm) * c);
+          m_t = tm;
+          am_t = idx;
+        }
+        int e = atomicAdd(&sh_ent, 1);
+        if (e < P.ke) {
+          ent_vec[e] = (int)n_full;
+#pragma unroll
+          for (int i = 0; i < N; ++i) ent_val[e * N + i] = v[i];
+        }
+      }
+
+      // ---------------------------------------------------------- finalize
+      float mv = m_t;
+      int mi = am_t;
+      block_argmax<B>(mv, mi, redf, redi);
+      m = mv;
+      argmax = mi;
+      // my tail sum at the row max
+      float tail_part = (m_t == -INFINITY) ? 0.f : s_t * exp2_fast((m_t - m) * c);
+      // Resolve the marked vectors element by element, in increasing vector
+      // order (rank sort), so that every sum below has a fixed order.
+      const int n_ent = min(sh_ent, P.ke);
+      for (int e = t; e < n_ent; e += B) {
+        const int my = ent_vec[e];
+        int r = 0;
+        for (int j = 0; j < n_ent; ++j) r += ent_vec[j] < my ? 1 : 0;
+        ent_perm[r] = e;
+      }
+      __syncthreads();
+      for (int r = t; r < n_ent; r += B) {
+        const int e = ent_perm[r];
+#pragma unroll
+        for (int l = 0; l < N; ++l) {
+          const int64_t vid = (int64_t)ent_vec[e] * N + l;
+          if (vid >= V) continue;
+          const float z = ent_val[e * N + l];
+          const int slot = idset_find(hkey, hval, hmask, hshift, (int32_t)vid);
+          if (slot >= 0) headz[slot] = z;
+          else tail_part += exp2_fast((z - m) * c);
+          if (vid == a) sh_za = z;
+        }
+      }
+      __syncthreads();
+      float head_part = 0.f;
+      for (int k = t; k < K; k += B) head_part += exp2_fast((headz[k] - m) * c);
+      float sums[2] = {tail_part, head_part};
+      block_sum<B, 2>(sums, redf);
+      const float s = sums[0] + sums[1];
+      log2s = log2f(s);
+      lse = (m * c + log2s) * kLn2;
+      tau = sums[0] / s;
+      const float za = sh_za;
+      logp_a = ((za - m) * c - log2s) * kLn2;
+      // log p and p at H; non-finite checks
+      uint32_t fl = 0;
+      for (int k = t; k < K; k += B) {
+        const float hz = headz[k];
+        if (hz == -INFINITY) fl |= F_NONFINITE;
+        const float l2 = (hz - m) * c - log2s;
+        headp[k] = exp2_fast(l2 + 32.f) * 0x1p-32f;  // subnormal-exact
+        hout[k] = l2 * kLn2;  // log p at H (reused below)
+      }
+      if (!(s < INFINITY) || !(m > -INFINITY) || !(m < INFINITY) || za == -INFINITY)
+        fl |= F_NONFINITE;
+      if (fl) atomicOr(&sh_flags, fl);
+      a_slot = a_ok ? idset_find(hkey, hval, hmask, hshift, a) : -1;
+      __syncthreads();
+    } else {
+      // sc_center: pass-1 results come from memory
+      lse = stats[C_LSE];
+      logp_a = stats[C_LOGP_A];
+      tau = stats[C_TAIL];
+      a_slot = ridx[1];
+      argmax = ridx[0];
+      for (int k = t; k < K; k += B) {
+        const float lp = P.head_logp[row * K + k];
+        hout[k] = lp;
+        headp[k] = expf(lp);
+      }
+      __syncthreads();
+    }
+
+    const uint32_t flags = sh_flags;
+
+    if (KIND == KIND_LOGPROBS) {
+      float ph = 0.f;
+      for (int k = t; k < K; k += B) ph += headp[k];
+      float sums[1] = {ph};
+      block_sum<B, 1>(sums, redf);
+      if (t == 0) {
+        const bool bad = flags != 0;
+        stats[C_LSE] = bad ? qnan : lse;
+        stats[C_LOGP_A] = bad ? qnan : logp_a;
+        stats[C_TAIL] = bad ? qnan : tau;
+        stats[C_P_H] = bad ? qnan : sums[0];
+        ridx[0] = bad ? -1 : argmax;
+        ridx[1] = bad ? -1 : a_slot;
+        if (flags) sh_status |= flags;
+      }
+      if (P.head_logp)
+        for (int k = t; k < K; k += B) P.head_logp[row * K + k] = flags ? qnan : hout[k];
+      continue;
+    }
+
+    // -------------------------------------------------------------- center
+    // Q_H and P_H in float64
+    double d1[2] = {0.0, 0.0};
+    for (int k = t; k < K; k += B) {
+      d1[0] += (double)P.head_probs[row * K + k];
+      d1[1] += (double)headp[k];
+    }
+    block_sum<B, 2>(d1, redd);
+    const double Q_H = d1[0], P_H = d1[1];
+    const double taud = (double)tau;
+    const double rho = fmax(1.0 - Q_H, kClamp) / fmax(taud, kClamp);
+    const double S = Q_H + rho * taud;
+    double d2[3] = {0.0, 0.0, 0.0};
+    for (int k = t; k < K; k += B) {
+      const double q = (double)P.head_probs[row * K + k];
+      const double p = (double)headp[k];
+      const double lp = (double)hout[k];
+      const double ck = q - rho * p;
+      if (P.coef) P.coef[row * K + k] = flags ? qnan : (float)ck;
+      d2[0] += ck * lp;
+      d2[1] += fabs(q - p);
+      if (q > 0.0) d2[2] += q * (log(q) - lp);
+    }
+    block_sum<B, 3>(d2, redd);
+
+    uint32_t rflags = flags;
+    if (resp >= P.n_responses) rflags |= F_BAD_RESP;
+    const double A = (resp < P.n_responses) ? (double)P.advantages[resp] : (double)qnan;
+    const double loss = -A * ((double)logp_a - d2[0]);
+    const double tv = 0.5 * (d2[1] + fabs(rho - 1.0) * taud);
+    double kl = d2[2];
+    if (rho * taud > 0.0) kl += rho * taud * log(rho);
+    double k3 = (double)qnan;
+    if (P.rollout_logp) {
+      const double d = (double)logp_a - (double)P.rollout_logp[row];
+      k3 = expm1(d) - d;
+    }
+
+    if (t == 0) {
+      const bool bad = rflags != 0;
+      if (KIND == KIND_CORRECT) {
+        stats[C_LSE] = bad ? qnan : lse;
+        stats[C_LOGP_A] = bad ? qnan : logp_a;
+        stats[C_TAIL] = bad ? qnan : tau;
+        ridx[0] = bad ? -1 : argmax;
+        ridx[1] = bad ? -1 : a_slot;
+      }
+      stats[C_P_H] = bad ? qnan : (float)P_H;
+      stats[C_Q_H] = bad ? qnan : (float)Q_H;
+      stats[C_RHO] = bad ? qnan : (float)rho;
+      stats[C_S] = bad ? qnan : (float)S;
+      stats[C_LOSS] = bad ? qnan : (float)loss;
+      stats[C_TV] = bad ? qnan : (float)tv;
+      stats[C_KL] = bad ? qnan : (float)kl;
+      stats[C_K3] = bad ? qnan : (float)k3;
+      stats[C_RES] = 0.f;
+      if (rflags) sh_status |= rflags;
+    }
+    if (KIND == KIND_CORRECT && P.head_logp)
+      for (int k = t; k < K; k += B) P.head_logp[row * K + k] = rflags ? qnan : hout[k];
+
+    if (!has_out) continue;
+
+    // -------------------------------------------------------------- pass 2
+    // Off-head entries are alpha * p_v; recorded ids take hout[k]; the
+    // sampled id, when outside H, adds `scale`.
+    double scale = 1.0, alpha;
+    if (P.row_mode == M_CORRECTION) {
+      alpha = rho - 1.0;
+      scale = 0.0;
+    } else {
+      if (P.row_mode == M_DLOGITS)
+        scale = -A / ((double)P.temperature * (double)P.n_valid[0]);
+      alpha = -scale * (rho + 1.0 - S);
+    }
+    if (rflags) { alpha = (double)qnan; scale = (double)qnan; }
+    __syncthreads();  // all reads of hout as log p are done
+    for (int k = t; k < K; k += B) {
+      const double p = (double)headp[k];
+      double val;
+      if (P.row_mode == M_CORRECTION) {
+        val = (double)P.head_probs[row * K + k] - p;
+      } else {
+        const double ind = (k == a_slot) ? 1.0 : 0.0;
+        val = scale * (ind - (double)P.head_probs[row * K + k] - (1.0 - S) * p);
+      }
+      hout[k] = rflags ? qnan : (float)val;
+    }
+    __syncthreads();
+
+    const bool neg = alpha < 0.0;
+    // p_v = 2^((z_v - mref) c - lref); value = sign(alpha) 2^((z_v - mref) c + off)
+    const float mref = (KIND == KIND_CORRECT) ? m : 0.f;
+    const double lref = (KIND == KIND_CORRECT) ? (double)log2s
+                                               : (double)lse * 1.4426950408889634;
+    // +32 here and the 2^-32 below keep results under 2^-126 exact
+    // subnormals (the exp2 instruction flushes them).
+    const float off = (float)(log2(fabs(alpha)) - lref + 32.0);
+    const float add_a = (float)scale;
+    TO* orow = reinterpret_cast<TO*>(P.row_out) + row * P.out_stride;
+
+    auto slow_value = [&](int64_t vid, float z) -> float {
+      const int slot = idset_find(hkey, hval, hmask, hshift, (int32_t)vid);
+      if (slot >= 0) return hout[slot];
+      float e = exp2_fast(fmaf(z - mref, c, off)) * 0x1p-32f;
+      e = neg ? -e : e;
+      if (vid == a) e += add_a;
+      return e;
+    };
+
+    for (int64_t j0 = 0; j0 < J; j0 += kU) {
+      float v[kU][N];
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (j0 + u < J) IO::template load<true>(zrow, (j0 + u) * B + t, v[u]);
+      const uint32_t bits = (bitmap[(j0 >> 5) * B + t] >> (j0 & 31)) & ((1u << kU) - 1u);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (j0 + u >= J) continue;
+        const int64_t n = (j0 + u) * B + t;
+        float o[N];
+        if ((bits >> u) & 1u) {
+#pragma unroll
+          for (int i = 0; i < N; ++i) o[i] = slow_value(n * N + i, v[u][i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < N; ++i) {
+            const float e = exp2_fast(fmaf(v[u][i] - mref, c, off)) * 0x1p-32f;
+            o[i] = neg ? -e : e;
+          }
+        }
+        RowOut<TO, N>::store(orow, n, o);
+      }
+    }
+    if (rem > 0 && t == (int)(n_full % B)) {
+      for (int i = 0; i < rem; ++i) {
+        const int64_t vid = n_full * N + i;
+        store_elem(orow, vid, slow_value(vid, load_elem(zrow, vid)));
+      }
+    }
+  }
+
+  __syncthreads();
+  if (t == 0 && sh_status && P.dev_status) atomicOr(P.dev_status, sh_status);
+}
+
+// ---------------------------------------------------------------------------
+// Group normalisation: one thread per group, float64 two-pass mean / std.
+// ---------------------------------------------------------------------------
+__global__ void k_group_norm(const float* __restrict__ rewards, int n_groups,
+                             int G, int mode, float eps, float* __restrict__ adv) {
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= n_groups) return;
+  const float* r = rewards + (int64_t)g * G;
+  float* o = adv + (int64_t)g * G;
+  double sum = 0.0;
+  for (int i = 0; i < G; ++i) sum += (double)r[i];
+  const double mean = sum / G;
+  if (mode == 2) {
+    for (int i = 0; i < G; ++i) o[i] = (float)((double)r[i] - mean);
+    return;
+  }
+  if (G == 1) { o[0] = 0.f; return; }
+  double ss = 0.0;
+  for (int i = 0; i < G; ++i) { const double d = (double)r[i] - mean; ss += d * d; }
+  const double sd = sqrt(ss / (mode == 0 ? (double)(G - 1) : (double)G));
+  for (int i = 0; i < G; ++i) o[i] = (float)(((double)r[i] - mean) / (sd + (double)eps));
+}
+
+// ---------------------------------------------------------------------------
+// Exact count of valid rows (single workgroup, int64).
+// ---------------------------------------------------------------------------
+template <int B>
+__global__ __launch_bounds__(B) void k_count_valid(const int32_t* __restrict__ resp,
+                                                   int64_t n, int64_t* out, int acc) {
+  __shared__ unsigned long long red[B / kWave];
+  unsigned long long c = 0;
+  for (int64_t i = threadIdx.x; i < n; i += B) c += resp[i] >= 0 ? 1ull : 0ull;
+  c = wave_sum(c);
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long s = 0;
+    for (int w = 0; w < B / kWave; ++w) s += red[w];
+    out[0] = (acc ? out[0] : 0) + (int64_t)s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Step reductions: fixed-order float64 sums (single workgroup).
+// ---------------------------------------------------------------------------
+template <int B>
+__global__ __launch_bounds__(B) void k_batch_sums(const float* __restrict__ st,
+                                                  const int32_t* __restrict__ resp,
+                                                  int64_t n, const int64_t* n_valid,
+                                                  double* batch, int acc) {
+  __shared__ double red[8 * (B / kWave)];
+  double v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int64_t i = threadIdx.x; i < n; i += B) {
+    if (resp[i] < 0) continue;
+    const float* s = st + i * C_N;
+    v[0] += (double)s[C_LOSS];
+    v[1] += (double)s[C_K3];
+    v[2] += (double)s[C_TV];
+    v[3] += (double)s[C_KL];
+    v[4] += (double)s[C_Q_H];
+    v[5] += (double)s[C_P_H];
+    v[6] += 1.0;
+    v[7] += (s[C_LOSS] != s[C_LOSS]) ? 1.0 : 0.0;
+  }
+  block_sum<B, 8>(v, red);
+  if (threadIdx.x == 0) {
+    const double nv = (double)n_valid[0];
+    for (int j = 0; j < 8; ++j) batch[j] = (acc ? batch[j] : 0.0) + v[j];
+    for (int j = 0; j < 6; ++j) batch[8 + j] = batch[j] / nv;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <typename TI, typename TO, bool VECTOR, int B, int KIND>
+static hipError_t launch_row_t(const RowParams& P, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_row<TI, TO, VECTOR, B, KIND>), dim3(grid), dim3(B),
+                     P.lds_bytes, s, P);
+  return hipGetLastError();
+}
+
+template <int B, int KIND>
+static hipError_t launch_row_b(const RowParams& P, int grid, hipStream_t s) {
+  const bool in_bf = P.in_dtype == 1, out_bf = P.out_dtype == 1;
+  if (P.vector) {
+    if (in_bf) return out_bf ? launch_row_t<uint16_t, uint16_t, true, B, KIND>(P, grid, s)
+                             : launch_row_t<uint16_t, float, true, B, KIND>(P, grid, s);
+    return out_bf ? launch_row_t<float, uint16_t, true, B, KIND>(P, grid, s)
+                  : launch_row_t<float, float, true, B, KIND>(P, grid, s);
+  }
+  if (in_bf) return out_bf ? launch_row_t<uint16_t, uint16_t, false, B, KIND>(P, grid, s)
+                           : launch_row_t<uint16_t, float, false, B, KIND>(P, grid, s);
+  return out_bf ? launch_row_t<float, uint16_t, false, B, KIND>(P, grid, s)
+                : launch_row_t<float, float, false, B, KIND>(P, grid, s);
+}
+
+hipError_t launch_row(const RowParams& P, int kind, int grid, hipStream_t s) {
+  switch (kind) {
+    case KIND_LOGPROBS: return launch_row_b<kRowBlock, KIND_LOGPROBS>(P, grid, s);
+    case KIND_CENTER: return launch_row_b<kRowBlock, KIND_CENTER>(P, grid, s);
+    default: return launch_row_b<kRowBlock, KIND_CORRECT>(P, grid, s);
+  }
+}
+
+hipError_t launch_group_norm(const float* r, int n_groups, int G, int mode,
+                             float eps, float* adv, hipStream_t s) {
+  const int b = 64;
+  hipLaunchKernelGGL(k_group_norm, dim3((n_groups + b - 1) / b), dim3(b), 0, s,
+                     r, n_groups, G, mode, eps, adv);
+  return hipGetLastError();
+}
+
+hipError_t launch_count_valid(const int32_t* resp, int64_t n, int64_t* out,
+                              int acc, hipStream_t s) {
+  hipLaunchKernelGGL((k_count_valid<1024>), dim3(1), dim3(1024), 0, s, resp, n,
+                     out, acc);
+  return hipGetLastError();
+}
+
+hipError_t launch_batch_sums(const float* st, const int32_t* resp, int64_t n,
+                             const int64_t* n_valid, double* batch, int acc,
+                             hipStream_t s) {
+  hipLaunchKernelGGL((k_batch_sums<1024>), dim3(1), dim3(1024), 0, s, st, resp,
+                     n, n_valid, batch, acc);
+  return hipGetLastError();
+}
+
+}  // namespace sc

@@ -1,0 +1,235 @@
+"""Thin ctypes binding of libsc.so (the SC correction library for gfx950).
+
+Argument marshalling only: every computation runs in the library's HIP
+kernels.  Each function mirrors the C entry point of the same name in
+``include/sc.h`` and launches on torch's current HIP stream.  Output buffers
+are allocated with torch when not supplied.  A missing library is an error:
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsc.so")
+
+# Mirrors of the enums in include/sc.h
+SC_OK, SC_ERR_ARG, SC_ERR_UNSUPPORTED, SC_ERR_HIP = 0, -1, -2, -3
+SC_F32, SC_BF16 = 0, 1
+DEV_BAD_ID, DEV_DUP_ID, DEV_BAD_SAMPLED, DEV_NONFINITE, DEV_BAD_RESP = 1, 2, 4, 8, 16
+ROW_DLOGITS, ROW_SCORE, ROW_CORRECTION = 0, 1, 2
+STATS = ("lse", "logp_a", "tail", "P_H", "Q_H", "rho", "S", "loss", "tv", "kl",
+         "k3", "reserved")
+NSTATS = len(STATS)
+STAT = {name: i for i, name in enumerate(STATS)}
+BATCH = ("sum_loss", "sum_k3", "sum_tv", "sum_kl", "sum_Q_H", "sum_P_H",
+         "rows", "flagged", "mean_loss", "mean_k3", "mean_tv", "mean_kl",
+         "mean_Q_H", "mean_P_H")
+NBATCH = len(BATCH)
+
+_vp, _i64, _i32, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+_SIGS = {
+    "sc_logprobs": [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i32, _vp, _vp,
+                    _f32, _vp, _vp, _vp, _vp, _vp],
+    "sc_center": [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _vp, _i32, _vp,
+                  _vp, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp,
+                  ctypes.c_int, _i64, ctypes.c_int, _vp, _vp],
+    "sc_correct": [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _vp, _i32, _vp,
+                   _vp, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp,
+                   ctypes.c_int, _i64, ctypes.c_int, _vp, _vp],
+    "sc_group_norm": [_vp, _i32, _i32, _i32, _f32, _vp, _vp],
+    "sc_count_valid": [_vp, _i64, _vp, _i32, _vp],
+    "sc_batch_sums": [_vp, _vp, _i64, _vp, _vp, _i32, _vp],
+    "sc_status_string": [ctypes.c_int],
+    "sc_version": [],
+}
+
+_lib = None
+
+
+class ScError(RuntimeError):
+    """A non-zero sc_status returned by the library."""
+
+
+def lib():
+    """Load libsc.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with "
+                "off_policy_logit_amd.build.build() (no fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_char_p if name == "sc_status_string" else ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != SC_OK:
+        raise ScError(lib().sc_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return SC_BF16
+    if t.dtype == torch.float32:
+        return SC_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t, dtype, name):
+    if t.dtype != dtype or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous {dtype} tensor")
+    return t
+
+
+def _rows(logits):
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise TypeError("logits must be [n_rows, vocab] with unit column stride")
+    return logits.shape[0], logits.shape[1], logits.stride(0)
+
+
+def _alloc_stats(n, k, device, head_logp=True):
+    out = dict(
+        row_stats=torch.empty(n, NSTATS, dtype=torch.float32, device=device),
+        row_idx=torch.empty(n, 2, dtype=torch.int32, device=device))
+    if head_logp:
+        out["head_logp"] = torch.empty(n, k, dtype=torch.float32, device=device)
+    return out
+
+
+def logprobs(logits, head_ids, sampled, resp_idx=None, temperature=1.0,
+             out=None, dev_status=None, stream=None):
+    """sc_logprobs: lse, log p(a), tail mass, P_H, argmax, a_slot, log p at H."""
+    n, V, stride = _rows(logits)
+    k = head_ids.shape[1]
+    _need(head_ids, torch.int32, "head_ids")
+    _need(sampled, torch.int32, "sampled")
+    if resp_idx is not None:
+        _need(resp_idx, torch.int32, "resp_idx")
+    out = out or _alloc_stats(n, k, logits.device)
+    _check(lib().sc_logprobs(
+        _ptr(logits), _dtype_code(logits), n, V, stride, _ptr(head_ids), k,
+        _ptr(sampled), _ptr(resp_idx), float(temperature), _ptr(out["row_stats"]),
+        _ptr(out["row_idx"]), _ptr(out.get("head_logp")), _ptr(dev_status),
+        _stream(stream)))
+    return out
+
+
+def _center_like(fn, logits, head_ids, head_probs, sampled, resp_idx,
+                 advantages, temperature, n_valid, rollout_logp, out, row_out,
+                 row_mode, coef, dev_status, stream, vocab=None):
+    if logits is not None:
+        n, V, stride = _rows(logits)
+        dcode = _dtype_code(logits)
+    else:
+        n, V, stride, dcode = head_ids.shape[0], vocab, vocab, SC_F32
+    k = head_ids.shape[1]
+    for t, dt, name in ((head_ids, torch.int32, "head_ids"),
+                        (head_probs, torch.float32, "head_probs"),
+                        (sampled, torch.int32, "sampled"),
+                        (resp_idx, torch.int32, "resp_idx"),
+                        (advantages, torch.float32, "advantages")):
+        _need(t, dt, name)
+    if row_out is not None:
+        if row_out.dim() != 2 or row_out.stride(1) != 1:
+            raise TypeError("row_out must be [n_rows, >= vocab] with unit column stride")
+        ocode, ostride = _dtype_code(row_out), row_out.stride(0)
+    else:
+        ocode, ostride = SC_F32, 0
+    _check(fn(
+        _ptr(logits), dcode, n, V, stride, _ptr(head_ids), _ptr(head_probs), k,
+        _ptr(sampled), _ptr(rollout_logp), _ptr(resp_idx), _ptr(advantages),
+        advantages.shape[0], float(temperature), _ptr(n_valid),
+        _ptr(out["row_stats"]), _ptr(out["row_idx"]), _ptr(out.get("head_logp")),
+        _ptr(coef), _ptr(row_out), ocode, ostride, int(row_mode),
+        _ptr(dev_status), _stream(stream)))
+
+
+def center(stats, head_ids, head_probs, sampled, resp_idx, advantages,
+           temperature=1.0, n_valid=None, rollout_logp=None, logits=None,
+           row_out=None, row_mode=ROW_DLOGITS, coef=None, dev_status=None,
+           stream=None, vocab=None):
+    """sc_center on the output dict of logprobs(); fills the remaining stats."""
+    if coef is None:
+        coef = torch.empty_like(stats["head_logp"])
+    if logits is None and vocab is None:
+        raise TypeError("vocab is required when logits is None")
+    _center_like(lib().sc_center, logits, head_ids, head_probs, sampled,
+                 resp_idx, advantages, temperature, n_valid, rollout_logp,
+                 stats, row_out, row_mode, coef, dev_status, stream, vocab)
+    stats["coef"] = coef
+    return stats
+
+
+def correct(logits, head_ids, head_probs, sampled, resp_idx, advantages,
+            temperature=1.0, n_valid=None, rollout_logp=None, row_out=None,
+            row_mode=ROW_DLOGITS, out=None, coef=None, dev_status=None,
+            stream=None):
+    """sc_correct: every output of logprobs() and center() in one kernel."""
+    n = logits.shape[0]
+    k = head_ids.shape[1]
+    out = out or _alloc_stats(n, k, logits.device)
+    if coef is None:
+        coef = torch.empty(n, k, dtype=torch.float32, device=logits.device)
+    _center_like(lib().sc_correct, logits, head_ids, head_probs, sampled,
+                 resp_idx, advantages, temperature, n_valid, rollout_logp, out,
+                 row_out, row_mode, coef, dev_status, stream)
+    out["coef"] = coef
+    return out
+
+
+def group_norm(rewards, group_size, mode=0, eps=1e-6, out=None, stream=None):
+    """sc_group_norm: advantages of consecutive groups of responses."""
+    _need(rewards, torch.float32, "rewards")
+    n = rewards.numel()
+    if n % group_size:
+        raise ValueError("rewards length must be a multiple of group_size")
+    out = torch.empty_like(rewards) if out is None else out
+    _check(lib().sc_group_norm(_ptr(rewards), n // group_size, group_size,
+                               int(mode), float(eps), _ptr(out), _stream(stream)))
+    return out
+
+
+def count_valid(resp_idx, out=None, accumulate=False, stream=None):
+    """sc_count_valid: exact int64 number of rows with resp_idx >= 0."""
+    _need(resp_idx, torch.int32, "resp_idx")
+    if out is None:
+        out = torch.empty(1, dtype=torch.int64, device=resp_idx.device)
+    _check(lib().sc_count_valid(_ptr(resp_idx), resp_idx.numel(), _ptr(out),
+                                int(bool(accumulate)), _stream(stream)))
+    return out
+
+
+def batch_sums(row_stats, resp_idx, n_valid, out=None, accumulate=False,
+               stream=None):
+    """sc_batch_sums: float64 step sums and global-token means."""
+    _need(row_stats, torch.float32, "row_stats")
+    _need(resp_idx, torch.int32, "resp_idx")
+    if out is None:
+        out = torch.empty(NBATCH, dtype=torch.float64, device=row_stats.device)
+    _check(lib().sc_batch_sums(_ptr(row_stats), _ptr(resp_idx), resp_idx.numel(),
+                               _ptr(n_valid), _ptr(out), int(bool(accumulate)),
+                               _stream(stream)))
+    return out
+
+
+def version():
+    return lib().sc_version()

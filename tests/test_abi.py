@@ -1,0 +1,135 @@
+"""The C-ABI library loads, exports every declared entry point and rejects bad
+arguments before touching HIP (so these run on a host without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from off_policy_logit_amd import sc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: validation fails first
+FAKE2 = ctypes.c_void_p(0x10002)     # 2-byte aligned only
+FAKE1 = ctypes.c_void_p(0x10001)     # odd address
+NULL = None
+ARG, UNSUP, OK = sc.SC_ERR_ARG, sc.SC_ERR_UNSUPPORTED, sc.SC_OK
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(sc_\w+)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"sc_logprobs", "sc_center", "sc_correct", "sc_group_norm",
+            "sc_count_valid", "sc_batch_sums"} <= set(names)
+    L = sc.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    L = sc.lib()
+    for code in (OK, ARG, UNSUP, sc.SC_ERR_HIP):
+        assert L.sc_status_string(code).startswith(b"SC_")
+    assert L.sc_version() >= 100
+
+
+def logprobs(**kw):
+    a = dict(logits=FAKE, dtype=sc.SC_BF16, n=4, V=1000, stride=1000, ids=FAKE,
+             k=10, sampled=FAKE, resp=NULL, T=1.0, stats=FAKE, idx=FAKE,
+             hlp=FAKE, dev=NULL, stream=NULL)
+    a.update(kw)
+    return sc.lib().sc_logprobs(a["logits"], a["dtype"], a["n"], a["V"], a["stride"],
+                                a["ids"], a["k"], a["sampled"], a["resp"], a["T"],
+                                a["stats"], a["idx"], a["hlp"], a["dev"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(logits=NULL), dict(ids=NULL), dict(sampled=NULL), dict(stats=NULL),
+    dict(idx=NULL), dict(dtype=2), dict(dtype=-1), dict(n=-1), dict(V=0),
+    dict(stride=999), dict(k=0), dict(k=1001), dict(k=1025, V=5000, stride=5000),
+    dict(T=0.0), dict(T=-1.0), dict(T=float("nan")), dict(T=float("inf")),
+    dict(logits=FAKE1), dict(dtype=sc.SC_F32, logits=FAKE2), dict(ids=FAKE2),
+    dict(V=2 ** 31, stride=2 ** 31), dict(n=2 ** 31),
+])
+def test_logprobs_rejects_bad_arguments(kw):
+    assert logprobs(**kw) == ARG
+
+
+def test_logprobs_zero_rows_is_a_noop_without_hip():
+    assert logprobs(n=0) == OK
+
+
+def test_lds_limit_is_reported_as_unsupported():
+    assert logprobs(V=2 ** 30, stride=2 ** 30, k=1024) == UNSUP
+
+
+def center(fn="sc_center", **kw):
+    a = dict(logits=FAKE, dtype=sc.SC_BF16, n=4, V=1000, stride=1000, ids=FAKE,
+             probs=FAKE, k=10, sampled=FAKE, rlp=NULL, resp=FAKE, adv=FAKE,
+             nresp=2, T=1.0, nvalid=FAKE, stats=FAKE, idx=FAKE, hlp=FAKE,
+             coef=FAKE, out=FAKE, odt=sc.SC_BF16, ostride=1000,
+             mode=sc.ROW_DLOGITS, dev=NULL, stream=NULL)
+    a.update(kw)
+    return getattr(sc.lib(), fn)(
+        a["logits"], a["dtype"], a["n"], a["V"], a["stride"], a["ids"], a["probs"],
+        a["k"], a["sampled"], a["rlp"], a["resp"], a["adv"], a["nresp"], a["T"],
+        a["nvalid"], a["stats"], a["idx"], a["hlp"], a["coef"], a["out"], a["odt"],
+        a["ostride"], a["mode"], a["dev"], a["stream"])
+
+
+@pytest.mark.parametrize("fn", ["sc_center", "sc_correct"])
+@pytest.mark.parametrize("kw", [
+    dict(probs=NULL), dict(resp=NULL), dict(adv=NULL), dict(nresp=-1),
+    dict(mode=3), dict(mode=-1), dict(odt=5), dict(ostride=999),
+    dict(nvalid=NULL), dict(out=FAKE1), dict(odt=sc.SC_F32, out=FAKE2),
+    dict(logits=NULL), dict(T=0.0), dict(k=0), dict(coef=FAKE2),
+])
+def test_center_and_correct_reject_bad_arguments(fn, kw):
+    assert center(fn, **kw) == ARG
+
+
+def test_center_without_row_out_needs_no_logits_or_n_valid():
+    assert center(logits=NULL, out=NULL, nvalid=NULL, n=0) == OK
+    assert center(logits=NULL, out=NULL, nvalid=NULL, hlp=NULL, n=0) == ARG
+    # scores and corrections do not need N_valid
+    assert center(nvalid=NULL, mode=sc.ROW_SCORE, n=0) == OK
+
+
+@pytest.mark.parametrize("args", [
+    (NULL, 2, 4, 0, 1e-6, FAKE), (FAKE, 2, 4, 0, 1e-6, NULL), (FAKE, -1, 4, 0, 1e-6, FAKE),
+    (FAKE, 2, 0, 0, 1e-6, FAKE), (FAKE, 2, 4097, 0, 1e-6, FAKE), (FAKE, 2, 4, 3, 1e-6, FAKE),
+    (FAKE, 2, 4, 0, -1.0, FAKE), (FAKE, 2, 4, 0, float("nan"), FAKE), (FAKE2, 2, 4, 0, 0.0, FAKE),
+])
+def test_group_norm_rejects_bad_arguments(args):
+    assert sc.lib().sc_group_norm(*args, NULL) == ARG
+
+
+def test_group_norm_zero_groups_is_a_noop():
+    assert sc.lib().sc_group_norm(FAKE, 0, 4, 0, 1e-6, FAKE, NULL) == OK
+
+
+def test_count_and_batch_sums_reject_bad_arguments():
+    L = sc.lib()
+    assert L.sc_count_valid(FAKE, 10, NULL, 0, NULL) == ARG
+    assert L.sc_count_valid(NULL, 10, FAKE, 0, NULL) == ARG
+    assert L.sc_count_valid(FAKE, -1, FAKE, 0, NULL) == ARG
+    assert L.sc_count_valid(FAKE, 10, FAKE2, 0, NULL) == ARG
+    assert L.sc_batch_sums(FAKE, FAKE, 10, NULL, FAKE, 0, NULL) == ARG
+    assert L.sc_batch_sums(FAKE, FAKE, 10, FAKE, NULL, 0, NULL) == ARG
+    assert L.sc_batch_sums(NULL, FAKE, 10, FAKE, FAKE, 0, NULL) == ARG
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(sc, "_lib", None)
+    monkeypatch.setattr(sc, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        sc.lib()

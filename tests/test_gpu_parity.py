@@ -1,0 +1,415 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Every test prints the case it is about to run (flushed) before touching the
+GPU.  Small cases compare every row and every element; the full-size
+workloads compare seeded samples of rows, each row element by element.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sc_oracle as O
+import synthetic
+from tests.parity import check_row, compare_bf16
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from off_policy_logit_amd import sc
+
+DEV = "cuda:0"
+MODES = {"dlogits": O.MODE_DLOGITS, "score": O.MODE_SCORE,
+         "correction": O.MODE_CORRECTION}
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def to_dev(d):
+    out = {}
+    for k, v in d.items():
+        if isinstance(v, np.ndarray):
+            out[k] = torch.from_numpy(np.ascontiguousarray(v)).to(DEV)
+        elif isinstance(v, torch.Tensor):
+            out[k] = v.to(DEV)
+        else:
+            out[k] = v
+    return out
+
+
+def host_rows(t, rows):
+    x = t[rows]
+    if x.dtype == torch.bfloat16:
+        x = x.float()
+    return x.cpu().numpy()
+
+
+def run_correct(d, adv, n_valid, T, mode, out_dtype, logits=None):
+    logits = d["logits"] if logits is None else logits
+    n, V = logits.shape
+    row_out = None
+    if out_dtype is not None:
+        row_out = torch.empty(n, V, device=DEV,
+                              dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = sc.correct(logits, d["head_ids"], d["head_probs"], d["sampled"],
+                     d["resp_idx"], adv, temperature=T, n_valid=n_valid,
+                     rollout_logp=d["rollout_logp"], row_out=row_out,
+                     row_mode=mode, dev_status=status)
+    out["row"] = row_out
+    out["status"] = status
+    return out
+
+
+def gather(out, rows, out_dtype):
+    g = dict(stats=host_rows(out["row_stats"], rows), idx=host_rows(out["row_idx"], rows),
+             head_logp=host_rows(out["head_logp"], rows), coef=host_rows(out["coef"], rows))
+    if out_dtype == "bf16":
+        g["row"] = out["row"][rows].view(torch.int16).cpu().numpy()
+    elif out_dtype == "f32":
+        g["row"] = host_rows(out["row"], rows)
+    return g
+
+
+def check_rows(tag, d, out, rows, adv_h, n_valid, T, mode, out_dtype,
+               min_equal=0.998, logits_h=None):
+    """Compare the listed rows of a GPU result with the oracle."""
+    rows = np.asarray(rows)
+    z = logits_h if logits_h is not None else host_rows(d["logits"], rows)
+    ids = host_rows(d["head_ids"], rows)
+    q = host_rows(d["head_probs"], rows)
+    a = host_rows(d["sampled"], rows)
+    rlp = host_rows(d["rollout_logp"], rows)
+    resp = host_rows(d["resp_idx"], rows)
+    g = gather(out, rows, out_dtype)
+    stats = []
+    for j, r in enumerate(rows):
+        gj = {key: val[j] for key, val in g.items()}
+        if resp[j] < 0:
+            assert np.all(gj["stats"][:11] == 0) and list(gj["idx"]) == [-1, -1]
+            if out_dtype is not None:
+                assert np.all(gj["row"] == 0)
+            continue
+        A = float(adv_h[resp[j]])
+        o = O.sc_row(z[j], T, ids[j], q[j], a[j], rollout_logp=rlp[j],
+                     advantage=A, n_valid=n_valid, row_mode=mode)
+        check_row(f"{tag} row {r}", gj, o, A=A, T=T, n_valid=n_valid, mode=mode,
+                  row_dtype=out_dtype, bf16_stats=stats, rlp=rlp[j])
+    if stats:
+        total = sum(s[2] for s in stats)
+        eq = sum(s[1] * s[2] for s in stats) / total
+        say(f"{tag}: bf16 bit-equal fraction {eq:.6f} over {total} entries")
+        assert eq >= min_equal, (tag, eq)
+
+
+# ---------------------------------------------------------------------------
+# Tiny workload: every row, every output, every row mode
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T", [1.0, 0.7])
+@pytest.mark.parametrize("mode,out_dtype", [("dlogits", "bf16"), ("score", "f32"),
+                                            ("correction", "f32"), ("dlogits", "f32"),
+                                            ("score", None)])
+def test_tiny_all_rows_correct(T, mode, out_dtype):
+    say(f"tiny 256x4096 fp32 T={T} sc_correct mode={mode} out={out_dtype}")
+    h = synthetic.tiny(seed=0, temperature=T)
+    d = to_dev(h)
+    adv = sc.group_norm(d["rewards"], h["group_size"])
+    n_valid = sc.count_valid(d["resp_idx"])
+    out = run_correct(d, adv, n_valid, T, MODES[mode], out_dtype)
+    torch.cuda.synchronize()
+    assert int(out["status"].item()) == 0
+    nv = int(n_valid.item())
+    assert nv == 256
+    adv_h = adv.cpu().numpy()
+    np.testing.assert_allclose(adv_h, O.group_norm(h["rewards"], 4), atol=1e-6)
+    check_rows(f"tiny T={T} {mode}/{out_dtype}", d, out, np.arange(256), adv_h, nv,
+               T, MODES[mode], out_dtype, logits_h=h["logits"])
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32", None])
+def test_tiny_two_call_path(out_dtype):
+    say(f"tiny sc_logprobs + sc_center out={out_dtype}")
+    h = synthetic.tiny(seed=4)
+    d = to_dev(h)
+    adv = sc.group_norm(d["rewards"], 4)
+    n_valid = sc.count_valid(d["resp_idx"])
+    st = sc.logprobs(d["logits"], d["head_ids"], d["sampled"], d["resp_idx"])
+    torch.cuda.synchronize()
+    # stats-only check of sc_logprobs
+    rows = np.arange(256)
+    z = h["logits"]
+    for r in rows[::17]:
+        o = O.sc_row(z[r], 1.0, h["head_ids"][r], h["head_probs"][r], h["sampled"][r])
+        g = dict(stats=st["row_stats"][r].cpu().numpy(), idx=st["row_idx"][r].cpu().numpy(),
+                 head_logp=st["head_logp"][r].cpu().numpy())
+        check_row(f"logprobs row {r}", g, o, stats_only=True)
+    row_out = None
+    if out_dtype:
+        row_out = torch.empty(256, 4096, device=DEV,
+                              dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    sc.center(st, d["head_ids"], d["head_probs"], d["sampled"], d["resp_idx"], adv,
+              n_valid=n_valid, rollout_logp=d["rollout_logp"], logits=d["logits"],
+              row_out=row_out, dev_status=status)
+    st["row"] = row_out
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    # the two-call path rounds lse to fp32 between the calls: a second
+    # rounding of relative size |lse| 2^-24 enters every p_v
+    check_rows(f"two-call {out_dtype}", d, st, rows, adv.cpu().numpy(), 256, 1.0,
+               O.MODE_DLOGITS, out_dtype, min_equal=0.995, logits_h=z)
+
+
+# ---------------------------------------------------------------------------
+# Ragged vocabulary, strided / misaligned rows (scalar path), K extremes
+# ---------------------------------------------------------------------------
+def crafted(n, V, K, seed, dtype, stride=None, scale=2.0):
+    rng = np.random.default_rng(seed)
+    z = rng.normal(0, scale, (n, V)).astype(np.float32)
+    if dtype == "bf16":
+        z = torch.from_numpy(z).to(torch.bfloat16).float().numpy()
+    ids = np.stack([rng.choice(V, K, replace=False) for _ in range(n)]).astype(np.int32)
+    q = (rng.dirichlet(np.ones(K), n) * rng.uniform(0.2, 0.999, (n, 1))).astype(np.float32)
+    a = rng.integers(0, V, n).astype(np.int32)
+    half = n // 2
+    a[:half] = ids[np.arange(half), rng.integers(0, K, half)]   # some a inside H
+    rlp = np.log(rng.uniform(0.01, 1.0, n)).astype(np.float32)
+    resp = (np.arange(n) // 4).astype(np.int32)
+    stride = stride or V
+    buf = np.zeros((n, stride), np.float32)
+    buf[:, :V] = z
+    t = torch.from_numpy(buf).to(DEV)
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    logits = t[:, :V]
+    d = dict(logits=logits, head_ids=torch.from_numpy(ids).to(DEV),
+             head_probs=torch.from_numpy(q).to(DEV), sampled=torch.from_numpy(a).to(DEV),
+             rollout_logp=torch.from_numpy(rlp).to(DEV), resp_idx=torch.from_numpy(resp).to(DEV))
+    return d, z
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V,K,stride", [(4099, 128, None), (4099, 128, 4100), (2000, 1, None),
+                                        (200, 200, None), (1031, 129, 1040), (4099, 64, 4101), (63, 7, None),
+                                        (8 * 1024 + 3, 1024, None)])
+def test_ragged_strided_and_k_extremes(dtype, V, K, stride):
+    say(f"crafted n=32 V={V} K={K} stride={stride} dtype={dtype}")
+    d, z = crafted(32, V, K, seed=V + K, dtype=dtype, stride=stride)
+    adv = torch.linspace(-1.5, 1.5, 8, device=DEV)
+    n_valid = sc.count_valid(d["resp_idx"])
+    for out_dtype in ("bf16", "f32"):
+        out = run_correct(d, adv, n_valid, 1.0, O.MODE_SCORE, out_dtype)
+        torch.cuda.synchronize()
+        assert int(out["status"].item()) == 0
+        check_rows(f"crafted V={V} K={K} {dtype}->{out_dtype}", d, out, np.arange(32),
+                   adv.cpu().numpy(), 32, 1.0, O.MODE_SCORE, out_dtype, logits_h=z,
+                   min_equal=0.99 if V < 300 else 0.998)
+
+
+# ---------------------------------------------------------------------------
+# Padding rows and data errors
+# ---------------------------------------------------------------------------
+def test_padding_rows_and_data_errors():
+    say("crafted data-error rows V=1000 K=16 bf16")
+    d, z = crafted(12, 1000, 16, seed=3, dtype="bf16")
+    ids = d["head_ids"].cpu().numpy()
+    a = d["sampled"].cpu().numpy()
+    resp = d["resp_idx"].cpu().numpy()
+    resp[1] = -1                        # padding
+    ids[2, 3] = 1000                    # id out of range
+    ids[3, 5] = ids[3, 6]               # duplicate id
+    a[4] = -2                           # sampled out of range
+    zl = z.copy()
+    zl[5, 10] = np.nan                  # NaN logit
+    zl[6, ids[6, 0]] = -np.inf          # -inf at a recorded id
+    zl[7, 999] = -np.inf                # -inf elsewhere: legal
+    if a[7] == 999 or 999 in ids[7]:
+        zl[7, 998] = -np.inf
+        zl[7, 999] = z[7, 999]
+    resp[8] = 3                         # response index beyond advantages
+    logits = torch.from_numpy(zl).to(DEV).to(torch.bfloat16)
+    d.update(logits=logits, head_ids=torch.from_numpy(ids).to(DEV),
+             sampled=torch.from_numpy(a).to(DEV), resp_idx=torch.from_numpy(resp).to(DEV))
+    adv = torch.tensor([0.5, -1.0, 2.0], device=DEV)   # resp 3 is out of range
+    n_valid = sc.count_valid(d["resp_idx"])
+    out = run_correct(d, adv, n_valid, 1.0, O.MODE_DLOGITS, "bf16")
+    torch.cuda.synchronize()
+    st = out["row_stats"].cpu().numpy()
+    idx = out["row_idx"].cpu().numpy()
+    row = out["row"].float().cpu().numpy()
+    flags = int(out["status"].item())
+    assert flags == (O.DEV_BAD_ID | O.DEV_DUP_ID | O.DEV_BAD_SAMPLED | O.DEV_NONFINITE
+                     | O.DEV_BAD_RESP)
+    assert np.all(st[1, :11] == 0) and np.all(row[1] == 0) and list(idx[1]) == [-1, -1]
+    for r in (2, 3, 4, 5, 6, 8):
+        assert np.all(np.isnan(st[r, [0, 1, 7]])), r
+        assert list(idx[r]) == [-1, -1], r
+        assert np.all(np.isnan(row[r])), r
+    assert int(n_valid.item()) == 11
+    # row 7 is valid: compare with the oracle
+    o = O.sc_row(zl[7].astype(np.float64), 1.0, ids[7], d["head_probs"][7].cpu().numpy(),
+                 a[7], rollout_logp=float(d["rollout_logp"][7]), advantage=-1.0,
+                 n_valid=11)
+    assert o["flags"] == 0
+    g = dict(stats=st[7], idx=idx[7], head_logp=out["head_logp"][7].cpu().numpy(),
+             coef=out["coef"][7].cpu().numpy(),
+             row=out["row"][7].view(torch.int16).cpu().numpy())
+    check_row("row 7 with -inf logit", g, o, A=-1.0, n_valid=11, row_dtype="bf16",
+              rlp=float(d["rollout_logp"][7]))
+
+
+# ---------------------------------------------------------------------------
+# Group normalisation, counts, step sums
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("G", [1, 4, 8, 33])
+def test_group_norm_matches_oracle(mode, G):
+    say(f"group_norm G={G} mode={mode}")
+    rng = np.random.default_rng(G * 10 + mode)
+    r = np.concatenate([
+        (rng.random(G * 16) < 0.5).astype(np.float32),
+        rng.normal(0, 1, G * 16).astype(np.float32),
+        np.full(G, 0.25, np.float32),
+        np.tile(np.array([1.0, 1.001], np.float32), G)[:G],
+        (rng.normal(0, 1, G) * 1e30).astype(np.float32),
+    ])
+    got = sc.group_norm(torch.from_numpy(r).to(DEV), G, mode=mode).cpu().numpy()
+    want = O.group_norm(r, G, mode=mode)
+    np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-6)
+    assert np.all(got[G * 32:G * 33] == 0)
+    if G > 1 and mode != 2:
+        pair = got[G * 33:G * 34]
+        assert len(set(pair.tolist())) == 2
+
+
+def test_count_valid_and_batch_sums():
+    say("count_valid / batch_sums on 3 chunks")
+    rng = np.random.default_rng(11)
+    n = 5000
+    chunks = []
+    for c in range(3):
+        resp = rng.integers(-1, 7, n).astype(np.int32)
+        st = rng.normal(0, 1, (n, 12)).astype(np.float32)
+        chunks.append((resp, st))
+    total = sum(int((r >= 0).sum()) for r, _ in chunks)
+    nv = torch.zeros(1, dtype=torch.int64, device=DEV)
+    for i, (resp, _) in enumerate(chunks):
+        sc.count_valid(torch.from_numpy(resp).to(DEV), out=nv, accumulate=i > 0)
+    assert int(nv.item()) == total
+    batch = torch.zeros(sc.NBATCH, dtype=torch.float64, device=DEV)
+    for i, (resp, st) in enumerate(chunks):
+        sc.batch_sums(torch.from_numpy(st).to(DEV), torch.from_numpy(resp).to(DEV), nv,
+                      out=batch, accumulate=i > 0)
+    b = batch.cpu().numpy()
+    rows = [dict(loss=s[7], k3=s[10], tv=s[8], kl=s[9], Q_H=s[4], P_H=s[3])
+            for resp, st in chunks for s, r in zip(st, resp) if r >= 0]
+    sums, means = O.batch_sums(rows, total)
+    for j, key in enumerate(("loss", "k3", "tv", "kl", "Q_H", "P_H")):
+        assert abs(b[j] - sums[key]) <= 1e-9 * max(1, abs(sums[key])), key
+        assert abs(b[8 + j] - means[key]) <= 1e-12 * max(1, abs(means[key])), key
+    assert b[6] == total and b[7] == 0
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads (V = 248,320), sampled rows
+# ---------------------------------------------------------------------------
+def sample_rows(n, count, seed, extra=()):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(n, count, replace=False).tolist()) | {0, n - 1} | set(extra)
+    return np.array(sorted(rows))
+
+
+@pytest.fixture(scope="module")
+def quick():
+    say("generate quick-check workload 8192 x 248320 bf16")
+    d = synthetic.quick_check(DEV)
+    torch.cuda.synchronize()
+    return d
+
+
+def test_quick_check_sampled_rows(quick):
+    d = quick
+    say("quick-check sc_correct bf16 dlogits (bench configuration)")
+    adv = sc.group_norm(d["rewards"], d["group_size"])
+    n_valid = sc.count_valid(d["resp_idx"])
+    out = run_correct(d, adv, n_valid, 1.0, O.MODE_DLOGITS, "bf16")
+    torch.cuda.synchronize()
+    assert int(out["status"].item()) == 0
+    rows = sample_rows(8192, 40, seed=21)
+    check_rows("quick-check dlogits bf16", d, out, rows, adv.cpu().numpy(), 8192, 1.0,
+               O.MODE_DLOGITS, "bf16")
+    # determinism: a second run is bitwise identical
+    out2 = run_correct(d, adv, n_valid, 1.0, O.MODE_DLOGITS, "bf16")
+    torch.cuda.synchronize()
+    for key in ("row_stats", "row_idx", "head_logp", "coef"):
+        assert torch.equal(out[key].view(torch.int32), out2[key].view(torch.int32)), key
+    assert torch.equal(out["row"].view(torch.int16), out2["row"].view(torch.int16))
+    # argmax and a_slot of every row against torch on the same logits
+    am = torch.argmax(d["logits"].float(), dim=1).to(torch.int32)
+    assert torch.equal(out["row_idx"][:, 0], am)
+    hit = (d["head_ids"] == d["sampled"][:, None])
+    slot = torch.where(hit.any(1), hit.int().argmax(1), torch.full_like(am, -1)).to(torch.int32)
+    assert torch.equal(out["row_idx"][:, 1], slot)
+
+
+def test_quick_check_two_call_and_f32_rows(quick):
+    d = quick
+    say("quick-check sc_logprobs + sc_center f32 score rows")
+    adv = sc.group_norm(d["rewards"], d["group_size"])
+    n_valid = sc.count_valid(d["resp_idx"])
+    st = sc.logprobs(d["logits"], d["head_ids"], d["sampled"], d["resp_idx"])
+    rows = sample_rows(8192, 12, seed=22)
+    sub = torch.as_tensor(rows, device=DEV)
+    dd = {k: (v[sub] if isinstance(v, torch.Tensor) and v.shape[0] == 8192 else v)
+          for k, v in d.items()}
+    stt = {k: v[sub].contiguous() for k, v in st.items()}
+    row_out = torch.empty(len(rows), synthetic.VOCAB, device=DEV)
+    sc.center(stt, dd["head_ids"].contiguous(), dd["head_probs"].contiguous(),
+              dd["sampled"].contiguous(), dd["resp_idx"].contiguous(), adv,
+              n_valid=n_valid, rollout_logp=dd["rollout_logp"].contiguous(),
+              logits=dd["logits"].contiguous(), row_out=row_out, row_mode=O.MODE_SCORE)
+    stt["row"] = row_out
+    torch.cuda.synchronize()
+    check_rows("quick-check two-call score f32", dd, stt, np.arange(len(rows)),
+               adv.cpu().numpy(), 8192, 1.0, O.MODE_SCORE, "f32")
+
+
+def test_full_step_chunk_with_padding():
+    lengths = synthetic.full_step_lengths()
+    say("full-step chunk 0 (16384 rows, padded responses)")
+    d = synthetic.full_step_chunk(DEV, 0, lengths)
+    resp_h = d["resp_idx"].cpu().numpy()
+    rewards = torch.from_numpy(
+        (np.random.default_rng(2).random(128) < 0.5).astype(np.float32)).to(DEV)
+    adv = sc.group_norm(rewards, 4)
+    # N_valid over the whole step (all 32 chunks), from the lengths
+    n_valid_total = int(np.sum(np.minimum(lengths, 4096)))
+    n_valid = torch.tensor([n_valid_total], dtype=torch.int64, device=DEV)
+    out = run_correct(d, adv, n_valid, 1.0, O.MODE_DLOGITS, "bf16")
+    torch.cuda.synchronize()
+    assert int(out["status"].item()) == 0
+    pad = np.nonzero(resp_h < 0)[0]
+    rows = sample_rows(16384, 24, seed=23, extra=pad[:3].tolist())
+    check_rows("full-step chunk 0", d, out, rows, adv.cpu().numpy(), n_valid_total, 1.0,
+               O.MODE_DLOGITS, "bf16")
+
+
+@pytest.mark.parametrize("sigma", [0.01, 0.1, 0.5])
+def test_stress_chunk(sigma):
+    say(f"distribution stress sigma={sigma} chunk 0 (16384 rows)")
+    d = synthetic.stress_chunk(DEV, 0, sigma)
+    adv = torch.tensor([1.0], device=DEV)
+    n_valid = torch.tensor([16384], dtype=torch.int64, device=DEV)
+    out = run_correct(d, adv, n_valid, 1.0, O.MODE_SCORE, "bf16")
+    torch.cuda.synchronize()
+    assert int(out["status"].item()) == 0
+    st = out["row_stats"].cpu().numpy()
+    clamp = np.nonzero((st[:, 2] < 1e-6) | (1 - st[:, 4] < 1e-6))[0]
+    rows = sample_rows(16384, 24, seed=int(sigma * 100), extra=clamp[:6].tolist())
+    say(f"  clamp-active rows in chunk: {len(clamp)}; checking {len(rows)} rows")
+    check_rows(f"stress sigma={sigma}", d, out, rows, np.array([1.0]), 16384, 1.0,
+               O.MODE_SCORE, "bf16")
