@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Throughput of the score-centering (SC) correction on one MI355X.
+
+One step is the whole per-position path over the quick-check workload
+(2 prompts x 4 responses x 1,024 tokens = 8,192 positions, V = 248,320,
+K = 128, bf16 trainer logits): exact valid-token count, group
+normalisation of the rewards, the fused correction kernel (trainer softmax
+statistics, gathers, mu_hat, loss, diagnostics and the bf16 dLogits row of
+every position) and the step reductions.  Inputs are resident in HBM before
+the timed region starts.
+
+Prints one JSON line.  Besides the throughput it reports the dominant
+kernel's roofline position (algorithmic bytes / its own event-timed launch
+duration) and the CPU oracle's throughput on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import multiprocessing as mp
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SC positions/sec at V=248,320 K=128 (1 GPU); achieved HBM GB/s vs peak"
+VOCAB, K = 248_320, 128
+PROMPTS, GROUP, TOKENS = 2, 4, 1024
+N_ROWS = PROMPTS * GROUP * TOKENS
+HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
+PROFILE = os.path.join(ROOT, "profiles", "sc_correct_quick_check_pmc.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "off_policy_logit_amd", "csrc", f)
+                  for f in ("sc_kernels.hip", "sc_device.h", "sc_internal.h", "sc_api.cpp")]
+
+# Algorithmic bytes of one position through the fused kernel (sc_correct with
+# a bf16 dLogits row): logits 2V, head ids 4K, head probs 4K, sampled,
+# resp_idx, rollout logp, advantage (4 B each) read; dLogits 2V, head logp 4K,
+# coefficients 4K, 12 fp32 statistics and 2 int32 indices written.
+BYTES_PER_POSITION = 2 * VOCAB + 8 * K + 16 + 2 * VOCAB + 8 * K + 48 + 8
+# Stats-only pass (sc_logprobs): logits 2V, ids 4K, sampled, resp_idx read;
+# log p at H 4K, 4 of the statistics and 2 indices written.
+BYTES_PER_POSITION_STATS = 2 * VOCAB + 4 * K + 8 + 4 * K + 16 + 8
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per launch from the committed PMC summary, or None when the
+    kernel sources changed since the counters were taken."""
+    if not os.path.exists(PROFILE):
+        return None
+    text = open(PROFILE).read()
+    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_src = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
+    if not (m_bytes and m_src) or m_src.group(1) != source_digest():
+        return None
+    return float(m_bytes.group(1))
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on a bounded sample of the same workload
+# ---------------------------------------------------------------------------
+_SAMPLE = None
+
+
+def _oracle_rows(idx):
+    from oracle import sc_oracle as O
+    z, ids, q, a, rlp = _SAMPLE
+    for i in idx:
+        O.sc_row(z[i], 1.0, ids[i], q[i], a[i], rollout_logp=rlp[i],
+                 advantage=0.5, n_valid=N_ROWS, row_mode=O.MODE_DLOGITS)
+    return len(idx)
+
+
+def cpu_baseline(rows):
+    """Time the oracle on `rows` positions generated on the host with the
+    quick-check generator.  Runs before anything touches the GPU, in a fork
+    pool of one process per available core (capped at 16)."""
+    global _SAMPLE
+    import synthetic
+    spec = synthetic.BigSpec(seed=1)
+    parts = [synthetic.big_chunk(spec, min(128, rows - r0), 9000 + r0, "cpu")
+             for r0 in range(0, rows, 128)]
+    z = np.concatenate([p["logits"].float().numpy() for p in parts])
+    ids = np.concatenate([p["head_ids"].numpy() for p in parts])
+    q = np.concatenate([p["head_probs"].numpy() for p in parts])
+    a = np.concatenate([p["sampled"].numpy() for p in parts])
+    rlp = np.concatenate([p["rollout_logp"].numpy() for p in parts])
+    _SAMPLE = (z, ids, q, a, rlp)
+    cores = min(16, len(os.sched_getaffinity(0)))
+    chunks = [list(range(i, rows, cores)) for i in range(cores)]
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(cores) as pool:
+        done = sum(pool.map(_oracle_rows, chunks))
+    dt = time.perf_counter() - t0
+    _SAMPLE = None
+    return dict(value=done / dt, unit="positions/s", cores=cores, kind="oracle",
+                sample=f"{rows} positions of the quick-check workload (V={VOCAB}, "
+                       f"K={K}, bf16 logits), full per-position outputs incl. the "
+                       f"dLogits row, float64, {dt:.1f} s wall")
+
+
+# ---------------------------------------------------------------------------
+# GPU
+# ---------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-rows", type=int, default=640,
+                    help="positions in the CPU-oracle sample (0 skips it)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB device copy before the timed region "
+                         "(reference kernel for PMC byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    cpu = cpu_baseline(args.cpu_rows) if args.cpu_rows > 0 else None
+
+    import torch
+    import synthetic
+    from off_policy_logit_amd import sc
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = synthetic.quick_check(dev, n_prompts=PROMPTS, group_size=GROUP, tokens=TOKENS)
+    n = d["logits"].shape[0]
+    assert n == N_ROWS and d["logits"].shape[1] == VOCAB
+    dlogits = torch.empty(n, VOCAB, dtype=torch.bfloat16, device=dev)
+    out = dict(row_stats=torch.empty(n, sc.NSTATS, device=dev),
+               row_idx=torch.empty(n, 2, dtype=torch.int32, device=dev),
+               head_logp=torch.empty(n, K, device=dev))
+    coef = torch.empty(n, K, device=dev)
+    n_valid = torch.empty(1, dtype=torch.int64, device=dev)
+    adv = torch.empty_like(d["rewards"])
+    batch = torch.empty(sc.NBATCH, dtype=torch.float64, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ev = []
+
+    def step(timed):
+        sc.count_valid(d["resp_idx"], out=n_valid)
+        sc.group_norm(d["rewards"], GROUP, out=adv)
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        sc.correct(d["logits"], d["head_ids"], d["head_probs"], d["sampled"],
+                   d["resp_idx"], adv, n_valid=n_valid, rollout_logp=d["rollout_logp"],
+                   row_out=dlogits, row_mode=sc.ROW_DLOGITS, out=out, coef=coef,
+                   dev_status=status)
+        if timed:
+            e1.record()
+            ev.append((e0, e1))
+        sc.batch_sums(out["row_stats"], d["resp_idx"], n_valid, out=batch)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item())}")
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    # stats-only pass (sc_logprobs), secondary line
+    st = dict(row_stats=out["row_stats"], row_idx=out["row_idx"], head_logp=out["head_logp"])
+    for _ in range(3):
+        sc.logprobs(d["logits"], d["head_ids"], d["sampled"], d["resp_idx"], out=st)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(5, args.steps // 2)
+    e0.record()
+    for _ in range(reps):
+        sc.logprobs(d["logits"], d["head_ids"], d["sampled"], d["resp_idx"], out=st)
+    e1.record()
+    torch.cuda.synchronize()
+    stats_ms = e0.elapsed_time(e1) / reps
+
+    bytes_launch = n * BYTES_PER_POSITION
+    achieved = bytes_launch / (kern_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile()
+    value = args.steps * n / dt
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dt / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "quick-check: 2 prompts x 4 responses x 1024 tokens "
+                               "= 8192 positions, V=248320, K=128, bf16 logits in, "
+                               "bf16 dLogits out",
+                   "positions": n, "vocab": VOCAB, "k": K,
+                   "logits_dtype": "bf16", "dlogits_dtype": "bf16"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "sc_correct (k_row bf16->bf16, fused)",
+                     "kernel_ms": round(kern_ms, 4),
+                     "bytes_per_launch": bytes_launch},
+        "cpu_baseline": cpu,
+        "secondary": {
+            "stats_only_positions_per_s": round(n / (stats_ms * 1e-3), 1),
+            "stats_only_kernel_ms": round(stats_ms, 4),
+            "stats_only_GBps": round(n * BYTES_PER_POSITION_STATS / (stats_ms * 1e-3) / 1e9, 1),
+        },
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -14,7 +14,7 @@ namespace {
 
 constexpr int64_t kMaxI32 = 2147483647;
 constexpr int kMaxK = 1024;
-constexpr size_t kMaxLds = 64 * 1024;
+constexpr size_t kMaxLds = 160 * 1024;  // gfx950 LDS per compute unit
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 size_t esize(int dtype) { return dtype == SC_BF16 ? 2 : 4; }
@@ -37,14 +37,13 @@ int cu_count(int* out) {
   return SC_OK;
 }
 
-// Workgroups per compute unit for the row kernels (tuning knob, read once).
-int row_wgs_per_cu() {
-  static int v = [] {
-    const char* e = std::getenv("SC_ROW_WGS_PER_CU");
-    int x = e ? std::atoi(e) : 0;
-    return (x >= 1 && x <= 8) ? x : 2;
-  }();
-  return v;
+// Resident workgroups per compute unit for the persistent row kernels.
+// SC_ROW_WGS_PER_CU (1..8) overrides the per-kernel default; it is read at
+// each call (a tuning knob).
+int row_wgs_per_cu(int kind) {
+  const char* e = std::getenv("SC_ROW_WGS_PER_CU");
+  const int x = e ? std::atoi(e) : 0;
+  return (x >= 1 && x <= 8) ? x : sc::kKindWgs[kind];
 }
 
 // Shared row-kernel argument checks; fills the geometry part of RowParams.
@@ -80,8 +79,8 @@ int check_rows(sc::RowParams& P, const void* logits, bool logits_needed, int log
 }
 
 // LDS layout of a row kernel; needs P.vector, P.vocab, P.k set.
-int layout(sc::RowParams& P) {
-  const int B = sc::kRowBlock;
+int layout(sc::RowParams& P, int kind) {
+  const int B = sc::kKindBlock[kind];
   const int64_t N = P.vector ? 16 / (int64_t)esize(P.in_dtype) : 1;
   const int64_t n_full = P.vocab / N;
   const int64_t jmax = (n_full + B - 1) / B;
@@ -91,6 +90,10 @@ int layout(sc::RowParams& P) {
   P.hs = hs;
   P.hshift = 32 - hbits;
   P.ke = P.k + 2;
+  int vs = 2, vbits = 1;
+  while (vs < 2 * P.ke) { vs <<= 1; ++vbits; }
+  P.vs = vs;
+  P.vshift = 32 - vbits;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = (off + bytes + 15) & ~size_t(15); return (int)o; };
   P.off_bitmap = take((size_t)P.bm_wpt * B * 4);
@@ -101,7 +104,10 @@ int layout(sc::RowParams& P) {
   P.off_hout = take((size_t)P.k * 4);
   P.off_entvec = take((size_t)P.ke * 4);
   P.off_entval = take((size_t)P.ke * N * 4);
-  P.off_entperm = take((size_t)P.ke * 4);
+  P.off_entslot = take((size_t)P.ke * N * 4);
+  P.off_vkey = take((size_t)vs * 4);
+  P.off_vval = take((size_t)vs * 4);
+  P.off_hid = take((size_t)P.k * 4);
   P.lds_bytes = off;
   return off <= kMaxLds ? SC_OK : SC_ERR_UNSUPPORTED;
 }
@@ -111,13 +117,13 @@ bool vector_ok(const void* p, int dtype, int64_t stride) {
 }
 
 int run_rows(sc::RowParams& P, int kind, void* stream) {
-  int st = layout(P);
+  int st = layout(P, kind);
   if (st != SC_OK) return st;
   if (P.n_rows == 0) return SC_OK;
   int cus = 0;
   st = cu_count(&cus);
   if (st != SC_OK) return st;
-  int64_t grid = std::min<int64_t>(P.n_rows, (int64_t)cus * row_wgs_per_cu());
+  int64_t grid = std::min<int64_t>(P.n_rows, (int64_t)cus * row_wgs_per_cu(kind));
   hipError_t e = sc::launch_row(P, kind, (int)grid, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SC_OK : SC_ERR_HIP;
 }

@@ -53,40 +53,47 @@ SC_DEV void wave_argmax(float& v, int& i) {
 
 // Workgroup reductions through a small LDS scratch.  Every thread of the
 // block must call them (they contain barriers); the result is returned to all
-// threads.  `red` needs B / 64 slots of the element type.
+// threads.  Each wave writes its partial, then every wave combines the B / 64
+// partials with a fixed butterfly, so the order is the same for all threads
+// and all runs.
 template <int B>
 SC_DEV void block_argmax(float& v, int& i, float* redf, int* redi) {
+  constexpr int NW = B / kWave;
   wave_argmax(v, i);
   const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
   __syncthreads();
   if (l == 0) { redf[w] = v; redi[w] = i; }
   __syncthreads();
-  v = redf[0]; i = redi[0];
+  float x = l < NW ? redf[l] : -INFINITY;
+  int xi = l < NW ? redi[l] : 0x7fffffff;
 #pragma unroll
-  for (int k = 1; k < B / kWave; ++k) {
-    float ov = redf[k]; int oi = redi[k];
-    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+  for (int o = NW / 2; o > 0; o >>= 1) {
+    const float ox = __shfl_xor(x, o);
+    const int oi = __shfl_xor(xi, o);
+    if (ox > x || (ox == x && oi < xi)) { x = ox; xi = oi; }
   }
+  v = __shfl(x, 0);
+  i = __shfl(xi, 0);
 }
 
-// Sum of N values per thread; fixed order (deterministic for a fixed B).
 template <int B, int N, typename F>
 SC_DEV void block_sum(F (&v)[N], F* red) {
+  constexpr int NW = B / kWave;
 #pragma unroll
   for (int n = 0; n < N; ++n) v[n] = wave_sum(v[n]);
   const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
   __syncthreads();
   if (l == 0) {
 #pragma unroll
-    for (int n = 0; n < N; ++n) red[n * (B / kWave) + w] = v[n];
+    for (int n = 0; n < N; ++n) red[n * NW + w] = v[n];
   }
   __syncthreads();
 #pragma unroll
   for (int n = 0; n < N; ++n) {
-    F s = red[n * (B / kWave)];
+    F x = l < NW ? red[n * NW + l] : F(0);
 #pragma unroll
-    for (int k = 1; k < B / kWave; ++k) s += red[n * (B / kWave) + k];
-    v[n] = s;
+    for (int o = NW / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    v[n] = __shfl(x, 0);
   }
 }
 
@@ -97,52 +104,72 @@ SC_DEV void block_sum(F (&v)[N], F* red) {
 // ---------------------------------------------------------------------------
 SC_DEV float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+// fp32 -> bf16 bits, round to nearest, ties to even (gfx950 converts in
+// hardware, two values per v_cvt_pk_bf16_f32).
 SC_DEV uint32_t f32_to_bf16(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+}
+SC_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
+// RowIO<T, VECTOR>: `raw` is one vector as loaded (16 bytes, or one element
+// on the scalar path); load() fetches vector n of a row, unpack() widens it to
+// fp32 and ninf() is a vector of -inf (padding of a partial tile).
 template <typename T, bool VECTOR> struct RowIO;
 
 template <> struct RowIO<uint16_t, true> {   // bf16, 16-byte vectors
   static constexpr int N = 8;
+  typedef u32x4 raw;
   template <bool NT>
-  static SC_DEV void load(const uint16_t* row, int64_t n, float (&v)[N]) {
+  static SC_DEV raw load(const uint16_t* row, int64_t n) {
     const u32x4* p = reinterpret_cast<const u32x4*>(row) + n;
-    u32x4 w = NT ? __builtin_nontemporal_load(p) : *p;
+    return NT ? __builtin_nontemporal_load(p) : *p;
+  }
+  static SC_DEV void unpack(const raw& w, float (&v)[N]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v[2 * i] = __uint_as_float(w[i] << 16);
       v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   }
+  static SC_DEV raw ninf() { u32x4 w = {0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u}; return w; }
+  static SC_DEV float elem(const raw& w, int i) {  // i is a compile-time constant after unrolling
+    return (i & 1) ? __uint_as_float(w[i >> 1] & 0xffff0000u) : __uint_as_float(w[i >> 1] << 16);
+  }
 };
 template <> struct RowIO<float, true> {      // fp32, 16-byte vectors
   static constexpr int N = 4;
+  typedef f32x4 raw;
   template <bool NT>
-  static SC_DEV void load(const float* row, int64_t n, float (&v)[N]) {
+  static SC_DEV raw load(const float* row, int64_t n) {
     const f32x4* p = reinterpret_cast<const f32x4*>(row) + n;
-    f32x4 w = NT ? __builtin_nontemporal_load(p) : *p;
+    return NT ? __builtin_nontemporal_load(p) : *p;
+  }
+  static SC_DEV void unpack(const raw& w, float (&v)[N]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = w[i];
   }
+  static SC_DEV raw ninf() { f32x4 w = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}; return w; }
+  static SC_DEV float elem(const raw& w, int i) { return w[i]; }
 };
 template <> struct RowIO<uint16_t, false> {  // bf16, one element at a time
   static constexpr int N = 1;
+  typedef uint32_t raw;
   template <bool NT>
-  static SC_DEV void load(const uint16_t* row, int64_t n, float (&v)[N]) {
-    v[0] = bf16_to_f32(row[n]);
-  }
+  static SC_DEV raw load(const uint16_t* row, int64_t n) { return row[n]; }
+  static SC_DEV void unpack(const raw& w, float (&v)[N]) { v[0] = __uint_as_float(w << 16); }
+  static SC_DEV raw ninf() { return 0xff80u; }
+  static SC_DEV float elem(const raw& w, int) { return __uint_as_float(w << 16); }
 };
 template <> struct RowIO<float, false> {     // fp32, one element at a time
   static constexpr int N = 1;
+  typedef float raw;
   template <bool NT>
-  static SC_DEV void load(const float* row, int64_t n, float (&v)[N]) {
-    v[0] = row[n];
-  }
+  static SC_DEV raw load(const float* row, int64_t n) { return row[n]; }
+  static SC_DEV void unpack(const raw& w, float (&v)[N]) { v[0] = w; }
+  static SC_DEV raw ninf() { return -INFINITY; }
+  static SC_DEV float elem(const raw& w, int) { return w; }
 };
 
 SC_DEV float load_elem(const uint16_t* row, int64_t i) { return bf16_to_f32(row[i]); }
@@ -154,15 +181,15 @@ template <> struct RowOut<uint16_t, 8> {
   static SC_DEV void store(uint16_t* row, int64_t n, const float (&v)[8]) {
     u32x4 w;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = f32_to_bf16(v[2 * i]) | (f32_to_bf16(v[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
     __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(row) + n);
   }
 };
 template <> struct RowOut<uint16_t, 4> {
   static SC_DEV void store(uint16_t* row, int64_t n, const float (&v)[4]) {
     u32x2 w;
-    w[0] = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-    w[1] = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+    w[0] = pack_bf16x2(v[0], v[1]);
+    w[1] = pack_bf16x2(v[2], v[3]);
     __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(row) + n);
   }
 };

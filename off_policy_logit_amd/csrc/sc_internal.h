@@ -7,7 +7,48 @@
 
 namespace sc {
 
-constexpr int kRowBlock = 512;  // threads per workgroup of the row kernels
+// Launch shape of each row kernel (compile-time; overridable for sweeps):
+// threads per workgroup, 16-byte vectors per thread per tile, resident
+// workgroups per compute unit, and the occupancy target (waves per SIMD, which
+// caps VGPRs at 512 / value).
+#ifndef SC_STATS_BLOCK
+#define SC_STATS_BLOCK 256
+#endif
+#ifndef SC_STATS_TILE
+#define SC_STATS_TILE 8
+#endif
+#ifndef SC_STATS_WGS
+#define SC_STATS_WGS 8
+#endif
+#ifndef SC_STATS_WAVES
+#define SC_STATS_WAVES 4
+#endif
+#ifndef SC_CENTER_BLOCK
+#define SC_CENTER_BLOCK 512
+#endif
+#ifndef SC_CENTER_TILE
+#define SC_CENTER_TILE 8
+#endif
+#ifndef SC_CENTER_WGS
+#define SC_CENTER_WGS 4
+#endif
+#ifndef SC_CENTER_WAVES
+#define SC_CENTER_WAVES 4
+#endif
+#ifndef SC_FUSED_BLOCK
+#define SC_FUSED_BLOCK 512
+#endif
+#ifndef SC_FUSED_TILE
+#define SC_FUSED_TILE 8
+#endif
+#ifndef SC_FUSED_WGS
+#define SC_FUSED_WGS 4
+#endif
+#ifndef SC_FUSED_WAVES
+#define SC_FUSED_WAVES 4
+#endif
+constexpr int kKindBlock[3] = {SC_STATS_BLOCK, SC_CENTER_BLOCK, SC_FUSED_BLOCK};
+constexpr int kKindWgs[3] = {SC_STATS_WGS, SC_CENTER_WGS, SC_FUSED_WGS};
 
 // Everything a row kernel needs, passed by value.
 struct RowParams {
@@ -36,9 +77,9 @@ struct RowParams {
   int row_mode;
   uint32_t* dev_status;
   // LDS layout (bytes into dynamic shared memory)
-  int hs, hshift, bm_wpt, ke;
+  int hs, hshift, vs, vshift, bm_wpt, ke;
   int off_bitmap, off_hkey, off_hval, off_headz, off_headp, off_hout;
-  int off_entvec, off_entval, off_entperm;
+  int off_entvec, off_entval, off_entslot, off_vkey, off_vval, off_hid;
   size_t lds_bytes;
 };
 

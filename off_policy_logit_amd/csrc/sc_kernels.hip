@@ -25,6 +25,9 @@
 #include "sc_device.h"
 #include "sc_internal.h"
 
+#include <cfloat>
+#include <type_traits>
+
 namespace sc {
 
 enum KernelKind { KIND_LOGPROBS = 0, KIND_CENTER = 1, KIND_CORRECT = 2 };
@@ -37,20 +40,22 @@ enum {
 enum { F_BAD_ID = 1, F_DUP_ID = 2, F_BAD_SAMPLED = 4, F_NONFINITE = 8, F_BAD_RESP = 16 };
 enum { M_DLOGITS = 0, M_SCORE = 1, M_CORRECTION = 2 };
 
-constexpr int kU = 4;  // vectors per thread per tile (divides 32)
-
-template <typename TI, typename TO, bool VECTOR, int B, int KIND>
-__global__ __launch_bounds__(B) void k_row(RowParams P) {
+// kU: 16-byte vectors per thread per pipelined tile (divides 32).
+template <typename TI, typename TO, bool VECTOR, int B, int KIND, int kU, int WAVES>
+__global__ __launch_bounds__(B) __attribute__((amdgpu_waves_per_eu(WAVES)))
+void k_row(RowParams P) {
+  static_assert(32 % kU == 0, "tile must divide the 32-bit bitmap word");
   using IO = RowIO<TI, VECTOR>;
+  using Raw = typename IO::raw;
   constexpr int N = IO::N;
   constexpr int NW = B / kWave;
   const bool has_out = (KIND != KIND_LOGPROBS) && P.row_out != nullptr;
   const int t = threadIdx.x;
   const int K = P.k;
-  const int64_t V = P.vocab;
-  const int64_t n_full = V / N;                 // full vectors per row
-  const int rem = (int)(V - n_full * N);        // elements of the partial vector
-  const int64_t J = n_full > t ? (n_full - 1 - t) / B + 1 : 0;  // my vectors
+  const int V = (int)P.vocab;
+  const int n_full = V / N;                 // full vectors per row
+  const int rem = V - n_full * N;        // elements of the partial vector
+  const int J = n_full > t ? (n_full - 1 - t) / B + 1 : 0;  // my vectors
   const float c = P.c;                          // log2(e) / T
 
   extern __shared__ __align__(16) unsigned char lds[];
@@ -59,14 +64,18 @@ __global__ __launch_bounds__(B) void k_row(RowParams P) {
   int* hval = reinterpret_cast<int*>(lds + P.off_hval);
   float* headz = reinterpret_cast<float*>(lds + P.off_headz);  // logits at H
   float* headp = reinterpret_cast<float*>(lds + P.off_headp);  // p at H
-  float* hout = reinterpret_cast<float*>(lds + P.off_hout);    // pass-2 value at H
+  float* hout = reinterpret_cast<float*>(lds + P.off_hout);    // log p / output at H
   int* ent_vec = reinterpret_cast<int*>(lds + P.off_entvec);
   float* ent_val = reinterpret_cast<float*>(lds + P.off_entval);
-  int* ent_perm = reinterpret_cast<int*>(lds + P.off_entperm);
+  int* ent_slot = reinterpret_cast<int*>(lds + P.off_entslot);  // slot or -1 per listed element
+  int* vkey = reinterpret_cast<int*>(lds + P.off_vkey);          // listed vector -> entry
+  int* vval = reinterpret_cast<int*>(lds + P.off_vval);
+  int* hid = reinterpret_cast<int*>(lds + P.off_hid);            // recorded id of each slot
 
   __shared__ float redf[4 * NW];
   __shared__ int redi[NW];
   __shared__ double redd[4 * NW];
+  __shared__ unsigned long long redu[NW];
   __shared__ int sh_ent;
   __shared__ uint32_t sh_flags;
   __shared__ float sh_za;
@@ -78,8 +87,27 @@ __global__ __launch_bounds__(B) void k_row(RowParams P) {
 
   if (t == 0) sh_status = 0;
 
-  for (int64_t row = blockIdx.x; row < P.n_rows; row += gridDim.x) {
-    const int resp = P.resp_idx ? P.resp_idx[row] : 0;
+  // The next row's response index, sampled id and (for K <= B) recorded ids
+  // are loaded one row ahead, so the stage does not wait on them.
+  int64_t row = blockIdx.x;
+  int nx_resp = 0, nx_a = 0, nx_id = -1;
+  if (row < P.n_rows) {
+    nx_resp = P.resp_idx ? P.resp_idx[row] : 0;
+    nx_a = P.sampled[row];
+    if (t < K) nx_id = P.head_ids[row * K + t];
+  }
+  for (; row < P.n_rows; row += gridDim.x) {
+    const int resp = nx_resp;
+    const int32_t a = nx_a;
+    const int my_id = nx_id;
+    {
+      const int64_t nr = row + gridDim.x;
+      if (nr < P.n_rows) {
+        nx_resp = P.resp_idx ? P.resp_idx[nr] : 0;
+        nx_a = P.sampled[nr];
+        if (t < K) nx_id = P.head_ids[nr * K + t];
+      }
+    }
     float* stats = P.row_stats + row * C_N;
     int32_t* ridx = P.row_idx + row * 2;
 
@@ -102,37 +130,101 @@ __global__ __launch_bounds__(B) void k_row(RowParams P) {
       }
       if (has_out) {
         TO* orow = reinterpret_cast<TO*>(P.row_out) + row * P.out_stride;
-        for (int64_t i = t; i < V; i += B) store_elem(orow, i, 0.f);
+        for (int i = t; i < V; i += B) store_elem(orow, i, 0.f);
       }
       continue;
     }
 
     const TI* zrow = reinterpret_cast<const TI*>(P.logits) + row * P.row_stride;
-    const int32_t a = P.sampled[row];
-    const bool a_ok = a >= 0 && (int64_t)a < V;
+    const bool a_ok = a >= 0 && a < V;
     const bool need_stage = (KIND != KIND_CENTER) || has_out;
+
+    // Vector j of this thread is row vector j * B + t.  Every thread owns at
+    // least Jmin vectors, so tiles of kU vectors below Jt are loaded with the
+    // same unconditional code by the whole workgroup; the remaining J - Jt
+    // vectors of a thread (fewer than kU + 1) are handled one at a time.
+    const int Jmin = n_full / B;
+    const int Jt = (Jmin / kU) * kU;
+    auto load_tile = [&](Raw (&r)[kU], int j0, auto nt) {
+      const int64_t n0 = (int64_t)j0 * B + t;
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        r[u] = IO::template load<decltype(nt)::value>(zrow, n0 + u * B);
+    };
+    auto load_one = [&](int j, auto nt) -> Raw {
+      return IO::template load<decltype(nt)::value>(zrow, (int64_t)j * B + t);
+    };
+    auto tile_bits = [&](int j0) -> uint32_t {
+      return (bitmap[(j0 >> 5) * B + t] >> (j0 & 31)) & ((1u << kU) - 1u);
+    };
+    auto append = [&](int n, const float (&v)[N]) {
+      const int e = atomicAdd(&sh_ent, 1);
+      if (e < P.ke) {
+        idset_insert(vkey, vval, (uint32_t)P.vs - 1, P.vshift, (int32_t)n, e);
+        ent_vec[e] = (int)n;
+#pragma unroll
+        for (int i = 0; i < N; ++i) ent_val[e * N + i] = v[i];
+      }
+    };
+
+    // List this thread's marked vectors (read again: the stream skipped them).
+    auto list_marked = [&]() {
+      for (int w = 0; w < P.bm_wpt; ++w) {
+        uint32_t word = bitmap[w * B + t];
+        while (word) {
+          const int j = w * 32 + __builtin_ctz(word);
+          word &= word - 1u;
+          float v[N];
+          IO::unpack(IO::template load<false>(zrow, (int64_t)j * B + t), v);
+          append(j * B + t, v);
+        }
+      }
+    };
+
+    // Map recorded ids and the sampled id onto the listed vectors: ent_slot
+    // gets the slot of every recorded element (-1 elsewhere), headz the
+    // recorded logits and sh_za the sampled logit.  Ends with a barrier.
+    auto resolve_slots = [&](int n_ent) {
+      for (int i = t; i < n_ent * N; i += B) ent_slot[i] = -1;
+      __syncthreads();
+      for (int k = t; k < K; k += B) {
+        const int id = hid[k];
+        if (id < 0 || id >= V) continue;
+        const int e = idset_find(vkey, vval, (uint32_t)P.vs - 1, P.vshift, id / N);
+        if (e < 0) continue;
+        headz[k] = ent_val[e * N + id % N];
+        ent_slot[e * N + id % N] = k;
+      }
+      if (t == 0 && a_ok) {
+        const int e = idset_find(vkey, vval, (uint32_t)P.vs - 1, P.vshift, a / N);
+        if (e >= 0) sh_za = ent_val[e * N + a % N];
+      }
+      __syncthreads();
+    };
 
     // ------------------------------------------------------------ stage
     if (need_stage) {
       for (int w = 0; w < P.bm_wpt; ++w) bitmap[w * B + t] = 0u;
       for (int i = t; i < P.hs; i += B) hkey[i] = -1;
+      for (int i = t; i < P.vs; i += B) vkey[i] = -1;
       for (int k = t; k < K; k += B) headz[k] = qnan;
     }
     if (t == 0) { sh_ent = 0; sh_flags = 0; sh_za = qnan; }
     __syncthreads();
     if (need_stage) {
       uint32_t fl = 0;
-      auto mark = [&](int64_t v) {
-        int64_t n = v / N;
+      auto mark = [&](int v) {
+        const int n = v / N;
         if (n < n_full) {
-          int64_t j = n / B;
-          int tt = (int)(n - j * B);
+          const int j = n / B;
+          const int tt = (int)(n - j * B);
           atomicOr(&bitmap[(j >> 5) * B + tt], 1u << (j & 31));
         }
       };
       for (int k = t; k < K; k += B) {
-        int32_t id = P.head_ids[row * K + k];
-        if (id < 0 || (int64_t)id >= V) {
+        const int32_t id = k == t ? my_id : P.head_ids[row * K + k];
+        hid[k] = id;
+        if (id < 0 || id >= V) {
           fl |= F_BAD_ID;
         } else {
           if (!idset_insert(hkey, hval, hmask, hshift, id, k)) fl |= F_DUP_ID;
@@ -146,7 +238,6 @@ __global__ __launch_bounds__(B) void k_row(RowParams P) {
       __syncthreads();
     }
 
-    // Quantities shared by the finalize and pass 2.
     float m = 0.f;        // row max of raw logits (pass-1 kernels)
     float log2s = 0.f;    // log2 sum_v 2^((z_v - m) c)
     float lse = 0.f, logp_a = 0.f, tau = 0.f;
@@ -154,60 +245,61 @@ __global__ __launch_bounds__(B) void k_row(RowParams P) {
 
     if (KIND != KIND_CENTER) {
       // ---------------------------------------------------------- pass 1
-      float m_t = -INFINITY, s_t = 0.f;
-      int am_t = 0x7fffffff;
-      for (int64_t j0 = 0; j0 < J; j0 += kU) {
-        float v[kU][N];
+      // Online update per vector: running max m_t (starts at -FLT_MAX so
+      // that all-(-inf) vectors rescale by 2^0 and add 2^-inf = 0), tail sum
+      // s_t relative to m_t, and the index of the vector that raised m_t
+      // (strictly, so the first of equal maxima is kept).
+      float m_t = -FLT_MAX, s_t = 0.f;
+      int am_vec = -1;
+      int am_direct = -1;
+      auto vec_update = [&](const float (&v)[N], int j) {
+        float vm = v[0];
+#pragma unroll
+        for (int i = 1; i < N; ++i) vm = fmaxf(vm, v[i]);
+        const float m_new = fmaxf(m_t, vm);
+        am_vec = vm > m_t ? j : am_vec;
+        s_t *= exp2_fast((m_t - m_new) * c);
+        m_t = m_new;
+      };
+      // Branch-free: marked vectors are summed too and the sum is dropped
+      // (they are resolved element by element after the stream).
+      auto process = [&](const Raw (&r)[kU], int j0) {
+        const uint32_t bits = tile_bits(j0);
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-          if (j0 + u < J) {
-            IO::template load<KIND == KIND_LOGPROBS>(zrow, (j0 + u) * B + t, v[u]);
-          } else {
+          float v[N];
+          IO::unpack(r[u], v);
+          vec_update(v, j0 + u);
+          float acc = 0.f;
 #pragma unroll
-            for (int i = 0; i < N; ++i) v[u][i] = -INFINITY;
-          }
+          for (int i = 0; i < N; ++i) acc += exp2_fast((v[i] - m_t) * c);
+          s_t += ((bits >> u) & 1u) ? 0.f : acc;
         }
-        const uint32_t bits = (bitmap[(j0 >> 5) * B + t] >> (j0 & 31)) & ((1u << kU) - 1u);
-        float tm = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < kU; ++u)
-#pragma unroll
-          for (int i = 0; i < N; ++i) tm = fmaxf(tm, v[u][i]);
-        if (tm > m_t) {
-          s_t *= exp2_fast((m_t - tm) * c);
-          int idx = 0x7fffffff;
-#pragma unroll
-          for (int u = kU - 1; u >= 0; --u)
-#pragma unroll
-            for (int i = N - 1; i >= 0; --i)
-              if (v[u][i] == tm) idx = (int)(((j0 + u) * B + t) * N + i);
-          am_t = idx;
-          m_t = tm;
+      };
+      {
+        std::integral_constant<bool, KIND == KIND_LOGPROBS> nt;
+        for (int j0 = 0; j0 < Jt; j0 += kU) {
+          Raw r[kU];
+          load_tile(r, j0, nt);
+          process(r, j0);
         }
+        for (int j = Jt; j < J; ++j) {
+          float v[N];
+          IO::unpack(load_one(j, nt), v);
+          vec_update(v, j);
+          float acc = 0.f;
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          if (j0 + u >= J) continue;
-          if ((bits >> u) & 1u) {
-            int e = atomicAdd(&sh_ent, 1);
-            if (e < P.ke) {
-              ent_vec[e] = (int)((j0 + u) * B + t);
-#pragma unroll
-              for (int i = 0; i < N; ++i) ent_val[e * N + i] = v[u][i];
-            }
-          } else {
-            float acc = 0.f;
-#pragma unroll
-            for (int i = 0; i < N; ++i) acc += exp2_fast((v[u][i] - m_t) * c);
-            s_t += acc;
-          }
+          for (int i = 0; i < N; ++i) acc += exp2_fast((v[i] - m_t) * c);
+          s_t += ((bitmap[(j >> 5) * B + t] >> (j & 31)) & 1u) ? 0.f : acc;
         }
       }
+      list_marked();
       // The partial last vector (vocab not a multiple of N) always goes to the
-      // LDS list; its thread is the owner of vector index n_full.
+      // LDS list; its owner is the thread of vector index n_full.
       if (rem > 0 && t == (int)(n_full % B)) {
         float v[N];
         float tm = -INFINITY;
-        int idx = 0x7fffffff;
+        int idx = -1;
 #pragma unroll
         for (int i = 0; i < N; ++i) {
           v[i] = i < rem ? load_elem(zrow, n_full * N + i) : -INFINITY;
@@ -216,14 +308,20 @@ __global__ __launch_bounds__(B) void k_row(RowParams P) {
         if (tm > m_t) {
           s_t *= exp2_fast((m_t - tm) * c);
           m_t = tm;
-          am_t = idx;
+          am_direct = idx;
         }
-        int e = atomicAdd(&sh_ent, 1);
-        if (e < P.ke) {
-          ent_vec[e] = (int)n_full;
+        append(n_full, v);
+      }
+      // Element index of my maximum: the first element equal to m_t in the
+      // vector that raised it (read again, one vector per thread and row).
+      int am_t = 0x7fffffff;
+      if (am_direct >= 0) {
+        am_t = am_direct;
+      } else if (am_vec >= 0) {
+        const Raw rv = IO::template load<false>(zrow, (int64_t)am_vec * B + t);
 #pragma unroll
-          for (int i = 0; i < N; ++i) ent_val[e * N + i] = v[i];
-        }
+        for (int i = N - 1; i >= 0; --i)
+          if (IO::elem(rv, i) == m_t) am_t = (int)((am_vec * B + t) * N + i);
       }
 
       // ---------------------------------------------------------- finalize
@@ -232,32 +330,23 @@ __global__ __launch_bounds__(B) void k_row(RowParams P) {
       block_argmax<B>(mv, mi, redf, redi);
       m = mv;
       argmax = mi;
-      // my tail sum at the row max
-      float tail_part = (m_t == -INFINITY) ? 0.f : s_t * exp2_fast((m_t - m) * c);
-      // Resolve the marked vectors element by element, in increasing vector
-      // order (rank sort), so that every sum below has a fixed order.
+      float tail_part = s_t * exp2_fast((m_t - m) * c);
+      // Resolve the listed vectors: each recorded id (and the sampled id)
+      // finds its vector's list entry through the vector map; every other
+      // listed element is a tail term.  Tail terms are summed as 64-bit
+      // fixed point (2^-52 units; each term is <= 1 since z <= m): integer
+      // sums are exact, so the total does not depend on the listing order.
       const int n_ent = min(sh_ent, P.ke);
-      for (int e = t; e < n_ent; e += B) {
-        const int my = ent_vec[e];
-        int r = 0;
-        for (int j = 0; j < n_ent; ++j) r += ent_vec[j] < my ? 1 : 0;
-        ent_perm[r] = e;
+      resolve_slots(n_ent);
+      unsigned long long tail_fx = 0ull;
+      for (int i = t; i < n_ent * N; i += B) {
+        const int vid = ent_vec[i / N] * N + (i % N);
+        if (vid < V && ent_slot[i] < 0)
+          tail_fx += (unsigned long long)(exp2_fast((ent_val[i] - m) * c) * 0x1p52f);
       }
-      __syncthreads();
-      for (int r = t; r < n_ent; r += B) {
-        const int e = ent_perm[r];
-#pragma unroll
-        for (int l = 0; l < N; ++l) {
-          const int64_t vid = (int64_t)ent_vec[e] * N + l;
-          if (vid >= V) continue;
-          const float z = ent_val[e * N + l];
-          const int slot = idset_find(hkey, hval, hmask, hshift, (int32_t)vid);
-          if (slot >= 0) headz[slot] = z;
-          else tail_part += exp2_fast((z - m) * c);
-          if (vid == a) sh_za = z;
-        }
-      }
-      __syncthreads();
+      unsigned long long fx[1] = {tail_fx};
+      block_sum<B, 1>(fx, redu);
+      tail_part += t == 0 ? (float)((double)fx[0] * 0x1p-52) : 0.f;
       float head_part = 0.f;
       for (int k = t; k < K; k += B) head_part += exp2_fast((headz[k] - m) * c);
       float sums[2] = {tail_part, head_part};
@@ -268,16 +357,15 @@ __global__ __launch_bounds__(B) void k_row(RowParams P) {
       tau = sums[0] / s;
       const float za = sh_za;
       logp_a = ((za - m) * c - log2s) * kLn2;
-      // log p and p at H; non-finite checks
       uint32_t fl = 0;
       for (int k = t; k < K; k += B) {
         const float hz = headz[k];
         if (hz == -INFINITY) fl |= F_NONFINITE;
         const float l2 = (hz - m) * c - log2s;
         headp[k] = exp2_fast(l2 + 32.f) * 0x1p-32f;  // subnormal-exact
-        hout[k] = l2 * kLn2;  // log p at H (reused below)
+        hout[k] = l2 * kLn2;                          // log p at H
       }
-      if (!(s < INFINITY) || !(m > -INFINITY) || !(m < INFINITY) || za == -INFINITY)
+      if (!(s < INFINITY) || !(m > -FLT_MAX) || !(m < INFINITY) || za == -INFINITY)
         fl |= F_NONFINITE;
       if (fl) atomicOr(&sh_flags, fl);
       a_slot = a_ok ? idset_find(hkey, hval, hmask, hshift, a) : -1;
@@ -320,7 +408,6 @@ __global__ __launch_bounds__(B) void k_row(RowParams P) {
     }
 
     // -------------------------------------------------------------- center
-    // Q_H and P_H in float64
     double d1[2] = {0.0, 0.0};
     for (int k = t; k < K; k += B) {
       d1[0] += (double)P.head_probs[row * K + k];
@@ -340,7 +427,7 @@ __global__ __launch_bounds__(B) void k_row(RowParams P) {
       if (P.coef) P.coef[row * K + k] = flags ? qnan : (float)ck;
       d2[0] += ck * lp;
       d2[1] += fabs(q - p);
-      if (q > 0.0) d2[2] += q * (log(q) - lp);
+      if (q > 0.0) d2[2] += q * ((double)logf((float)q) - lp);
     }
     block_sum<B, 3>(d2, redd);
 
@@ -350,11 +437,11 @@ __global__ __launch_bounds__(B) void k_row(RowParams P) {
     const double loss = -A * ((double)logp_a - d2[0]);
     const double tv = 0.5 * (d2[1] + fabs(rho - 1.0) * taud);
     double kl = d2[2];
-    if (rho * taud > 0.0) kl += rho * taud * log(rho);
+    if (rho * taud > 0.0) kl += rho * taud * (double)logf((float)rho);
     double k3 = (double)qnan;
     if (P.rollout_logp) {
       const double d = (double)logp_a - (double)P.rollout_logp[row];
-      k3 = expm1(d) - d;
+      k3 = (double)expm1f((float)d) - d;
     }
 
     if (t == 0) {
@@ -411,53 +498,73 @@ __global__ __launch_bounds__(B) void k_row(RowParams P) {
 
     const bool neg = alpha < 0.0;
     // p_v = 2^((z_v - mref) c - lref); value = sign(alpha) 2^((z_v - mref) c + off)
+    // computed as 2^(y + 32) 2^-32 so that results below 2^-126 stay exact
+    // subnormals (the exp2 instruction flushes them).
     const float mref = (KIND == KIND_CORRECT) ? m : 0.f;
     const double lref = (KIND == KIND_CORRECT) ? (double)log2s
                                                : (double)lse * 1.4426950408889634;
-    // +32 here and the 2^-32 below keep results under 2^-126 exact
-    // subnormals (the exp2 instruction flushes them).
-    const float off = (float)(log2(fabs(alpha)) - lref + 32.0);
+    const float off = log2f(fabsf((float)alpha)) - (float)lref + 32.f;
     const float add_a = (float)scale;
     TO* orow = reinterpret_cast<TO*>(P.row_out) + row * P.out_stride;
 
-    auto slow_value = [&](int64_t vid, float z) -> float {
-      const int slot = idset_find(hkey, hval, hmask, hshift, (int32_t)vid);
-      if (slot >= 0) return hout[slot];
-      float e = exp2_fast(fmaf(z - mref, c, off)) * 0x1p-32f;
-      e = neg ? -e : e;
-      if (vid == a) e += add_a;
-      return e;
+    // Stream the row; marked vectors are not stored here (the sc_center kind
+    // lists them now, the fused kind listed them in pass 1).
+    // One output vector; the sign is a compile-time choice so that the
+    // negation folds into the bf16 conversion.
+    auto out_vec = [&](const Raw& r, float (&o)[N], auto negc) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const float e = exp2_fast(fmaf(IO::elem(r, i) - mref, c, off)) * 0x1p-32f;
+        o[i] = decltype(negc)::value ? -e : e;
+      }
     };
-
-    for (int64_t j0 = 0; j0 < J; j0 += kU) {
-      float v[kU][N];
+    auto stream2 = [&](auto negc) {
+      std::integral_constant<bool, true> nt;
+      for (int j0 = 0; j0 < Jt; j0 += kU) {
+        Raw r[kU];
+        load_tile(r, j0, nt);
+        const uint32_t bits = tile_bits(j0);
 #pragma unroll
-      for (int u = 0; u < kU; ++u)
-        if (j0 + u < J) IO::template load<true>(zrow, (j0 + u) * B + t, v[u]);
-      const uint32_t bits = (bitmap[(j0 >> 5) * B + t] >> (j0 & 31)) & ((1u << kU) - 1u);
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        if (j0 + u >= J) continue;
-        const int64_t n = (j0 + u) * B + t;
-        float o[N];
-        if ((bits >> u) & 1u) {
-#pragma unroll
-          for (int i = 0; i < N; ++i) o[i] = slow_value(n * N + i, v[u][i]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < N; ++i) {
-            const float e = exp2_fast(fmaf(v[u][i] - mref, c, off)) * 0x1p-32f;
-            o[i] = neg ? -e : e;
-          }
+        for (int u = 0; u < kU; ++u) {
+          float o[N];
+          out_vec(r[u], o, negc);
+          if (!((bits >> u) & 1u)) RowOut<TO, N>::store(orow, (j0 + u) * B + t, o);
         }
-        RowOut<TO, N>::store(orow, n, o);
       }
+      for (int j = Jt; j < J; ++j) {
+        if ((bitmap[(j >> 5) * B + t] >> (j & 31)) & 1u) continue;
+        float o[N];
+        out_vec(load_one(j, nt), o, negc);
+        RowOut<TO, N>::store(orow, j * B + t, o);
+      }
+    };
+    if (neg) stream2(std::true_type{});
+    else stream2(std::false_type{});
+    if (KIND == KIND_CENTER) list_marked();
+    if (KIND == KIND_CENTER && rem > 0 && t == (int)(n_full % B)) {
+      float v[N];
+#pragma unroll
+      for (int i = 0; i < N; ++i) v[i] = i < rem ? load_elem(zrow, n_full * N + i) : 0.f;
+      append(n_full, v);
     }
-    if (rem > 0 && t == (int)(n_full % B)) {
-      for (int i = 0; i < rem; ++i) {
-        const int64_t vid = n_full * N + i;
-        store_elem(orow, vid, slow_value(vid, load_elem(zrow, vid)));
+    __syncthreads();
+    // Marked vectors: exact values, one element per thread.
+    const int n_ent = min(sh_ent, P.ke);
+    if (KIND == KIND_CENTER) resolve_slots(n_ent);
+    for (int i = t; i < n_ent * N; i += B) {
+      const int e = i / N, l = i - e * N;
+      const int vid = ent_vec[e] * N + l;
+      if (vid >= V) continue;
+      const int slot = ent_slot[i];
+      float val;
+      if (slot >= 0) {
+        val = hout[slot];
+      } else {
+        val = exp2_fast(fmaf(ent_val[i] - mref, c, off)) * 0x1p-32f;
+        val = neg ? -val : val;
+        if (vid == a) val += add_a;
       }
+      store_elem(orow, vid, val);
     }
   }
 
@@ -542,8 +649,18 @@ __global__ __launch_bounds__(B) void k_batch_sums(const float* __restrict__ st,
 // ---------------------------------------------------------------------------
 template <typename TI, typename TO, bool VECTOR, int B, int KIND>
 static hipError_t launch_row_t(const RowParams& P, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_row<TI, TO, VECTOR, B, KIND>), dim3(grid), dim3(B),
-                     P.lds_bytes, s, P);
+  constexpr int U = KIND == KIND_LOGPROBS ? SC_STATS_TILE
+                  : KIND == KIND_CENTER ? SC_CENTER_TILE : SC_FUSED_TILE;
+  constexpr int W = KIND == KIND_LOGPROBS ? SC_STATS_WAVES
+                  : KIND == KIND_CENTER ? SC_CENTER_WAVES : SC_FUSED_WAVES;
+  auto kern = k_row<TI, TO, VECTOR, B, KIND, U, W>;
+  if (P.lds_bytes > 64 * 1024) {  // large K: opt in to more than 64 KiB of LDS
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)P.lds_bytes);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(B), P.lds_bytes, s, P);
   return hipGetLastError();
 }
 
@@ -564,9 +681,9 @@ static hipError_t launch_row_b(const RowParams& P, int grid, hipStream_t s) {
 
 hipError_t launch_row(const RowParams& P, int kind, int grid, hipStream_t s) {
   switch (kind) {
-    case KIND_LOGPROBS: return launch_row_b<kRowBlock, KIND_LOGPROBS>(P, grid, s);
-    case KIND_CENTER: return launch_row_b<kRowBlock, KIND_CENTER>(P, grid, s);
-    default: return launch_row_b<kRowBlock, KIND_CORRECT>(P, grid, s);
+    case KIND_LOGPROBS: return launch_row_b<SC_STATS_BLOCK, KIND_LOGPROBS>(P, grid, s);
+    case KIND_CENTER: return launch_row_b<SC_CENTER_BLOCK, KIND_CENTER>(P, grid, s);
+    default: return launch_row_b<SC_FUSED_BLOCK, KIND_CORRECT>(P, grid, s);
   }
 }
 

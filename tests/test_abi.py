@@ -70,6 +70,7 @@ def test_logprobs_zero_rows_is_a_noop_without_hip():
 
 def test_lds_limit_is_reported_as_unsupported():
     assert logprobs(V=2 ** 30, stride=2 ** 30, k=1024) == UNSUP
+    assert logprobs(V=2 ** 24, stride=2 ** 24, k=1024) == UNSUP
 
 
 def center(fn="sc_center", **kw):
