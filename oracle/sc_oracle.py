@@ -72,6 +72,12 @@ DEV_BAD_SAMPLED = 4
 DEV_NONFINITE = 8
 DEV_BAD_RESP = 16
 
+# Importance-weighting modes (Score Centering page, SC settings table:
+# is_mode none / tis / mis with tis_max 2.0 and the MIS interval [0.5, 5.0]).
+IS_NONE = 0
+IS_TIS = 1
+IS_MIS = 2
+
 # Row output modes for the full-vocabulary row.
 MODE_DLOGITS = 0      # -A / (T * N_valid) * g
 MODE_SCORE = 1        # g, the centered score
@@ -118,15 +124,37 @@ def _row_flags(z, head_ids, sampled):
     return flags
 
 
+def is_weight(w, is_mode, lo, hi):
+    """Stop-gradient weight of one token from its ratio w = p(a) / mu(a).
+
+    Truncated IS replaces w by min(w, w_max) (lecture notes "RL systems for
+    agents", section 1, where the truncated weight is defined); masked IS keeps
+    the token, weighted by w, only when lo <= w <= hi and drops it otherwise
+    (reading of "masked importance sampling" with its acceptance interval,
+    Score Centering page, SC settings).
+    """
+    if is_mode == IS_NONE:
+        return 1.0
+    if is_mode == IS_TIS:
+        return min(w, hi)
+    if is_mode == IS_MIS:
+        return w if lo <= w <= hi else 0.0
+    raise ValueError("is_mode")
+
+
 def sc_row(z, temperature, head_ids, head_probs, sampled, rollout_logp=None,
-           advantage=1.0, n_valid=1, row_mode=MODE_DLOGITS):
+           advantage=1.0, n_valid=1, row_mode=MODE_DLOGITS, is_mode=IS_NONE,
+           is_lo=0.5, is_hi=2.0, centering=True):
     """All per-position SC outputs of one valid row, by definition, in float64.
 
     Arguments: z (V,) logits (any float dtype, widened exactly), temperature T,
     head_ids (K,) recorded ids H, head_probs (K,) recorded probabilities q,
     sampled id a, rollout_logp = log mu(a) recorded by the rollout (or None),
     advantage A of the row's response, n_valid = number of valid positions of
-    the whole step, row_mode selecting the full-vocabulary row to return.
+    the whole step, row_mode selecting the full-vocabulary row to return,
+    is_mode / is_lo / is_hi the importance weighting of the token (needs
+    rollout_logp), centering=False dropping the centering term (the grpo_mis
+    ablation: "centering disabled").
 
     Returns a dict; see the keys at the end.
     """
@@ -144,7 +172,8 @@ def sc_row(z, temperature, head_ids, head_probs, sampled, rollout_logp=None,
         return dict(flags=flags, lse=nan, logp_a=nan, argmax=-1, a_slot=-1,
                     head_logp=np.full(K, nan), P_H=nan, Q_H=nan, tau=nan,
                     rho=nan, coef=np.full(K, nan), S=nan, loss=nan, tv=nan,
-                    kl=nan, k3=nan, row=np.full(V, nan))
+                    kl=nan, k3=nan, entropy=nan, w=nan, weight=nan,
+                    rev_kl=nan, row=np.full(V, nan))
 
     # Trainer softmax at the rollout temperature; gather at H and at a.
     logp, lse = trainer_log_softmax(z, T)
@@ -166,18 +195,30 @@ def sc_row(z, temperature, head_ids, head_probs, sampled, rollout_logp=None,
     # rho with both clamps, as printed.
     rho = max(1.0 - Q_H, CLAMP) / max(tau, CLAMP)
 
+    # Importance ratio of the sampled token and its stop-gradient weight.
+    if rollout_logp is None:
+        if is_mode != IS_NONE:
+            raise ValueError("importance weighting needs rollout_logp")
+        w = float("nan")
+    else:
+        w = math.exp(logp_a - float(rollout_logp))
+    weight = is_weight(w, is_mode, is_lo, is_hi)
+
     # Stop-gradient coefficients and the token loss.
     coef = q - rho * p_H
-    loss = -float(advantage) * (logp_a - float(np.sum(coef * head_logp)))
+    centered = float(np.sum(coef * head_logp)) if centering else 0.0
+    loss = -float(advantage) * weight * (logp_a - centered)
 
     # Behaviour estimate mu_hat: recorded head, tail proportional to p.
     mu_hat = rho * p
     mu_hat[ids] = q
     S = float(np.sum(mu_hat))
 
-    # Centered score: gradient of the bracket with respect to u = z / T.
-    g = -mu_hat - (1.0 - S) * p
+    # Centered score: gradient of the bracket with respect to u = z / T
+    # (without centering: the plain score e_a - p), times the weight.
+    g = (-mu_hat - (1.0 - S) * p) if centering else -p.copy()
     g[a] += 1.0
+    g *= weight
 
     if row_mode == MODE_DLOGITS:
         row = (-float(advantage) / (T * float(n_valid))) * g
@@ -197,10 +238,20 @@ def sc_row(z, temperature, head_ids, head_probs, sampled, rollout_logp=None,
     else:
         d = logp_a - float(rollout_logp)
         k3 = math.expm1(d) - d
+    # Extra per-position signals (lecture notes, section 7, list of debugging
+    # signals: entropy and the largest importance weight): the trainer
+    # entropy -sum p log p and the reverse divergence KL(p || mu_hat).
+    ppos = p > 0
+    entropy = -float(np.sum(p[ppos] * logp[ppos]))
+    if np.any(ppos & (mu_hat <= 0)):
+        rev_kl = float("inf")
+    else:
+        rev_kl = float(np.sum(p[ppos] * (logp[ppos] - np.log(mu_hat[ppos]))))
 
     return dict(flags=0, lse=lse, logp_a=logp_a, argmax=argmax, a_slot=a_slot,
                 head_logp=head_logp, P_H=P_H, Q_H=Q_H, tau=tau, rho=rho,
-                coef=coef, S=S, loss=loss, tv=tv, kl=kl, k3=k3, row=row)
+                coef=coef, S=S, loss=loss, tv=tv, kl=kl, k3=k3,
+                entropy=entropy, w=w, weight=weight, rev_kl=rev_kl, row=row)
 
 
 def masked_row(V, K):
@@ -208,7 +259,7 @@ def masked_row(V, K):
     return dict(flags=0, lse=0.0, logp_a=0.0, argmax=-1, a_slot=-1,
                 head_logp=np.zeros(K), P_H=0.0, Q_H=0.0, tau=0.0, rho=0.0,
                 coef=np.zeros(K), S=0.0, loss=0.0, tv=0.0, kl=0.0, k3=0.0,
-                row=np.zeros(V))
+                entropy=0.0, w=0.0, weight=0.0, rev_kl=0.0, row=np.zeros(V))
 
 
 def group_norm(rewards, group_size, mode=0, eps=1e-6):
@@ -236,18 +287,24 @@ def group_norm(rewards, group_size, mode=0, eps=1e-6):
     return out.reshape(-1)
 
 
+BATCH_KEYS = ("loss", "k3", "tv", "kl", "Q_H", "P_H", "entropy", "rev_kl")
+
+
 def batch_sums(rows, n_valid):
     """Step-level reductions over valid rows (global generated-token mean).
 
     rows: iterable of sc_row() dicts of the valid rows.  Returns the sums and
-    the means over n_valid, in float64: loss, k3, tv, kl, Q_H, P_H.
+    the means over n_valid, in float64, of BATCH_KEYS, plus the largest
+    importance ratio w of the step under the key "max_w".
     """
-    keys = ("loss", "k3", "tv", "kl", "Q_H", "P_H")
-    sums = {k: 0.0 for k in keys}
+    sums = {k: 0.0 for k in BATCH_KEYS}
+    max_w = float("-inf")
     for r in rows:
-        for k in keys:
+        for k in BATCH_KEYS:
             sums[k] += float(r[k])
-    means = {k: sums[k] / float(n_valid) for k in keys}
+        max_w = max(max_w, float(r["w"]))
+    means = {k: sums[k] / float(n_valid) for k in BATCH_KEYS}
+    means["max_w"] = max_w
     return sums, means
 
 

@@ -369,10 +369,153 @@ def test_group_norm_keeps_fractional_rewards_and_large_values():
 
 
 def test_batch_sums_global_token_mean():
-    rows = [dict(loss=1.0, k3=0.1, tv=0.2, kl=0.3, Q_H=0.9, P_H=0.8),
-            dict(loss=3.0, k3=0.3, tv=0.4, kl=0.5, Q_H=0.7, P_H=0.6)]
+    rows = [dict(loss=1.0, k3=0.1, tv=0.2, kl=0.3, Q_H=0.9, P_H=0.8, entropy=2.0,
+                 rev_kl=0.1, w=1.5),
+            dict(loss=3.0, k3=0.3, tv=0.4, kl=0.5, Q_H=0.7, P_H=0.6, entropy=4.0,
+                 rev_kl=0.3, w=0.5)]
     sums, means = O.batch_sums(rows, 4)
-    _close([sums["loss"], means["loss"], means["Q_H"]], [4.0, 1.0, 0.4])
+    _close([sums["loss"], means["loss"], means["Q_H"], means["entropy"]],
+           [4.0, 1.0, 0.4, 1.5])
+    assert means["max_w"] == 1.5
+
+
+# --------------------------------------------------------------------------
+# Importance weighting (TIS / MIS) and centering off
+# --------------------------------------------------------------------------
+def test_tis_worked_example_from_the_lecture_notes():
+    with open(os.path.join(GOLDEN, "tis_page_example.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        # a two-token vocabulary whose trainer probability of token 0 is pi
+        z = np.log(np.array([c["pi"], 1.0 - c["pi"]]))
+        r = O.sc_row(z, 1.0, [1], [0.1], 0, rollout_logp=math.log(c["mu"]),
+                     is_mode=O.IS_TIS, is_hi=c["w_max"])
+        _close(r["w"], c["w"], 1e-12)
+        _close(r["weight"], c["weight"], 1e-12)
+        _close(max(0.0, c["pi"] - c["w_max"] * c["mu"]) if c["w"] > c["w_max"] else 0.0,
+               c["bias_coef"], 1e-12)
+
+
+def _behaviour_and_trainer(rng, V):
+    pi = rng.dirichlet(np.ones(V) * 0.7)
+    mu = rng.dirichlet(np.ones(V) * 0.7)
+    return pi, mu
+
+
+def test_tis_bias_equals_the_exact_formula_by_brute_force():
+    # E_pi[f] - E_mu[min(w, w_max) f] = sum_{w > w_max} (pi - w_max mu) f
+    # (lecture notes, section 1), with the oracle's weight for every token.
+    rng = np.random.default_rng(31)
+    for trial in range(30):
+        V = int(rng.integers(3, 12))
+        pi, mu = _behaviour_and_trainer(rng, V)
+        f = rng.normal(size=V)
+        z = np.log(pi)
+        wmax = float(rng.uniform(1.0, 3.0))
+        weights = np.array([O.sc_row(z, 1.0, [0], [0.1], a, rollout_logp=math.log(mu[a]),
+                                     is_mode=O.IS_TIS, is_hi=wmax)["weight"]
+                            for a in range(V)])
+        lhs = np.sum(pi * f) - np.sum(mu * weights * f)
+        w = pi / mu
+        rhs = np.sum(np.where(w > wmax, pi - wmax * mu, 0.0) * f)
+        assert abs(lhs - rhs) < 1e-12
+
+
+def test_mis_keeps_exactly_the_accepted_tokens():
+    # With weight w inside [lo, hi] and 0 outside, E_mu[weight f] is the
+    # trainer expectation restricted to accepted tokens.
+    rng = np.random.default_rng(32)
+    for trial in range(30):
+        V = int(rng.integers(3, 12))
+        pi, mu = _behaviour_and_trainer(rng, V)
+        f = rng.normal(size=V)
+        z = np.log(pi)
+        weights = np.array([O.sc_row(z, 1.0, [0], [0.1], a, rollout_logp=math.log(mu[a]),
+                                     is_mode=O.IS_MIS, is_lo=0.5, is_hi=5.0)["weight"]
+                            for a in range(V)])
+        w = pi / mu
+        acc = (w >= 0.5) & (w <= 5.0)
+        assert abs(np.sum(mu * weights * f) - np.sum(np.where(acc, pi, 0) * f)) < 1e-12
+
+
+@pytest.mark.parametrize("mode", ["tis", "mis"])
+def test_weighted_and_uncentered_gradients_match_autograd(mode):
+    # loss = -sg(A) sg(weight) [log p_a - centering sum_H sg(c) log p]
+    rng = np.random.default_rng(33)
+    is_mode = O.IS_TIS if mode == "tis" else O.IS_MIS
+    for V in (8, 16):
+        for trial in range(15):
+            K = int(rng.integers(1, V))
+            z, ids, q, a = _rand_case(rng, V, K)
+            rlp = float(np.log(rng.uniform(0.01, 0.9)))
+            A, n_valid = float(rng.normal()), 5
+            for centering in (True, False):
+                r = O.sc_row(z, 1.0, ids, q, a, rollout_logp=rlp, advantage=A,
+                             n_valid=n_valid, is_mode=is_mode, is_lo=0.5, is_hi=2.0,
+                             centering=centering)
+                zt = torch.tensor(z, dtype=torch.float64, requires_grad=True)
+                logp = torch.log_softmax(zt, 0)
+                p = logp.exp()
+                w = math.exp(float(logp[a].detach()) - rlp)
+                weight = min(w, 2.0) if mode == "tis" else (w if 0.5 <= w <= 2.0 else 0.0)
+                rho = torch.clamp(1 - torch.tensor(q).sum(), min=1e-6) / torch.clamp(
+                    1 - p[torch.tensor(ids)].sum(), min=1e-6)
+                c = (torch.tensor(q) - rho * p[torch.tensor(ids)]).detach()
+                bracket = logp[a] - (c * logp[torch.tensor(ids)]).sum() * centering
+                (-A * weight * bracket / n_valid).backward()
+                np.testing.assert_allclose(r["row"], zt.grad.numpy(), rtol=1e-9, atol=1e-11)
+                _close(r["weight"], weight, 1e-12)
+
+
+def test_centering_off_is_the_weighted_policy_gradient():
+    # centering disabled: g = weight (e_a - p), the plain importance-weighted
+    # score (the grpo_mis ablation).
+    rng = np.random.default_rng(34)
+    z, ids, q, a = _rand_case(rng, 20, 5)
+    logp, _ = O.trainer_log_softmax(z, 1.0)
+    rlp = float(logp[a]) - 0.3
+    r = O.sc_row(z, 1.0, ids, q, a, rollout_logp=rlp, row_mode=O.MODE_SCORE,
+                 is_mode=O.IS_MIS, is_lo=0.5, is_hi=5.0, centering=False)
+    expect = math.exp(0.3) * (np.eye(20)[a] - np.exp(logp))
+    np.testing.assert_allclose(r["row"], expect, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Entropy and reverse KL
+# --------------------------------------------------------------------------
+def test_entropy_matches_torch_distribution():
+    rng = np.random.default_rng(35)
+    for T in (1.0, 0.6):
+        z = rng.normal(0, 3, 500)
+        r = O.sc_row(z, T, [1, 2], [0.1, 0.1], 0)
+        ref = torch.distributions.Categorical(logits=torch.tensor(z / T)).entropy().item()
+        assert abs(r["entropy"] - ref) < 1e-10
+    # uniform logits: entropy log V
+    r = O.sc_row(np.zeros(64), 1.0, [1], [0.1], 0)
+    _close(r["entropy"], math.log(64), 1e-12)
+
+
+def test_reverse_kl_closed_form_and_special_cases():
+    rng = np.random.default_rng(36)
+    for trial in range(50):
+        V = int(rng.integers(3, 200))
+        K = int(rng.integers(1, V))
+        z, ids, q, a = _rand_case(rng, V, K, rng.choice([None, "tail", "head"]))
+        r = O.sc_row(z, 1.0, ids, q, a)
+        logp, _ = O.trainer_log_softmax(z, 1.0)
+        p_h = np.exp(logp[ids])
+        # the tail of mu_hat is rho p, so its part of sum p log(p / mu_hat)
+        # is -tau log rho
+        cf = np.sum(p_h * (logp[ids] - np.log(q))) - r["tau"] * math.log(r["rho"])
+        assert abs(r["rev_kl"] - cf) < 1e-9 * max(1, abs(cf))
+        assert r["rev_kl"] >= -1e-12 or r["S"] != 1
+    # identical distributions: zero
+    logp, _ = O.trainer_log_softmax(Z4, 1.0)
+    r = O.sc_row(Z4, 1.0, [3, 1], np.exp(logp[[3, 1]]), 2)
+    assert abs(r["rev_kl"]) < 1e-13
+    # a recorded id with q = 0 but p > 0 makes the reverse KL infinite
+    r = O.sc_row(Z4, 1.0, [3, 1], [0.5, 0.0], 2)
+    assert r["rev_kl"] == float("inf")
 
 
 # --------------------------------------------------------------------------
