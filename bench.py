@@ -42,11 +42,11 @@ KERNEL_SOURCES = [os.path.join(ROOT, "off_policy_logit_amd", "csrc", f)
 # Algorithmic bytes of one position through the fused kernel (sc_correct with
 # a bf16 dLogits row): logits 2V, head ids 4K, head probs 4K, sampled,
 # resp_idx, rollout logp, advantage (4 B each) read; dLogits 2V, head logp 4K,
-# coefficients 4K, 12 fp32 statistics and 2 int32 indices written.
-BYTES_PER_POSITION = 2 * VOCAB + 8 * K + 16 + 2 * VOCAB + 8 * K + 48 + 8
+# coefficients 4K, 16 fp32 statistics and 2 int32 indices written.
+BYTES_PER_POSITION = 2 * VOCAB + 8 * K + 16 + 2 * VOCAB + 8 * K + 64 + 8
 # Stats-only pass (sc_logprobs): logits 2V, ids 4K, sampled, resp_idx read;
-# log p at H 4K, 4 of the statistics and 2 indices written.
-BYTES_PER_POSITION_STATS = 2 * VOCAB + 4 * K + 8 + 4 * K + 16 + 8
+# log p at H 4K, 5 of the statistics and 2 indices written.
+BYTES_PER_POSITION_STATS = 2 * VOCAB + 4 * K + 8 + 4 * K + 20 + 8
 
 
 def source_digest():

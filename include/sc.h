@@ -75,21 +75,34 @@ enum sc_row_mode {
   SC_ROW_CORRECTION = 2  /* correction mu_hat - p                             */
 };
 
+/* Importance weighting of the token loss (Score Centering page, SC settings:
+ * is_mode none / tis / mis; lecture notes "RL systems for agents", section 1,
+ * truncated importance sampling).  w = p(a) / mu(a) from the recorded
+ * rollout log-probability; the weight is a stop-gradient factor:
+ *   SC_IS_NONE  1
+ *   SC_IS_TIS   min(w, is_hi)                      (tis_max, default 2.0)
+ *   SC_IS_MIS   w if is_lo <= w <= is_hi, else 0   (mis_min 0.5, mis_max 5.0) */
+enum sc_is_mode { SC_IS_NONE = 0, SC_IS_TIS = 1, SC_IS_MIS = 2 };
+
 /* Columns of the per-row statistics array row_stats[n_rows][SC_NSTATS]. */
 enum sc_stat {
-  SC_STAT_LSE = 0,     /* log sum_v exp(z_v / T)                               */
-  SC_STAT_LOGP_A = 1,  /* log p(a) of the sampled token                        */
-  SC_STAT_TAIL = 2,    /* tau = sum of p over ids outside H (= 1 - P_H)        */
-  SC_STAT_P_H = 3,     /* trainer mass on the recorded ids                     */
-  SC_STAT_Q_H = 4,     /* recorded behaviour mass (coverage)                   */
-  SC_STAT_RHO = 5,     /* tail scale rho, both clamps applied                  */
-  SC_STAT_S = 6,       /* sum of mu_hat = Q_H + rho * tau                      */
-  SC_STAT_LOSS = 7,    /* token loss -A [log p_a - sum_H c log p]              */
-  SC_STAT_TV = 8,      /* 1/2 sum_v |mu_hat_v - p_v|                           */
-  SC_STAT_KL = 9,      /* KL(mu_hat || p)                                      */
-  SC_STAT_K3 = 10,     /* exp(d) - 1 - d, d = log p(a) - rollout log mu(a)     */
-  SC_STAT_RESERVED = 11,
-  SC_NSTATS = 12
+  SC_STAT_LSE = 0,      /* log sum_v exp(z_v / T)                              */
+  SC_STAT_LOGP_A = 1,   /* log p(a) of the sampled token                       */
+  SC_STAT_TAIL = 2,     /* tau = sum of p over ids outside H (= 1 - P_H)       */
+  SC_STAT_P_H = 3,      /* trainer mass on the recorded ids                    */
+  SC_STAT_Q_H = 4,      /* recorded behaviour mass (coverage)                  */
+  SC_STAT_RHO = 5,      /* tail scale rho, both clamps applied                 */
+  SC_STAT_S = 6,        /* sum of mu_hat = Q_H + rho * tau                     */
+  SC_STAT_LOSS = 7,     /* token loss -A wt [log p_a - centering sum_H c log p] */
+  SC_STAT_TV = 8,       /* 1/2 sum_v |mu_hat_v - p_v|                          */
+  SC_STAT_KL = 9,       /* KL(mu_hat || p)                                     */
+  SC_STAT_K3 = 10,      /* exp(d) - 1 - d, d = log p(a) - rollout log mu(a)    */
+  SC_STAT_ENTROPY = 11, /* -sum_v p_v log p_v of the trainer policy            */
+  SC_STAT_W = 12,       /* importance ratio w = p(a) / mu(a)                   */
+  SC_STAT_WEIGHT = 13,  /* stop-gradient weight wt applied (sc_is_mode)        */
+  SC_STAT_REV_KL = 14,  /* KL(p || mu_hat)                                     */
+  SC_STAT_RESERVED = 15,
+  SC_NSTATS = 16
 };
 
 /* Columns of the per-row integer array row_idx[n_rows][2]. */
@@ -98,10 +111,11 @@ enum sc_idx { SC_IDX_ARGMAX = 0, SC_IDX_A_SLOT = 1, SC_NIDX = 2 };
 /* Sums and means written by sc_batch_sums, batch[SC_NBATCH] (float64). */
 enum sc_batch {
   SC_SUM_LOSS = 0, SC_SUM_K3 = 1, SC_SUM_TV = 2, SC_SUM_KL = 3,
-  SC_SUM_Q_H = 4, SC_SUM_P_H = 5, SC_SUM_ROWS = 6, SC_SUM_FLAGGED = 7,
-  SC_MEAN_LOSS = 8, SC_MEAN_K3 = 9, SC_MEAN_TV = 10, SC_MEAN_KL = 11,
-  SC_MEAN_Q_H = 12, SC_MEAN_P_H = 13,
-  SC_NBATCH = 14
+  SC_SUM_Q_H = 4, SC_SUM_P_H = 5, SC_SUM_ENTROPY = 6, SC_SUM_REV_KL = 7,
+  SC_SUM_ROWS = 8, SC_SUM_FLAGGED = 9, SC_MAX_W = 10,
+  SC_MEAN_LOSS = 11, SC_MEAN_K3 = 12, SC_MEAN_TV = 13, SC_MEAN_KL = 14,
+  SC_MEAN_Q_H = 15, SC_MEAN_P_H = 16, SC_MEAN_ENTROPY = 17, SC_MEAN_REV_KL = 18,
+  SC_NBATCH = 19
 };
 
 /*
@@ -118,8 +132,8 @@ enum sc_batch {
  *                 padding; NULL means every row is valid
  *   temperature   T > 0; p = softmax(z / T)
  * Outputs (device, written for every row):
- *   row_stats     float [n_rows, SC_NSTATS]: columns LSE, LOGP_A, TAIL, P_H
- *                 (the other columns are left untouched)
+ *   row_stats     float [n_rows, SC_NSTATS]: columns LSE, LOGP_A, TAIL, P_H,
+ *                 ENTROPY (the other columns are left untouched)
  *   row_idx       int32 [n_rows, SC_NIDX]: argmax of the raw logits (lowest
  *                 index among equal maxima) and the slot k with H_k = a (-1 if
  *                 a is not recorded)
@@ -140,7 +154,7 @@ int sc_logprobs(const void* logits, int logits_dtype, int64_t n_rows,
  * coefficients c = q - rho p on H, the tail proportional to p, global
  * generated-token reduction with padding masked; rollout_corr/k3_kl.
  * Reads row_stats columns LSE, LOGP_A, TAIL and row_idx / head_logp as written
- * by sc_logprobs on the same rows; writes row_stats columns P_H .. K3.
+ * by sc_logprobs on the same rows; writes columns P_H .. K3 and W .. REV_KL.
  * When row_out is not NULL the logits are streamed once more to write it.
  *
  *   logits, logits_dtype, row_stride   as for sc_logprobs; may be NULL when
@@ -155,8 +169,15 @@ int sc_logprobs(const void* logits, int logits_dtype, int64_t n_rows,
  *   n_valid       device int64 [1]: valid positions of the WHOLE step (all
  *                 chunks); read only for SC_ROW_DLOGITS with row_out
  *   row_out       device [n_rows, out_stride] of out_dtype, or NULL
- *   row_mode      sc_row_mode
+ *   row_mode      sc_row_mode; SC_ROW_DLOGITS and SC_ROW_SCORE carry the
+ *                 importance weight, SC_ROW_CORRECTION does not
  *   coef          device float [n_rows, k]: c_k = q_k - rho p_k, or NULL
+ *   is_mode       sc_is_mode; TIS and MIS need rollout_logp
+ *   is_lo, is_hi  MIS acceptance interval [is_lo, is_hi]; TIS cap is_hi
+ *                 (finite, 0 <= is_lo <= is_hi, is_hi > 0)
+ *   centering     non-zero: the SC loss; zero: the centering term is dropped
+ *                 (loss -A wt log p_a, score wt (e_a - p)), the ablation of
+ *                 the Score Centering page that turns centering off
  */
 int sc_center(const void* logits, int logits_dtype, int64_t n_rows,
               int64_t vocab, int64_t row_stride, const int32_t* head_ids,
@@ -165,8 +186,9 @@ int sc_center(const void* logits, int logits_dtype, int64_t n_rows,
               const float* advantages, int32_t n_responses, float temperature,
               const int64_t* n_valid, float* row_stats, int32_t* row_idx,
               const float* head_logp, float* coef, void* row_out,
-              int out_dtype, int64_t out_stride, int row_mode,
-              uint32_t* dev_status, void* stream);
+              int out_dtype, int64_t out_stride, int row_mode, int is_mode,
+              float is_lo, float is_hi, int centering, uint32_t* dev_status,
+              void* stream);
 
 /*
  * sc_correct -- sc_logprobs followed by sc_center in one kernel: every output
@@ -182,14 +204,14 @@ int sc_correct(const void* logits, int logits_dtype, int64_t n_rows,
                const float* advantages, int32_t n_responses, float temperature,
                const int64_t* n_valid, float* row_stats, int32_t* row_idx,
                float* head_logp, float* coef, void* row_out, int out_dtype,
-               int64_t out_stride, int row_mode, uint32_t* dev_status,
-               void* stream);
+               int64_t out_stride, int row_mode, int is_mode, float is_lo,
+               float is_hi, int centering, uint32_t* dev_status, void* stream);
 
 /*
  * sc_group_norm -- rollout-level advantages by group normalisation.
  *
- * Score Centering page, section "Training": both algorithms use "group
- * standard deviation normalization"; Agent Lightning v1.0.3 release note,
+ * Score Centering page, section "Training": both algorithms normalise the
+ * advantages by the group's standard deviation; Agent Lightning v1.0.3 release note,
  * section 4: rewards stay fractional (no bf16 cast first) and the normaliser
  * must not overflow -- the kernel accumulates in float64.
  *
@@ -214,9 +236,11 @@ int sc_count_valid(const int32_t* resp_idx, int64_t n_rows, int64_t* out,
 
 /*
  * sc_batch_sums -- step-level reductions in a fixed order (deterministic):
- * float64 sums over the valid rows of loss, K3, TV, KL, Q_H and P_H, the
- * number of valid rows and of rows whose statistics are NaN, then the means
- * over n_valid (global generated-token reduction, Score Centering section).
+ * float64 sums over the valid rows of loss, K3, TV, KL, Q_H, P_H, entropy and
+ * KL(p || mu_hat), the number of valid rows and of rows whose statistics are
+ * NaN, the largest importance ratio w (lecture notes, section 7, debugging signals),
+ * then the means over n_valid (global generated-token reduction, Score
+ * Centering section).
  *   row_stats   device float [n_rows, SC_NSTATS] from sc_center / sc_correct
  *   resp_idx    device int32 [n_rows]
  *   n_valid     device int64 [1]

@@ -131,8 +131,16 @@ int run_rows(sc::RowParams& P, int kind, void* stream) {
 int check_center(sc::RowParams& P, const float* head_probs, const float* rollout_logp,
                  const int32_t* resp_idx, const float* advantages, int32_t n_responses,
                  const int64_t* n_valid, float* coef, void* row_out, int out_dtype,
-                 int64_t out_stride, int row_mode, uint32_t* dev_status) {
+                 int64_t out_stride, int row_mode, int is_mode, float is_lo, float is_hi,
+                 int centering, uint32_t* dev_status) {
   if (!head_probs || !resp_idx || !advantages) return SC_ERR_ARG;
+  if (is_mode < SC_IS_NONE || is_mode > SC_IS_MIS) return SC_ERR_ARG;
+  if (is_mode != SC_IS_NONE) {
+    if (!rollout_logp) return SC_ERR_ARG;
+    if (!(std::isfinite(is_lo) && std::isfinite(is_hi) && is_lo >= 0.f && is_hi > 0.f &&
+          is_lo <= is_hi))
+      return SC_ERR_ARG;
+  }
   if (n_responses < 0) return SC_ERR_ARG;
   if (row_mode < SC_ROW_DLOGITS || row_mode > SC_ROW_CORRECTION) return SC_ERR_ARG;
   if (row_out) {
@@ -155,6 +163,10 @@ int check_center(sc::RowParams& P, const float* head_probs, const float* rollout
   P.out_dtype = row_out ? out_dtype : SC_F32;
   P.out_stride = row_out ? out_stride : 0;
   P.row_mode = row_mode;
+  P.is_mode = is_mode;
+  P.is_lo = is_lo;
+  P.is_hi = is_hi;
+  P.centering = centering ? 1 : 0;
   P.dev_status = dev_status;
   P.vector = (vector_ok(P.logits, P.in_dtype, P.row_stride) &&
               vector_ok(row_out, P.out_dtype, P.out_stride)) ? 1 : 0;
@@ -191,15 +203,16 @@ int sc_center(const void* logits, int logits_dtype, int64_t n_rows, int64_t voca
               const int32_t* resp_idx, const float* advantages, int32_t n_responses,
               float temperature, const int64_t* n_valid, float* row_stats,
               int32_t* row_idx, const float* head_logp, float* coef, void* row_out,
-              int out_dtype, int64_t out_stride, int row_mode, uint32_t* dev_status,
-              void* stream) {
+              int out_dtype, int64_t out_stride, int row_mode, int is_mode, float is_lo,
+              float is_hi, int centering, uint32_t* dev_status, void* stream) {
   sc::RowParams P{};
   int st = check_rows(P, logits, row_out != nullptr, logits_dtype, n_rows, vocab, row_stride,
                       head_ids, k, sampled, temperature, row_stats, row_idx);
   if (st != SC_OK) return st;
   if (!head_logp || !aligned(head_logp, 4)) return SC_ERR_ARG;
   st = check_center(P, head_probs, rollout_logp, resp_idx, advantages, n_responses, n_valid,
-                    coef, row_out, out_dtype, out_stride, row_mode, dev_status);
+                    coef, row_out, out_dtype, out_stride, row_mode, is_mode, is_lo,
+                    is_hi, centering, dev_status);
   if (st != SC_OK) return st;
   P.head_logp = const_cast<float*>(head_logp);
   return run_rows(P, 1, stream);
@@ -211,15 +224,16 @@ int sc_correct(const void* logits, int logits_dtype, int64_t n_rows, int64_t voc
                const int32_t* resp_idx, const float* advantages, int32_t n_responses,
                float temperature, const int64_t* n_valid, float* row_stats,
                int32_t* row_idx, float* head_logp, float* coef, void* row_out,
-               int out_dtype, int64_t out_stride, int row_mode, uint32_t* dev_status,
-               void* stream) {
+               int out_dtype, int64_t out_stride, int row_mode, int is_mode, float is_lo,
+               float is_hi, int centering, uint32_t* dev_status, void* stream) {
   sc::RowParams P{};
   int st = check_rows(P, logits, true, logits_dtype, n_rows, vocab, row_stride, head_ids, k,
                       sampled, temperature, row_stats, row_idx);
   if (st != SC_OK) return st;
   if (head_logp && !aligned(head_logp, 4)) return SC_ERR_ARG;
   st = check_center(P, head_probs, rollout_logp, resp_idx, advantages, n_responses, n_valid,
-                    coef, row_out, out_dtype, out_stride, row_mode, dev_status);
+                    coef, row_out, out_dtype, out_stride, row_mode, is_mode, is_lo,
+                    is_hi, centering, dev_status);
   if (st != SC_OK) return st;
   P.head_logp = head_logp;
   return run_rows(P, 2, stream);

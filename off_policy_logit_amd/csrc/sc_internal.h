@@ -75,6 +75,9 @@ struct RowParams {
   int out_dtype;
   int64_t out_stride;
   int row_mode;
+  int is_mode;           // sc_is_mode
+  float is_lo, is_hi;    // MIS interval / TIS cap
+  int centering;         // 0: centering term dropped
   uint32_t* dev_status;
   // LDS layout (bytes into dynamic shared memory)
   int hs, hshift, vs, vshift, bm_wpt, ke;

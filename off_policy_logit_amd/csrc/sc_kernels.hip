@@ -35,8 +35,10 @@ enum KernelKind { KIND_LOGPROBS = 0, KIND_CENTER = 1, KIND_CORRECT = 2 };
 // Stats columns (mirror of sc.h; duplicated here so device code needs no C header)
 enum {
   C_LSE = 0, C_LOGP_A = 1, C_TAIL = 2, C_P_H = 3, C_Q_H = 4, C_RHO = 5,
-  C_S = 6, C_LOSS = 7, C_TV = 8, C_KL = 9, C_K3 = 10, C_RES = 11, C_N = 12
+  C_S = 6, C_LOSS = 7, C_TV = 8, C_KL = 9, C_K3 = 10, C_ENT = 11, C_W = 12,
+  C_WT = 13, C_RKL = 14, C_RES = 15, C_N = 16
 };
+enum { IS_NONE = 0, IS_TIS = 1, IS_MIS = 2 };
 enum { F_BAD_ID = 1, F_DUP_ID = 2, F_BAD_SAMPLED = 4, F_NONFINITE = 8, F_BAD_RESP = 16 };
 enum { M_DLOGITS = 0, M_SCORE = 1, M_CORRECTION = 2 };
 
@@ -75,7 +77,7 @@ void k_row(RowParams P) {
   __shared__ float redf[4 * NW];
   __shared__ int redi[NW];
   __shared__ double redd[4 * NW];
-  __shared__ unsigned long long redu[NW];
+  __shared__ unsigned long long redu[2 * NW];
   __shared__ int sh_ent;
   __shared__ uint32_t sh_flags;
   __shared__ float sh_za;
@@ -120,7 +122,7 @@ void k_row(RowParams P) {
           stats[C_LSE] = 0.f; stats[C_LOGP_A] = 0.f; stats[C_TAIL] = 0.f;
           ridx[0] = -1; ridx[1] = -1;
         }
-        if (KIND == KIND_LOGPROBS) stats[C_P_H] = 0.f;
+        if (KIND == KIND_LOGPROBS) { stats[C_P_H] = 0.f; stats[C_ENT] = 0.f; }
         if (KIND != KIND_LOGPROBS)
           for (int col = C_P_H; col <= C_RES; ++col) stats[col] = 0.f;
       }
@@ -240,16 +242,17 @@ void k_row(RowParams P) {
 
     float m = 0.f;        // row max of raw logits (pass-1 kernels)
     float log2s = 0.f;    // log2 sum_v 2^((z_v - m) c)
-    float lse = 0.f, logp_a = 0.f, tau = 0.f;
+    float lse = 0.f, logp_a = 0.f, tau = 0.f, entropy = 0.f;
     int argmax = -1, a_slot = -1;
 
     if (KIND != KIND_CENTER) {
       // ---------------------------------------------------------- pass 1
       // Online update per vector: running max m_t (starts at -FLT_MAX so
       // that all-(-inf) vectors rescale by 2^0 and add 2^-inf = 0), tail sum
-      // s_t relative to m_t, and the index of the vector that raised m_t
-      // (strictly, so the first of equal maxima is kept).
-      float m_t = -FLT_MAX, s_t = 0.f;
+      // s_t relative to m_t, h_t = sum 2^((z - m_t) c) (z - m_t) for the
+      // entropy, and the index of the vector that raised m_t (strictly, so
+      // the first of equal maxima is kept).
+      float m_t = -FLT_MAX, s_t = 0.f, h_t = 0.f;
       int am_vec = -1;
       int am_direct = -1;
       auto vec_update = [&](const float (&v)[N], int j) {
@@ -258,8 +261,22 @@ void k_row(RowParams P) {
         for (int i = 1; i < N; ++i) vm = fmaxf(vm, v[i]);
         const float m_new = fmaxf(m_t, vm);
         am_vec = vm > m_t ? j : am_vec;
-        s_t *= exp2_fast((m_t - m_new) * c);
+        const float r = exp2_fast((m_t - m_new) * c);
+        h_t = r * (h_t - (m_new - m_t) * s_t);
+        s_t *= r;
         m_t = m_new;
+      };
+      // exp sum and exp-weighted offset sum of one vector (-inf entries add 0)
+      auto vec_sums = [&](const float (&v)[N], float& acc, float& acch) {
+        acc = 0.f;
+        acch = 0.f;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          const float d = v[i] - m_t;
+          const float e = exp2_fast(d * c);
+          acc += e;
+          acch = fmaf(e, fmaxf(d, -FLT_MAX), acch);
+        }
       };
       // Branch-free: marked vectors are summed too and the sum is dropped
       // (they are resolved element by element after the stream).
@@ -270,10 +287,11 @@ void k_row(RowParams P) {
           float v[N];
           IO::unpack(r[u], v);
           vec_update(v, j0 + u);
-          float acc = 0.f;
-#pragma unroll
-          for (int i = 0; i < N; ++i) acc += exp2_fast((v[i] - m_t) * c);
-          s_t += ((bits >> u) & 1u) ? 0.f : acc;
+          float acc, acch;
+          vec_sums(v, acc, acch);
+          const bool marked = (bits >> u) & 1u;
+          s_t += marked ? 0.f : acc;
+          h_t += marked ? 0.f : acch;
         }
       };
       {
@@ -287,10 +305,11 @@ void k_row(RowParams P) {
           float v[N];
           IO::unpack(load_one(j, nt), v);
           vec_update(v, j);
-          float acc = 0.f;
-#pragma unroll
-          for (int i = 0; i < N; ++i) acc += exp2_fast((v[i] - m_t) * c);
-          s_t += ((bitmap[(j >> 5) * B + t] >> (j & 31)) & 1u) ? 0.f : acc;
+          float acc, acch;
+          vec_sums(v, acc, acch);
+          const bool marked = (bitmap[(j >> 5) * B + t] >> (j & 31)) & 1u;
+          s_t += marked ? 0.f : acc;
+          h_t += marked ? 0.f : acch;
         }
       }
       list_marked();
@@ -306,7 +325,9 @@ void k_row(RowParams P) {
           if (v[i] > tm) { tm = v[i]; idx = (int)(n_full * N + i); }
         }
         if (tm > m_t) {
-          s_t *= exp2_fast((m_t - tm) * c);
+          const float r = exp2_fast((m_t - tm) * c);
+          h_t = r * (h_t - (tm - m_t) * s_t);
+          s_t *= r;
           m_t = tm;
           am_direct = idx;
         }
@@ -330,7 +351,9 @@ void k_row(RowParams P) {
       block_argmax<B>(mv, mi, redf, redi);
       m = mv;
       argmax = mi;
-      float tail_part = s_t * exp2_fast((m_t - m) * c);
+      const float r_t = exp2_fast((m_t - m) * c);
+      float tail_part = s_t * r_t;
+      float h_part = r_t * (h_t - (m - m_t) * s_t);
       // Resolve the listed vectors: each recorded id (and the sampled id)
       // finds its vector's list entry through the vector map; every other
       // listed element is a tail term.  Tail terms are summed as 64-bit
@@ -338,21 +361,30 @@ void k_row(RowParams P) {
       // sums are exact, so the total does not depend on the listing order.
       const int n_ent = min(sh_ent, P.ke);
       resolve_slots(n_ent);
-      unsigned long long tail_fx = 0ull;
+      // The entropy sum D = sum_v 2^((z - m) c) (z - m) takes every listed
+      // element (recorded ids included) in signed 2^-32 fixed point, added
+      // modulo 2^64 (terms are >= -0.37 T each).
+      unsigned long long tail_fx = 0ull, h_fx = 0ull;
       for (int i = t; i < n_ent * N; i += B) {
         const int vid = ent_vec[i / N] * N + (i % N);
-        if (vid < V && ent_slot[i] < 0)
-          tail_fx += (unsigned long long)(exp2_fast((ent_val[i] - m) * c) * 0x1p52f);
+        if (vid >= V) continue;
+        const float d = ent_val[i] - m;
+        const float e = exp2_fast(d * c);
+        if (ent_slot[i] < 0) tail_fx += (unsigned long long)(e * 0x1p52f);
+        h_fx += (unsigned long long)(long long)(e * fmaxf(d, -FLT_MAX) * 0x1p32f);
       }
-      unsigned long long fx[1] = {tail_fx};
-      block_sum<B, 1>(fx, redu);
+      unsigned long long fx[2] = {tail_fx, h_fx};
+      block_sum<B, 2>(fx, redu);
       tail_part += t == 0 ? (float)((double)fx[0] * 0x1p-52) : 0.f;
+      h_part += t == 0 ? (float)((double)(long long)fx[1] * 0x1p-32) : 0.f;
       float head_part = 0.f;
       for (int k = t; k < K; k += B) head_part += exp2_fast((headz[k] - m) * c);
-      float sums[2] = {tail_part, head_part};
-      block_sum<B, 2>(sums, redf);
+      float sums[3] = {tail_part, head_part, h_part};
+      block_sum<B, 3>(sums, redf);
       const float s = sums[0] + sums[1];
       log2s = log2f(s);
+      // entropy = ln s - D / (T s), with 1 / T = c ln 2
+      entropy = (log2s - sums[2] * c / s) * kLn2;
       lse = (m * c + log2s) * kLn2;
       tau = sums[0] / s;
       const float za = sh_za;
@@ -398,6 +430,7 @@ void k_row(RowParams P) {
         stats[C_LOGP_A] = bad ? qnan : logp_a;
         stats[C_TAIL] = bad ? qnan : tau;
         stats[C_P_H] = bad ? qnan : sums[0];
+        stats[C_ENT] = bad ? qnan : entropy;
         ridx[0] = bad ? -1 : argmax;
         ridx[1] = bad ? -1 : a_slot;
         if (flags) sh_status |= flags;
@@ -418,7 +451,7 @@ void k_row(RowParams P) {
     const double taud = (double)tau;
     const double rho = fmax(1.0 - Q_H, kClamp) / fmax(taud, kClamp);
     const double S = Q_H + rho * taud;
-    double d2[3] = {0.0, 0.0, 0.0};
+    double d2[4] = {0.0, 0.0, 0.0, 0.0};
     for (int k = t; k < K; k += B) {
       const double q = (double)P.head_probs[row * K + k];
       const double p = (double)headp[k];
@@ -427,22 +460,31 @@ void k_row(RowParams P) {
       if (P.coef) P.coef[row * K + k] = flags ? qnan : (float)ck;
       d2[0] += ck * lp;
       d2[1] += fabs(q - p);
-      if (q > 0.0) d2[2] += q * ((double)logf((float)q) - lp);
+      const double lq = (double)logf((float)q);
+      if (q > 0.0) d2[2] += q * (lq - lp);
+      if (p > 0.0) d2[3] += p * (lp - lq);   // reverse KL, head part
     }
-    block_sum<B, 3>(d2, redd);
+    block_sum<B, 4>(d2, redd);
 
     uint32_t rflags = flags;
     if (resp >= P.n_responses) rflags |= F_BAD_RESP;
     const double A = (resp < P.n_responses) ? (double)P.advantages[resp] : (double)qnan;
-    const double loss = -A * ((double)logp_a - d2[0]);
-    const double tv = 0.5 * (d2[1] + fabs(rho - 1.0) * taud);
-    double kl = d2[2];
-    if (rho * taud > 0.0) kl += rho * taud * (double)logf((float)rho);
+    // importance ratio of the sampled token and its stop-gradient weight
+    double w = (double)qnan, wt = 1.0;
     double k3 = (double)qnan;
     if (P.rollout_logp) {
       const double d = (double)logp_a - (double)P.rollout_logp[row];
       k3 = (double)expm1f((float)d) - d;
+      w = (double)expf((float)d);
+      if (P.is_mode == IS_TIS) wt = fmin(w, (double)P.is_hi);
+      else if (P.is_mode == IS_MIS) wt = (w >= (double)P.is_lo && w <= (double)P.is_hi) ? w : 0.0;
     }
+    const double loss = -A * wt * ((double)logp_a - (P.centering ? d2[0] : 0.0));
+    const double tv = 0.5 * (d2[1] + fabs(rho - 1.0) * taud);
+    const double lrho = (double)logf((float)rho);
+    double kl = d2[2];
+    if (rho * taud > 0.0) kl += rho * taud * lrho;
+    const double rkl = d2[3] - (taud > 0.0 ? taud * lrho : 0.0);
 
     if (t == 0) {
       const bool bad = rflags != 0;
@@ -450,6 +492,7 @@ void k_row(RowParams P) {
         stats[C_LSE] = bad ? qnan : lse;
         stats[C_LOGP_A] = bad ? qnan : logp_a;
         stats[C_TAIL] = bad ? qnan : tau;
+        stats[C_ENT] = bad ? qnan : entropy;
         ridx[0] = bad ? -1 : argmax;
         ridx[1] = bad ? -1 : a_slot;
       }
@@ -461,6 +504,9 @@ void k_row(RowParams P) {
       stats[C_TV] = bad ? qnan : (float)tv;
       stats[C_KL] = bad ? qnan : (float)kl;
       stats[C_K3] = bad ? qnan : (float)k3;
+      stats[C_W] = bad ? qnan : (float)w;
+      stats[C_WT] = bad ? qnan : (float)wt;
+      stats[C_RKL] = bad ? qnan : (float)rkl;
       stats[C_RES] = 0.f;
       if (rflags) sh_status |= rflags;
     }
@@ -471,7 +517,8 @@ void k_row(RowParams P) {
 
     // -------------------------------------------------------------- pass 2
     // Off-head entries are alpha * p_v; recorded ids take hout[k]; the
-    // sampled id, when outside H, adds `scale`.
+    // sampled id, when outside H, adds `scale`.  The score rows carry the
+    // weight wt; without centering mu_hat is replaced by p (score e_a - p).
     double scale = 1.0, alpha;
     if (P.row_mode == M_CORRECTION) {
       alpha = rho - 1.0;
@@ -479,7 +526,8 @@ void k_row(RowParams P) {
     } else {
       if (P.row_mode == M_DLOGITS)
         scale = -A / ((double)P.temperature * (double)P.n_valid[0]);
-      alpha = -scale * (rho + 1.0 - S);
+      scale *= wt;
+      alpha = P.centering ? -scale * (rho + 1.0 - S) : -scale;
     }
     if (rflags) { alpha = (double)qnan; scale = (double)qnan; }
     __syncthreads();  // all reads of hout as log p are done
@@ -490,7 +538,8 @@ void k_row(RowParams P) {
         val = (double)P.head_probs[row * K + k] - p;
       } else {
         const double ind = (k == a_slot) ? 1.0 : 0.0;
-        val = scale * (ind - (double)P.head_probs[row * K + k] - (1.0 - S) * p);
+        val = P.centering ? scale * (ind - (double)P.head_probs[row * K + k] - (1.0 - S) * p)
+                          : scale * (ind - p);
       }
       hout[k] = rflags ? qnan : (float)val;
     }
@@ -622,25 +671,32 @@ __global__ __launch_bounds__(B) void k_batch_sums(const float* __restrict__ st,
                                                   const int32_t* __restrict__ resp,
                                                   int64_t n, const int64_t* n_valid,
                                                   double* batch, int acc) {
-  __shared__ double red[8 * (B / kWave)];
-  double v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  constexpr int NS = 8;   // summed statistics
+  constexpr int SUMS[NS] = {C_LOSS, C_K3, C_TV, C_KL, C_Q_H, C_P_H, C_ENT, C_RKL};
+  __shared__ double red[(NS + 2) * (B / kWave)];
+  __shared__ float redf[B / kWave];
+  __shared__ int redi[B / kWave];
+  double v[NS + 2];
+#pragma unroll
+  for (int j = 0; j < NS + 2; ++j) v[j] = 0.0;
+  float wmax = -INFINITY;
   for (int64_t i = threadIdx.x; i < n; i += B) {
     if (resp[i] < 0) continue;
     const float* s = st + i * C_N;
-    v[0] += (double)s[C_LOSS];
-    v[1] += (double)s[C_K3];
-    v[2] += (double)s[C_TV];
-    v[3] += (double)s[C_KL];
-    v[4] += (double)s[C_Q_H];
-    v[5] += (double)s[C_P_H];
-    v[6] += 1.0;
-    v[7] += (s[C_LOSS] != s[C_LOSS]) ? 1.0 : 0.0;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) v[j] += (double)s[SUMS[j]];
+    v[NS] += 1.0;
+    v[NS + 1] += (s[C_LOSS] != s[C_LOSS]) ? 1.0 : 0.0;
+    wmax = fmaxf(wmax, s[C_W]);
   }
-  block_sum<B, 8>(v, red);
+  block_sum<B, NS + 2>(v, red);
+  int dummy = 0;
+  block_argmax<B>(wmax, dummy, redf, redi);
   if (threadIdx.x == 0) {
     const double nv = (double)n_valid[0];
-    for (int j = 0; j < 8; ++j) batch[j] = (acc ? batch[j] : 0.0) + v[j];
-    for (int j = 0; j < 6; ++j) batch[8 + j] = batch[j] / nv;
+    for (int j = 0; j < NS + 2; ++j) batch[j] = (acc ? batch[j] : 0.0) + v[j];
+    batch[NS + 2] = acc ? fmax(batch[NS + 2], (double)wmax) : (double)wmax;
+    for (int j = 0; j < NS; ++j) batch[NS + 3 + j] = batch[j] / nv;
   }
 }
 

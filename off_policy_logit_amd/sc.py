@@ -21,13 +21,15 @@ SC_OK, SC_ERR_ARG, SC_ERR_UNSUPPORTED, SC_ERR_HIP = 0, -1, -2, -3
 SC_F32, SC_BF16 = 0, 1
 DEV_BAD_ID, DEV_DUP_ID, DEV_BAD_SAMPLED, DEV_NONFINITE, DEV_BAD_RESP = 1, 2, 4, 8, 16
 ROW_DLOGITS, ROW_SCORE, ROW_CORRECTION = 0, 1, 2
+IS_NONE, IS_TIS, IS_MIS = 0, 1, 2
 STATS = ("lse", "logp_a", "tail", "P_H", "Q_H", "rho", "S", "loss", "tv", "kl",
-         "k3", "reserved")
+         "k3", "entropy", "w", "weight", "rev_kl", "reserved")
 NSTATS = len(STATS)
 STAT = {name: i for i, name in enumerate(STATS)}
 BATCH = ("sum_loss", "sum_k3", "sum_tv", "sum_kl", "sum_Q_H", "sum_P_H",
-         "rows", "flagged", "mean_loss", "mean_k3", "mean_tv", "mean_kl",
-         "mean_Q_H", "mean_P_H")
+         "sum_entropy", "sum_rev_kl", "rows", "flagged", "max_w",
+         "mean_loss", "mean_k3", "mean_tv", "mean_kl", "mean_Q_H", "mean_P_H",
+         "mean_entropy", "mean_rev_kl")
 NBATCH = len(BATCH)
 
 _vp, _i64, _i32, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
@@ -36,10 +38,12 @@ _SIGS = {
                     _f32, _vp, _vp, _vp, _vp, _vp],
     "sc_center": [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _vp, _i32, _vp,
                   _vp, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp,
-                  ctypes.c_int, _i64, ctypes.c_int, _vp, _vp],
+                  ctypes.c_int, _i64, ctypes.c_int, ctypes.c_int, _f32, _f32,
+                  ctypes.c_int, _vp, _vp],
     "sc_correct": [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _vp, _i32, _vp,
                    _vp, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp,
-                   ctypes.c_int, _i64, ctypes.c_int, _vp, _vp],
+                   ctypes.c_int, _i64, ctypes.c_int, ctypes.c_int, _f32, _f32,
+                  ctypes.c_int, _vp, _vp],
     "sc_group_norm": [_vp, _i32, _i32, _i32, _f32, _vp, _vp],
     "sc_count_valid": [_vp, _i64, _vp, _i32, _vp],
     "sc_batch_sums": [_vp, _vp, _i64, _vp, _vp, _i32, _vp],
@@ -133,9 +137,16 @@ def logprobs(logits, head_ids, sampled, resp_idx=None, temperature=1.0,
     return out
 
 
+def _default_hi(is_mode, is_hi):
+    if is_hi is not None:
+        return is_hi
+    return 5.0 if is_mode == IS_MIS else 2.0
+
+
 def _center_like(fn, logits, head_ids, head_probs, sampled, resp_idx,
                  advantages, temperature, n_valid, rollout_logp, out, row_out,
-                 row_mode, coef, dev_status, stream, vocab=None):
+                 row_mode, coef, dev_status, stream, is_mode, is_lo, is_hi,
+                 centering, vocab=None):
     if logits is not None:
         n, V, stride = _rows(logits)
         dcode = _dtype_code(logits)
@@ -159,22 +170,32 @@ def _center_like(fn, logits, head_ids, head_probs, sampled, resp_idx,
         _ptr(sampled), _ptr(rollout_logp), _ptr(resp_idx), _ptr(advantages),
         advantages.shape[0], float(temperature), _ptr(n_valid),
         _ptr(out["row_stats"]), _ptr(out["row_idx"]), _ptr(out.get("head_logp")),
-        _ptr(coef), _ptr(row_out), ocode, ostride, int(row_mode),
-        _ptr(dev_status), _stream(stream)))
+        _ptr(coef), _ptr(row_out), ocode, ostride, int(row_mode), int(is_mode),
+        float(is_lo), float(_default_hi(is_mode, is_hi)), int(bool(centering)),
+        _ptr(dev_status),
+        _stream(stream)))
 
 
 def center(stats, head_ids, head_probs, sampled, resp_idx, advantages,
            temperature=1.0, n_valid=None, rollout_logp=None, logits=None,
            row_out=None, row_mode=ROW_DLOGITS, coef=None, dev_status=None,
-           stream=None, vocab=None):
-    """sc_center on the output dict of logprobs(); fills the remaining stats."""
+           stream=None, vocab=None, is_mode=IS_NONE, is_lo=0.5, is_hi=None,
+           centering=True):
+    """sc_center on the output dict of logprobs(); fills the remaining stats.
+
+    is_mode / is_lo / is_hi select the importance weighting of the sampled
+    token (IS_TIS: min(w, is_hi); IS_MIS: w inside [is_lo, is_hi], else 0;
+    both need rollout_logp); is_hi defaults to 2.0 for TIS and 5.0 for MIS
+    (the Score Centering page's settings table); centering=False drops the
+    centering term."""
     if coef is None:
         coef = torch.empty_like(stats["head_logp"])
     if logits is None and vocab is None:
         raise TypeError("vocab is required when logits is None")
     _center_like(lib().sc_center, logits, head_ids, head_probs, sampled,
                  resp_idx, advantages, temperature, n_valid, rollout_logp,
-                 stats, row_out, row_mode, coef, dev_status, stream, vocab)
+                 stats, row_out, row_mode, coef, dev_status, stream, is_mode,
+                 is_lo, is_hi, centering, vocab)
     stats["coef"] = coef
     return stats
 
@@ -182,7 +203,7 @@ def center(stats, head_ids, head_probs, sampled, resp_idx, advantages,
 def correct(logits, head_ids, head_probs, sampled, resp_idx, advantages,
             temperature=1.0, n_valid=None, rollout_logp=None, row_out=None,
             row_mode=ROW_DLOGITS, out=None, coef=None, dev_status=None,
-            stream=None):
+            stream=None, is_mode=IS_NONE, is_lo=0.5, is_hi=None, centering=True):
     """sc_correct: every output of logprobs() and center() in one kernel."""
     n = logits.shape[0]
     k = head_ids.shape[1]
@@ -191,7 +212,8 @@ def correct(logits, head_ids, head_probs, sampled, resp_idx, advantages,
         coef = torch.empty(n, k, dtype=torch.float32, device=logits.device)
     _center_like(lib().sc_correct, logits, head_ids, head_probs, sampled,
                  resp_idx, advantages, temperature, n_valid, rollout_logp, out,
-                 row_out, row_mode, coef, dev_status, stream)
+                 row_out, row_mode, coef, dev_status, stream, is_mode, is_lo,
+                 is_hi, centering)
     out["coef"] = coef
     return out
 

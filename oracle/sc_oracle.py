@@ -46,8 +46,8 @@ Readings taken where the page is silent (each is listed in the design notes):
   a NaN or +inf logit, a -inf logit at a recorded or sampled id) make every
   float output of the row NaN and its integer outputs -1.
 
-Group normalisation (same page, "Training" section: "group standard deviation
-normalization"; Agent Lightning v1.0.3 release note, section 4: rewards are not
+Group normalisation (same page, "Training" section: advantages normalised by
+the group's standard deviation; Agent Lightning v1.0.3 release note, section 4: rewards are not
 rounded to bf16 first and the denominator must not overflow): rewards are
 widened to float64; mode 0 divides by the unbiased standard deviation plus eps,
 mode 1 by the population standard deviation plus eps, mode 2 only subtracts the
@@ -130,7 +130,7 @@ def is_weight(w, is_mode, lo, hi):
     Truncated IS replaces w by min(w, w_max) (lecture notes "RL systems for
     agents", section 1, where the truncated weight is defined); masked IS keeps
     the token, weighted by w, only when lo <= w <= hi and drops it otherwise
-    (reading of "masked importance sampling" with its acceptance interval,
+    (reading of the masked-IS setting with its acceptance interval,
     Score Centering page, SC settings).
     """
     if is_mode == IS_NONE:
@@ -144,7 +144,7 @@ def is_weight(w, is_mode, lo, hi):
 
 def sc_row(z, temperature, head_ids, head_probs, sampled, rollout_logp=None,
            advantage=1.0, n_valid=1, row_mode=MODE_DLOGITS, is_mode=IS_NONE,
-           is_lo=0.5, is_hi=2.0, centering=True):
+           is_lo=0.5, is_hi=None, centering=True):
     """All per-position SC outputs of one valid row, by definition, in float64.
 
     Arguments: z (V,) logits (any float dtype, widened exactly), temperature T,
@@ -154,7 +154,7 @@ def sc_row(z, temperature, head_ids, head_probs, sampled, rollout_logp=None,
     the whole step, row_mode selecting the full-vocabulary row to return,
     is_mode / is_lo / is_hi the importance weighting of the token (needs
     rollout_logp), centering=False dropping the centering term (the grpo_mis
-    ablation: "centering disabled").
+    ablation of the SC settings table, which turns centering off).
 
     Returns a dict; see the keys at the end.
     """
@@ -202,6 +202,9 @@ def sc_row(z, temperature, head_ids, head_probs, sampled, rollout_logp=None,
         w = float("nan")
     else:
         w = math.exp(logp_a - float(rollout_logp))
+    if is_hi is None:
+        # settings-table defaults: TIS cap 2.0, MIS interval [0.5, 5.0]
+        is_hi = 5.0 if is_mode == IS_MIS else 2.0
     weight = is_weight(w, is_mode, is_lo, is_hi)
 
     # Stop-gradient coefficients and the token loss.

@@ -78,13 +78,15 @@ def center(fn="sc_center", **kw):
              probs=FAKE, k=10, sampled=FAKE, rlp=NULL, resp=FAKE, adv=FAKE,
              nresp=2, T=1.0, nvalid=FAKE, stats=FAKE, idx=FAKE, hlp=FAKE,
              coef=FAKE, out=FAKE, odt=sc.SC_BF16, ostride=1000,
-             mode=sc.ROW_DLOGITS, dev=NULL, stream=NULL)
+             mode=sc.ROW_DLOGITS, is_mode=sc.IS_NONE, lo=0.5, hi=2.0, cen=1,
+             dev=NULL, stream=NULL)
     a.update(kw)
     return getattr(sc.lib(), fn)(
         a["logits"], a["dtype"], a["n"], a["V"], a["stride"], a["ids"], a["probs"],
         a["k"], a["sampled"], a["rlp"], a["resp"], a["adv"], a["nresp"], a["T"],
         a["nvalid"], a["stats"], a["idx"], a["hlp"], a["coef"], a["out"], a["odt"],
-        a["ostride"], a["mode"], a["dev"], a["stream"])
+        a["ostride"], a["mode"], a["is_mode"], a["lo"], a["hi"], a["cen"],
+        a["dev"], a["stream"])
 
 
 @pytest.mark.parametrize("fn", ["sc_center", "sc_correct"])
@@ -93,6 +95,12 @@ def center(fn="sc_center", **kw):
     dict(mode=3), dict(mode=-1), dict(odt=5), dict(ostride=999),
     dict(nvalid=NULL), dict(out=FAKE1), dict(odt=sc.SC_F32, out=FAKE2),
     dict(logits=NULL), dict(T=0.0), dict(k=0), dict(coef=FAKE2),
+    dict(is_mode=3), dict(is_mode=-1), dict(is_mode=sc.IS_TIS),
+    dict(is_mode=sc.IS_MIS, rlp=FAKE, lo=2.0, hi=1.0),
+    dict(is_mode=sc.IS_MIS, rlp=FAKE, lo=-0.1),
+    dict(is_mode=sc.IS_TIS, rlp=FAKE, hi=0.0),
+    dict(is_mode=sc.IS_TIS, rlp=FAKE, hi=float("inf")),
+    dict(is_mode=sc.IS_MIS, rlp=FAKE, lo=float("nan")),
 ])
 def test_center_and_correct_reject_bad_arguments(fn, kw):
     assert center(fn, **kw) == ARG
@@ -103,6 +111,14 @@ def test_center_without_row_out_needs_no_logits_or_n_valid():
     assert center(logits=NULL, out=NULL, nvalid=NULL, hlp=NULL, n=0) == ARG
     # scores and corrections do not need N_valid
     assert center(nvalid=NULL, mode=sc.ROW_SCORE, n=0) == OK
+
+
+def test_weighting_arguments_are_accepted():
+    for is_mode in (sc.IS_TIS, sc.IS_MIS):
+        assert center(is_mode=is_mode, rlp=FAKE, n=0) == OK
+        assert center("sc_correct", is_mode=is_mode, rlp=FAKE, lo=0.0, hi=5.0, n=0) == OK
+    # bounds are not read without weighting; centering off is always valid
+    assert center(lo=float("nan"), hi=-1.0, cen=0, n=0) == OK
 
 
 @pytest.mark.parametrize("args", [

@@ -48,7 +48,7 @@ def host_rows(t, rows):
     return x.cpu().numpy()
 
 
-def run_correct(d, adv, n_valid, T, mode, out_dtype, logits=None):
+def run_correct(d, adv, n_valid, T, mode, out_dtype, logits=None, **weighting):
     logits = d["logits"] if logits is None else logits
     n, V = logits.shape
     row_out = None
@@ -59,7 +59,7 @@ def run_correct(d, adv, n_valid, T, mode, out_dtype, logits=None):
     out = sc.correct(logits, d["head_ids"], d["head_probs"], d["sampled"],
                      d["resp_idx"], adv, temperature=T, n_valid=n_valid,
                      rollout_logp=d["rollout_logp"], row_out=row_out,
-                     row_mode=mode, dev_status=status)
+                     row_mode=mode, dev_status=status, **weighting)
     out["row"] = row_out
     out["status"] = status
     return out
@@ -76,8 +76,10 @@ def gather(out, rows, out_dtype):
 
 
 def check_rows(tag, d, out, rows, adv_h, n_valid, T, mode, out_dtype,
-               min_equal=0.998, logits_h=None):
-    """Compare the listed rows of a GPU result with the oracle."""
+               min_equal=0.998, logits_h=None, **weighting):
+    """Compare the listed rows of a GPU result with the oracle.
+
+    weighting: is_mode / is_lo / is_hi / centering, passed to both sides."""
     rows = np.asarray(rows)
     z = logits_h if logits_h is not None else host_rows(d["logits"], rows)
     ids = host_rows(d["head_ids"], rows)
@@ -90,15 +92,19 @@ def check_rows(tag, d, out, rows, adv_h, n_valid, T, mode, out_dtype,
     for j, r in enumerate(rows):
         gj = {key: val[j] for key, val in g.items()}
         if resp[j] < 0:
-            assert np.all(gj["stats"][:11] == 0) and list(gj["idx"]) == [-1, -1]
+            assert np.all(gj["stats"][:15] == 0) and list(gj["idx"]) == [-1, -1]
             if out_dtype is not None:
                 assert np.all(gj["row"] == 0)
             continue
         A = float(adv_h[resp[j]])
-        o = O.sc_row(z[j], T, ids[j], q[j], a[j], rollout_logp=rlp[j],
-                     advantage=A, n_valid=n_valid, row_mode=mode)
+        def rerun(j=j, A=A, **over):
+            return O.sc_row(z[j], T, ids[j], q[j], a[j], rollout_logp=rlp[j],
+                            advantage=A, n_valid=n_valid, row_mode=mode,
+                            **dict(weighting, **over))
+        o = rerun()
         check_row(f"{tag} row {r}", gj, o, A=A, T=T, n_valid=n_valid, mode=mode,
-                  row_dtype=out_dtype, bf16_stats=stats, rlp=rlp[j])
+                  row_dtype=out_dtype, bf16_stats=stats, rlp=rlp[j], rerun=rerun,
+                  **weighting)
     if stats:
         total = sum(s[2] for s in stats)
         eq = sum(s[1] * s[2] for s in stats) / total
@@ -167,6 +173,66 @@ def test_tiny_two_call_path(out_dtype):
 # ---------------------------------------------------------------------------
 # Ragged vocabulary, strided / misaligned rows (scalar path), K extremes
 # ---------------------------------------------------------------------------
+# ---------------------------------------------------------------------------
+# Importance weighting (truncated / masked) and the uncentered ablation
+# ---------------------------------------------------------------------------
+IS_LO, IS_HI = 0.8, 1.25
+# bf16 rows of a weighted token carry the weight's relative error as well:
+# a flip probability of at most 2^9 (4e-6 + 2e-5) per entry
+MIN_EQUAL_WEIGHTED = 1.0 - 2 ** 9 * (4e-6 + 2e-5)
+
+
+def tiny_spread(seed):
+    """Tiny workload whose rollout log-probabilities are shifted by N(0, 0.5)
+    (capped at 0), so that importance ratios fall on both sides of
+    [IS_LO, IS_HI]."""
+    h = synthetic.tiny(seed=seed, temperature=0.8)
+    rng = np.random.default_rng(seed + 100)
+    shift = rng.normal(0.0, 0.5, h["rollout_logp"].shape)
+    h["rollout_logp"] = np.minimum(h["rollout_logp"] + shift, 0.0).astype(np.float32)
+    return h
+
+
+@pytest.mark.parametrize("is_mode,centering", [(O.IS_TIS, True), (O.IS_MIS, True),
+                                               (O.IS_MIS, False), (O.IS_NONE, False)])
+@pytest.mark.parametrize("mode,out_dtype", [("dlogits", "f32"), ("score", "bf16")])
+def test_tiny_importance_weighting(is_mode, centering, mode, out_dtype):
+    say(f"tiny weighting is_mode={is_mode} centering={centering} {mode}/{out_dtype}")
+    h = tiny_spread(3)
+    d = to_dev(h)
+    adv = sc.group_norm(d["rewards"], h["group_size"])
+    n_valid = sc.count_valid(d["resp_idx"])
+    wkw = dict(is_mode=is_mode, is_lo=IS_LO, is_hi=IS_HI, centering=centering)
+    out = run_correct(d, adv, n_valid, 0.8, MODES[mode], out_dtype, **wkw)
+    torch.cuda.synchronize()
+    assert int(out["status"].item()) == 0
+    check_rows(f"tiny weighting {is_mode}/{centering} {mode}/{out_dtype}", d, out,
+               np.arange(256), adv.cpu().numpy(), 256, 0.8, MODES[mode], out_dtype,
+               min_equal=MIN_EQUAL_WEIGHTED, logits_h=h["logits"], **wkw)
+    w = out["row_stats"][:, sc.STAT["w"]].cpu().numpy()
+    assert (w < IS_LO).sum() >= 20 and (w > IS_HI).sum() >= 20
+    assert ((w >= IS_LO) & (w <= IS_HI)).sum() >= 20
+
+
+def test_tiny_two_call_weighting():
+    say("tiny sc_logprobs + sc_center, masked IS, f32 dlogits")
+    h = tiny_spread(4)
+    d = to_dev(h)
+    adv = sc.group_norm(d["rewards"], h["group_size"])
+    n_valid = sc.count_valid(d["resp_idx"])
+    wkw = dict(is_mode=O.IS_MIS, is_lo=IS_LO, is_hi=IS_HI, centering=True)
+    st = sc.logprobs(d["logits"], d["head_ids"], d["sampled"], d["resp_idx"],
+                     temperature=0.8)
+    row_out = torch.empty(256, 4096, device=DEV)
+    sc.center(st, d["head_ids"], d["head_probs"], d["sampled"], d["resp_idx"], adv,
+              temperature=0.8, n_valid=n_valid, rollout_logp=d["rollout_logp"],
+              logits=d["logits"], row_out=row_out, row_mode=O.MODE_DLOGITS, **wkw)
+    st["row"] = row_out
+    torch.cuda.synchronize()
+    check_rows("tiny two-call MIS", d, st, np.arange(256), adv.cpu().numpy(), 256, 0.8,
+               O.MODE_DLOGITS, "f32", logits_h=h["logits"], **wkw)
+
+
 def crafted(n, V, K, seed, dtype, stride=None, scale=2.0):
     rng = np.random.default_rng(seed)
     z = rng.normal(0, scale, (n, V)).astype(np.float32)
@@ -293,7 +359,8 @@ def test_count_valid_and_batch_sums():
     chunks = []
     for c in range(3):
         resp = rng.integers(-1, 7, n).astype(np.int32)
-        st = rng.normal(0, 1, (n, 12)).astype(np.float32)
+        st = rng.normal(0, 1, (n, sc.NSTATS)).astype(np.float32)
+        st[:, sc.STAT["w"]] = np.exp(st[:, sc.STAT["w"]])
         chunks.append((resp, st))
     total = sum(int((r >= 0).sum()) for r, _ in chunks)
     nv = torch.zeros(1, dtype=torch.int64, device=DEV)
@@ -305,13 +372,17 @@ def test_count_valid_and_batch_sums():
         sc.batch_sums(torch.from_numpy(st).to(DEV), torch.from_numpy(resp).to(DEV), nv,
                       out=batch, accumulate=i > 0)
     b = batch.cpu().numpy()
-    rows = [dict(loss=s[7], k3=s[10], tv=s[8], kl=s[9], Q_H=s[4], P_H=s[3])
+    rows = [dict(loss=s[7], k3=s[10], tv=s[8], kl=s[9], Q_H=s[4], P_H=s[3],
+                 entropy=s[11], rev_kl=s[14], w=s[12])
             for resp, st in chunks for s, r in zip(st, resp) if r >= 0]
     sums, means = O.batch_sums(rows, total)
-    for j, key in enumerate(("loss", "k3", "tv", "kl", "Q_H", "P_H")):
-        assert abs(b[j] - sums[key]) <= 1e-9 * max(1, abs(sums[key])), key
-        assert abs(b[8 + j] - means[key]) <= 1e-12 * max(1, abs(means[key])), key
-    assert b[6] == total and b[7] == 0
+    B = sc.BATCH.index
+    for key in O.BATCH_KEYS:
+        got_s, got_m = b[B("sum_" + key)], b[B("mean_" + key)]
+        assert abs(got_s - sums[key]) <= 1e-9 * max(1, abs(sums[key])), key
+        assert abs(got_m - means[key]) <= 1e-12 * max(1, abs(means[key])), key
+    assert b[B("rows")] == total and b[B("flagged")] == 0
+    assert b[B("max_w")] == np.float32(means["max_w"])
 
 
 # ---------------------------------------------------------------------------
@@ -376,6 +447,29 @@ def test_quick_check_two_call_and_f32_rows(quick):
     torch.cuda.synchronize()
     check_rows("quick-check two-call score f32", dd, stt, np.arange(len(rows)),
                adv.cpu().numpy(), 8192, 1.0, O.MODE_SCORE, "f32")
+
+
+def test_quick_check_masked_is_and_step_sums(quick):
+    d = quick
+    say("quick-check sc_correct bf16 dlogits, masked IS, then batch_sums")
+    adv = sc.group_norm(d["rewards"], d["group_size"])
+    n_valid = sc.count_valid(d["resp_idx"])
+    wkw = dict(is_mode=O.IS_MIS, is_lo=0.99, is_hi=1.01, centering=True)
+    out = run_correct(d, adv, n_valid, 1.0, O.MODE_DLOGITS, "bf16", **wkw)
+    batch = sc.batch_sums(out["row_stats"], d["resp_idx"], n_valid)
+    torch.cuda.synchronize()
+    assert int(out["status"].item()) == 0
+    rows = sample_rows(8192, 24, seed=24)
+    check_rows("quick-check MIS dlogits bf16", d, out, rows, adv.cpu().numpy(), 8192,
+               1.0, O.MODE_DLOGITS, "bf16", min_equal=MIN_EQUAL_WEIGHTED, **wkw)
+    st = out["row_stats"].double().cpu().numpy()
+    b = batch.cpu().numpy()
+    B = sc.BATCH.index
+    assert b[B("max_w")] == st[:, sc.STAT["w"]].max()
+    assert b[B("rows")] == 8192 and b[B("flagged")] == 0
+    for key in ("entropy", "rev_kl", "loss"):
+        ref = math.fsum(st[:, sc.STAT[key]])
+        assert abs(b[B("sum_" + key)] - ref) <= 1e-9 * max(1.0, abs(ref)), key
 
 
 def test_full_step_chunk_with_padding():
