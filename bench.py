@@ -35,6 +35,8 @@ VOCAB, K = 248_320, 128
 PROMPTS, GROUP, TOKENS = 2, 4, 1024
 N_ROWS = PROMPTS * GROUP * TOKENS
 HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix peak
+LM_ROWS, LM_D = 16_384, 4096    # fused LM-head slice (64 x 8,800-token batch, d = 4,096)
 PROFILE = os.path.join(ROOT, "profiles", "sc_correct_quick_check_pmc.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "off_policy_logit_amd", "csrc", f)
                   for f in ("sc_kernels.hip", "sc_device.h", "sc_internal.h", "sc_api.cpp")]
@@ -124,6 +126,47 @@ def cpu_baseline(rows, min_seconds=10.0, max_passes=200):
 # ---------------------------------------------------------------------------
 # GPU
 # ---------------------------------------------------------------------------
+def lmhead_measure(dev, reps):
+    """Fused LM-head statistics (sc_logprobs_lmhead) on a 16,384-row slice at
+    V = 248,320, d = 4,096: event-timed average of the three kernels, in
+    positions/s and dense bf16 TFLOP/s (2 d V per position)."""
+    import torch
+    import synthetic
+    from off_policy_logit_amd import sc
+    w, wr = synthetic.lmhead_weights(dev, vocab=VOCAB, d=LM_D, seed=5)
+    c = synthetic.lmhead_chunk(dev, wr, LM_ROWS, seed=6)
+    del wr
+    ws = torch.empty(sc.lmhead_workspace_size(LM_ROWS, VOCAB, K), dtype=torch.uint8, device=dev)
+    out = dict(row_stats=torch.empty(LM_ROWS, sc.NSTATS, device=dev),
+               row_idx=torch.empty(LM_ROWS, 2, dtype=torch.int32, device=dev),
+               head_logp=torch.empty(LM_ROWS, K, device=dev))
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def run():
+        sc.logprobs_lmhead(c["hidden"], w, c["head_ids"], c["sampled"], None, out=out,
+                           workspace=ws, dev_status=status)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError(f"lmhead device status {int(status.item())}")
+    ms = e0.elapsed_time(e1) / reps
+    tflops = 2.0 * LM_D * VOCAB * LM_ROWS / (ms * 1e-3) / 1e12
+    del w, c, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"{LM_ROWS} rows x V={VOCAB} x d={LM_D}, bf16 hidden and "
+                        "projection, K=128, logits never stored",
+            "kernel_ms": round(ms, 3), "positions_per_s": round(LM_ROWS / (ms * 1e-3), 1),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +174,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-rows", type=int, default=512,
                     help="positions in the CPU-oracle sample (0 skips it)")
+    ap.add_argument("--no-lmhead", action="store_true",
+                    help="skip the fused LM-head measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy before the timed region "
                          "(reference kernel for PMC byte counters)")
@@ -211,6 +256,8 @@ def main():
     torch.cuda.synchronize()
     stats_ms = e0.elapsed_time(e1) / reps
 
+    lm = None if args.no_lmhead else lmhead_measure(dev, max(3, args.steps // 10))
+
     bytes_launch = n * BYTES_PER_POSITION
     achieved = bytes_launch / (kern_ms * 1e-3) / 1e9
     traffic = traffic_from_profile()
@@ -245,6 +292,7 @@ def main():
             "stats_only_positions_per_s": round(n / (stats_ms * 1e-3), 1),
             "stats_only_kernel_ms": round(stats_ms, 4),
             "stats_only_GBps": round(n * BYTES_PER_POSITION_STATS / (stats_ms * 1e-3) / 1e9, 1),
+            "lmhead": lm,
         },
     }
     print(json.dumps(line), flush=True)

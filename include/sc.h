@@ -254,6 +254,54 @@ int sc_batch_sums(const float* row_stats, const int32_t* resp_idx,
 /* Human-readable name of a status code (static storage). */
 const char* sc_status_string(int status);
 
+/*
+ * Fused LM-head statistics.
+ *
+ * Score Centering page, section "Score Centering": the trainer scores the
+ * current policy over the full vocabulary at the rollout temperature and
+ * gathers the log-probabilities of the recorded ids and of the sampled token
+ * (the page's SC worker does this on materialised logits and has no fused
+ * LM-head path).  sc_logprobs_lmhead produces exactly the outputs of
+ * sc_logprobs for logits z = X W^T / T without writing the [n_rows, vocab]
+ * logits anywhere: z is computed tile by tile with bf16 matrix cores (fp32
+ * accumulation over d) and folded into the running row statistics on chip.
+ * sc_center (with logits = NULL and no full-vocabulary row) completes the
+ * correction from these outputs.
+ *
+ *   hidden         device bf16 [n_rows, d], row stride hidden_stride elements
+ *                  (16-byte aligned, stride a multiple of 8, <= 4,194,303)
+ *   d              hidden size, a multiple of 64 (else SC_ERR_UNSUPPORTED)
+ *   weight         device bf16 [vocab, d] (vocabulary projection, one row per
+ *                  id), row stride weight_stride (same rules as hidden)
+ *   head_ids .. dev_status   as sc_logprobs (row_stats columns LSE, LOGP_A,
+ *                  TAIL, P_H and ENTROPY are written; head_logp may be NULL)
+ *   workspace      device memory of at least sc_lmhead_workspace_size(n_rows,
+ *                  vocab, k) bytes, 256-byte aligned, owned by the caller; its
+ *                  contents need no initialisation and are scratch afterwards
+ * A NaN or infinite logit (from non-finite inputs or overflow) flags the row
+ * SC_DEV_NONFINITE.  Argmax is over the fp32 logits, lowest id on ties.
+ */
+int64_t sc_lmhead_workspace_size(int64_t n_rows, int64_t vocab, int32_t k);
+
+int sc_logprobs_lmhead(const void* hidden, int64_t n_rows, int32_t d,
+                       int64_t hidden_stride, const void* weight, int64_t vocab,
+                       int64_t weight_stride, const int32_t* head_ids, int32_t k,
+                       const int32_t* sampled, const int32_t* resp_idx,
+                       float temperature, float* row_stats, int32_t* row_idx,
+                       float* head_logp, void* workspace, int64_t workspace_bytes,
+                       uint32_t* dev_status, void* stream);
+
+/*
+ * sc_lmhead_logits -- the logits X W^T of the fused kernel's GEMM, written as
+ * fp32 [n_rows, logits_stride >= vocab] (the same tiles and accumulation
+ * order, so its values are bit-identical to the ones sc_logprobs_lmhead
+ * consumes).  Meant for checking; it writes n_rows * vocab floats.
+ */
+int sc_lmhead_logits(const void* hidden, int64_t n_rows, int32_t d,
+                     int64_t hidden_stride, const void* weight, int64_t vocab,
+                     int64_t weight_stride, float* logits, int64_t logits_stride,
+                     void* stream);
+
 /* Library version, major * 10000 + minor * 100 + patch. */
 int sc_version(void);
 

@@ -2,6 +2,7 @@
 // layout, persistent-grid sizing and kernel dispatch.  See include/sc.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -270,6 +271,131 @@ int sc_batch_sums(const float* row_stats, const int32_t* resp_idx, int64_t n_row
     return SC_ERR_ARG;
   hipError_t e = sc::launch_batch_sums(row_stats, resp_idx, n_rows, n_valid, batch,
                                        accumulate ? 1 : 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SC_OK : SC_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// Fused LM-head statistics
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int64_t kLmMaxStride = 4194303;  // tile offsets stay below 2^31 bytes
+
+int lm_splits(int64_t vocab) {
+  const int64_t chunks = (vocab + sc::kLmTileV - 1) / sc::kLmTileV;
+  return (int)std::min<int64_t>(sc::kLmMaxSplits, chunks);
+}
+
+size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace layout; returns its size and, when P is given, points P's
+// workspace arrays into `base`.
+size_t lm_workspace(int64_t n, int64_t vocab, int k, sc::LmParams* P, char* base) {
+  const int S = lm_splits(vocab);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += up256(bytes); return base + o; };
+  char* skey = take((size_t)n * k * 8);
+  char* head_raw = take((size_t)n * k * 4);
+  char* state = take((size_t)S * n * 16);
+  char* za = take((size_t)n * 4);
+  char* scount = take((size_t)n * 4);
+  char* sa = take((size_t)n * 4);
+  char* sflags = take((size_t)n * 4);
+  if (P) {
+    P->skey = reinterpret_cast<long long*>(skey);
+    P->head_raw = reinterpret_cast<float*>(head_raw);
+    P->state = reinterpret_cast<float4*>(state);
+    P->za = reinterpret_cast<float*>(za);
+    P->scount = reinterpret_cast<int32_t*>(scount);
+    P->sa = reinterpret_cast<int32_t*>(sa);
+    P->sflags = reinterpret_cast<uint32_t*>(sflags);
+  }
+  return off;
+}
+
+// Checks shared by the two LM-head entry points; fills the GEMM geometry.
+int check_lm(sc::LmParams& P, const void* hidden, int64_t n_rows, int32_t d,
+             int64_t hidden_stride, const void* weight, int64_t vocab, int64_t weight_stride) {
+  if (!hidden || !weight) return SC_ERR_ARG;
+  if (n_rows < 0 || n_rows > kMaxI32) return SC_ERR_ARG;
+  if (vocab < 1 || vocab > kMaxI32 - sc::kLmTileV) return SC_ERR_ARG;
+  if (d < 1 || hidden_stride < d || weight_stride < d) return SC_ERR_ARG;
+  if (hidden_stride > kLmMaxStride || weight_stride > kLmMaxStride) return SC_ERR_ARG;
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || hidden_stride % 8 || weight_stride % 8)
+    return SC_ERR_ARG;
+  if (d % sc::kLmKStage) return SC_ERR_UNSUPPORTED;
+  P.x = static_cast<const uint16_t*>(hidden);
+  P.xs = hidden_stride;
+  P.w = static_cast<const uint16_t*>(weight);
+  P.ws = weight_stride;
+  P.n_rows = n_rows;
+  P.vocab = vocab;
+  P.d = d;
+  P.splits = lm_splits(vocab);
+  P.n_chunks = (int)((vocab + sc::kLmTileV - 1) / sc::kLmTileV);
+  P.n_ptiles = (int)((n_rows + sc::kLmTileP - 1) / sc::kLmTileP);
+  // 32 concurrent workgroups per XCD: 4 row tiles x 8 splits when the split
+  // count allows, else every split of 32 / splits row tiles.
+  P.lm_sp = P.splits % 8 == 0 ? 8 : P.splits;
+  P.lm_pt = std::max(1, 32 / P.lm_sp);
+  return SC_OK;
+}
+
+}  // namespace
+
+int64_t sc_lmhead_workspace_size(int64_t n_rows, int64_t vocab, int32_t k) {
+  if (n_rows < 0 || n_rows > kMaxI32 || vocab < 1 || vocab > kMaxI32 - sc::kLmTileV)
+    return SC_ERR_ARG;
+  if (k < 1 || k > kMaxK || (int64_t)k > vocab) return SC_ERR_ARG;
+  return (int64_t)lm_workspace(n_rows, vocab, k, nullptr, nullptr);
+}
+
+int sc_logprobs_lmhead(const void* hidden, int64_t n_rows, int32_t d, int64_t hidden_stride,
+                       const void* weight, int64_t vocab, int64_t weight_stride,
+                       const int32_t* head_ids, int32_t k, const int32_t* sampled,
+                       const int32_t* resp_idx, float temperature, float* row_stats,
+                       int32_t* row_idx, float* head_logp, void* workspace,
+                       int64_t workspace_bytes, uint32_t* dev_status, void* stream) {
+  sc::LmParams P{};
+  int st = check_lm(P, hidden, n_rows, d, hidden_stride, weight, vocab, weight_stride);
+  if (st != SC_OK) return st;
+  if (k < 1 || k > kMaxK || (int64_t)k > vocab) return SC_ERR_ARG;
+  if (!(std::isfinite(temperature) && temperature > 0.f)) return SC_ERR_ARG;
+  if (!head_ids || !sampled || !row_stats || !row_idx || !workspace) return SC_ERR_ARG;
+  if (!aligned(head_ids, 4) || !aligned(sampled, 4) || !aligned(row_stats, 4) ||
+      !aligned(row_idx, 4) || !aligned(workspace, 256) ||
+      (head_logp && !aligned(head_logp, 4)) || (resp_idx && !aligned(resp_idx, 4)) ||
+      (dev_status && !aligned(dev_status, 4)))
+    return SC_ERR_ARG;
+  const size_t need = lm_workspace(n_rows, vocab, k, nullptr, nullptr);
+  if (workspace_bytes < 0 || (size_t)workspace_bytes < need) return SC_ERR_ARG;
+  lm_workspace(n_rows, vocab, k, &P, static_cast<char*>(workspace));
+  P.c = (float)(1.4426950408889634 / (double)temperature);
+  P.head_ids = head_ids;
+  P.k = k;
+  P.sampled = sampled;
+  P.resp_idx = resp_idx;
+  P.row_stats = row_stats;
+  P.row_idx = row_idx;
+  P.head_logp = head_logp;
+  P.dev_status = dev_status;
+  if (n_rows == 0) return SC_OK;
+  hipError_t e = sc::launch_lmhead(P, false, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SC_OK : SC_ERR_HIP;
+}
+
+int sc_lmhead_logits(const void* hidden, int64_t n_rows, int32_t d, int64_t hidden_stride,
+                     const void* weight, int64_t vocab, int64_t weight_stride, float* logits,
+                     int64_t logits_stride, void* stream) {
+  sc::LmParams P{};
+  int st = check_lm(P, hidden, n_rows, d, hidden_stride, weight, vocab, weight_stride);
+  if (st != SC_OK) return st;
+  if (!logits || !aligned(logits, 4) || logits_stride < vocab) return SC_ERR_ARG;
+  P.out = logits;
+  P.os = logits_stride;
+  P.c = 1.f;
+  if (n_rows == 0) return SC_OK;
+  hipError_t e = sc::launch_lmhead(P, true, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SC_OK : SC_ERR_HIP;
 }
 

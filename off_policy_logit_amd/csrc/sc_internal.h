@@ -87,6 +87,46 @@ struct RowParams {
 };
 
 hipError_t launch_row(const RowParams& P, int kind, int grid, hipStream_t s);
+
+// Fused LM-head statistics (sc_logprobs_lmhead / sc_lmhead_logits): tile of
+// 256 vocabulary ids x 256 rows, k stages of 64, at most 32 vocabulary splits.
+constexpr int kLmTileV = 256;
+constexpr int kLmTileP = 256;
+constexpr int kLmKStage = 64;
+constexpr int kLmMaxSplits = 32;
+
+struct LmParams {
+  const uint16_t* x;     // hidden states, bf16 [n_rows, d], row stride xs
+  int64_t xs;
+  const uint16_t* w;     // vocabulary projection, bf16 [vocab, d], row stride ws
+  int64_t ws;
+  int64_t n_rows, vocab;
+  int d;
+  float c;               // log2(e) / T
+  int splits, n_chunks, n_ptiles;
+  int lm_pt, lm_sp;      // row tiles x splits per XCD group (lm_sp divides splits)
+  const int32_t* head_ids;
+  int32_t k;
+  const int32_t* sampled;
+  const int32_t* resp_idx;
+  // workspace
+  long long* skey;       // [n_rows, k] sorted (id << 32 | slot)
+  int32_t* scount;       // [n_rows] keys to use (0: padding or data error)
+  int32_t* sa;           // [n_rows] sampled id, -1 when nothing is captured
+  uint32_t* sflags;      // [n_rows] data-error bits found by the stage kernel
+  float4* state;         // [splits, n_rows] (max, tail sum, entropy sum, argmax)
+  float* za;             // [n_rows] logit of the sampled id
+  float* head_raw;       // [n_rows, k] logits of the recorded ids
+  // outputs
+  float* out;            // logits check: fp32 [n_rows, os]
+  int64_t os;
+  float* row_stats;
+  int32_t* row_idx;
+  float* head_logp;
+  uint32_t* dev_status;
+};
+
+hipError_t launch_lmhead(const LmParams& P, bool store_logits, hipStream_t s);
 hipError_t launch_group_norm(const float* r, int n_groups, int G, int mode,
                              float eps, float* adv, hipStream_t s);
 hipError_t launch_count_valid(const int32_t* resp, int64_t n, int64_t* out,

@@ -1,0 +1,558 @@
+// Fused LM-head statistics of the SC correction for gfx950.
+//
+// The trainer step of the Score Centering page (section "Score Centering")
+// scores the current policy over the full vocabulary at the rollout
+// temperature and gathers log-probabilities at the recorded ids H and at the
+// sampled id a.  Here the logits z = X W^T (X: final hidden states [n, d],
+// W: vocabulary projection [V, d], both bf16) are produced tile by tile by
+// bf16 MFMA with fp32 accumulation and consumed in the same kernel by the
+// per-row online softmax statistics, so the [n, V] logits never reach HBM.
+// (The page's SC worker has no fused LM-head path; this is an addition with
+// the same outputs as the unfused statistics pass.)
+//
+// Three kernels:
+//   k_lm_stage     per row: validate and sort the recorded ids (id, slot).
+//   k_lm_main      per (256-row tile, vocabulary split): MFMA GEMM over d in
+//                  64-wide k stages, double-buffered through LDS; after each
+//                  256-id vocabulary chunk the epilogue folds the 256 x 256
+//                  logit tile into per-row running (max, tail sum, entropy
+//                  sum, argmax) and captures the logits at H and at a.
+//   k_lm_finalize  per row: merge the split states in a fixed order, add the
+//                  recorded ids, write the same statistics as sc_logprobs.
+// k_lm_main<true> instead stores the logit tile (a check of the GEMM with
+// the identical accumulation order).
+#include <hip/hip_runtime.h>
+#include <float.h>
+#include <stdint.h>
+
+#include "sc.h"
+#include "sc_device.h"
+#include "sc_internal.h"
+
+namespace sc {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kTV = kLmTileV;           // vocabulary ids per chunk (MFMA M)
+constexpr int kTP = kLmTileP;           // rows per tile (MFMA N)
+constexpr int kKB = kLmKStage;          // k per stage
+constexpr int kB = 512;                 // threads: 8 waves, 2 (vocab) x 4 (rows)
+constexpr int kWR = 64;                 // rows per wave (2 MFMA column blocks)
+constexpr int kPitch = kKB * 2 + 16;    // LDS bytes per tile row (bank rotation)
+constexpr int kBuf = kTV * kPitch;      // one operand buffer
+constexpr int kOffBm = 4 * kBuf;        // [kTP][8] hit words of the chunk
+constexpr int kOffBeg = kOffBm + kTP * 8 * 4;
+constexpr int kLds = kOffBeg + kTP * 4;
+static_assert(kTV == 256 && kTP == 256 && kKB == 64, "tile shape is fixed");
+static_assert(kLds <= 160 * 1024, "LDS budget");
+
+constexpr int kNoIdx = 0x7fffffff;
+
+SC_DEV int lm_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+
+// Merge running state (m, s, hy, am) with (m2, s2, h2, am2).  s is a sum of
+// 2^((z - m) c), hy the sum of 2^((z - m) c) (z - m) c over the same ids.
+SC_DEV void lm_merge(float& m, float& s, float& hy, int& am, float m2, float s2,
+                     float h2, int am2, float c) {
+  const float M = fmaxf(m, m2);
+  const float r1 = exp2_fast((m - M) * c), r2 = exp2_fast((m2 - M) * c);
+  const float t1 = s > 0.f ? r1 * (hy - (M - m) * c * s) : 0.f;
+  const float t2 = s2 > 0.f ? r2 * (h2 - (M - m2) * c * s2) : 0.f;
+  am = (m2 > m || (m2 == m && am2 < am)) ? am2 : am;
+  s = r1 * s + r2 * s2;
+  hy = t1 + t2;
+  m = M;
+}
+
+// ---------------------------------------------------------------------------
+// Stage: one workgroup per row.  Sorted keys (id << 32 | slot) of the recorded
+// ids, the sampled id and the data-error flags.  A padding row or a row with
+// an error gets no keys and sampled id -1, so the main kernel captures nothing
+// for it.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_lm_stage(LmParams P) {
+  __shared__ long long key[1024];
+  __shared__ uint32_t sh_fl;
+  const int t = threadIdx.x;
+  const int64_t p = blockIdx.x;
+  const int K = P.k;
+  const int resp = P.resp_idx ? P.resp_idx[p] : 0;
+  if (resp < 0) {
+    if (t == 0) { P.scount[p] = 0; P.sa[p] = -1; P.sflags[p] = 0u; }
+    return;
+  }
+  int P2 = 2;
+  while (P2 < K) P2 <<= 1;
+  if (t == 0) sh_fl = 0u;
+  __syncthreads();
+  uint32_t fl = 0;
+  for (int i = t; i < P2; i += 256) {
+    long long kv = 0x7fffffffffffffffll;
+    if (i < K) {
+      const int32_t id = P.head_ids[p * K + i];
+      if (id < 0 || id >= P.vocab) fl |= SC_DEV_BAD_ID;
+      kv = (long long)(((unsigned long long)(uint32_t)id << 32) | (uint32_t)i);
+    }
+    key[i] = kv;
+  }
+  __syncthreads();
+  for (int k2 = 2; k2 <= P2; k2 <<= 1) {
+    for (int j = k2 >> 1; j > 0; j >>= 1) {
+      for (int i = t; i < P2; i += 256) {
+        const int ij = i ^ j;
+        if (ij > i) {
+          const long long x = key[i], y = key[ij];
+          const bool up = (i & k2) == 0;
+          if ((x > y) == up) { key[i] = y; key[ij] = x; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = t; i + 1 < K; i += 256)
+    if ((key[i] >> 32) == (key[i + 1] >> 32)) fl |= SC_DEV_DUP_ID;
+  const int32_t a = P.sampled[p];
+  if (t == 0 && (a < 0 || a >= P.vocab)) fl |= SC_DEV_BAD_SAMPLED;
+  if (fl) atomicOr(&sh_fl, fl);
+  __syncthreads();
+  const uint32_t f = sh_fl;
+  for (int i = t; i < K; i += 256) P.skey[p * K + i] = key[i];
+  if (t == 0) {
+    P.scount[p] = f ? 0 : K;
+    P.sa[p] = f ? -1 : a;
+    P.sflags[p] = f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Main: GEMM tile loop with the statistics (or store) epilogue.
+// ---------------------------------------------------------------------------
+template <bool STORE>
+__global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int t = threadIdx.x, l = t & 63, w = t >> 6;
+  const int wv = w & 1, wp = w >> 1;   // wave's vocabulary half, row quarter
+  const int h = l >> 5, lc = l & 31;
+
+  // Work item.  Workgroups are dispatched round-robin over the 8 XCDs
+  // (blockIdx mod 8); each XCD's group of lm_pt * lm_sp concurrent workgroups
+  // covers lm_pt row tiles x lm_sp vocabulary splits, so every W chunk is
+  // read by lm_pt and every hidden-state tile by lm_sp workgroups sharing
+  // that XCD's L2 (instead of one of the two being read once per workgroup).
+  const int b = blockIdx.x;
+  const int xcd = b & 7, idx = b >> 3;
+  const int grp = idx / (P.lm_pt * P.lm_sp), loc = idx % (P.lm_pt * P.lm_sp);
+  const int sg = P.splits / P.lm_sp;                 // split groups
+  const int split = (grp % sg) * P.lm_sp + loc % P.lm_sp;
+  const int ptile = ((grp / sg) * P.lm_pt + loc / P.lm_sp) * 8 + xcd;
+  if (ptile >= P.n_ptiles) return;
+  const int64_t p0 = (int64_t)ptile * kTP;
+  const int c_begin = (int)((int64_t)split * P.n_chunks / P.splits);
+  const int c_end = (int)((int64_t)(split + 1) * P.n_chunks / P.splits);
+  const int n_ck = c_end - c_begin;
+  if (n_ck <= 0) return;  // the host keeps splits <= chunks
+  const int ST = P.d / kKB;
+  const int total = n_ck * ST;
+  const float c = P.c;
+  const int V = (int)P.vocab;
+
+  // Loader: thread t moves 16 bytes of rows (t >> 3) + 64 j, j < 4, of each
+  // operand per stage.  Rows past the end read row 0 of the tile (valid
+  // memory); their results are masked or never written.
+  constexpr int kLJ = kTV * kKB * 2 / 16 / kB;  // 16-byte loads per operand
+  const int lrow = t >> 3, lcol = t & 7;
+  const char* xb = reinterpret_cast<const char*>(P.x) + p0 * P.xs * 2;
+  uint32_t xoff[kLJ];
+#pragma unroll
+  for (int j = 0; j < kLJ; ++j) {
+    const int r = lrow + 64 * j;
+    xoff[j] = (uint32_t)(((p0 + r < P.n_rows) ? r : 0) * P.xs * 2 + lcol * 16);
+  }
+  uint32_t woff[kLJ];
+  const char* wb = nullptr;
+  auto set_chunk_rows = [&](int ck) {
+    const int64_t v0 = (int64_t)ck * kTV;
+    wb = reinterpret_cast<const char*>(P.w) + v0 * P.ws * 2;
+#pragma unroll
+    for (int j = 0; j < kLJ; ++j) {
+      const int r = lrow + 64 * j;
+      woff[j] = (uint32_t)(((v0 + r < V) ? r : 0) * P.ws * 2 + lcol * 16);
+    }
+  };
+
+  u32x4 ra[kLJ], rb[kLJ];
+  auto load = [&](int g) {
+    const int ks = g % ST;
+    const int ck = c_begin + g / ST;
+    if (ks == 0) set_chunk_rows(ck);
+    const int kb = ks * kKB * 2;
+#pragma unroll
+    for (int j = 0; j < kLJ; ++j) {
+      ra[j] = *reinterpret_cast<const u32x4*>(wb + woff[j] + kb);
+      rb[j] = *reinterpret_cast<const u32x4*>(xb + xoff[j] + kb);
+    }
+  };
+  auto store = [&](int buf) {
+    unsigned char* A = lds + buf * 2 * kBuf;
+    unsigned char* Bm = A + kBuf;
+#pragma unroll
+    for (int j = 0; j < kLJ; ++j) {
+      const int o = (lrow + 64 * j) * kPitch + lcol * 16;
+      *reinterpret_cast<u32x4*>(A + o) = ra[j];
+      *reinterpret_cast<u32x4*>(Bm + o) = rb[j];
+    }
+  };
+
+  constexpr int NJ = kWR / 32;  // column blocks (rows of the tile) per wave
+  f32x16 acc[4][NJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
+
+  auto compute = [&](int buf) {
+    const unsigned char* A = lds + buf * 2 * kBuf + (wv * 128 + lc) * kPitch + h * 16;
+    const unsigned char* Bm = lds + buf * 2 * kBuf + kBuf + (wp * kWR + lc) * kPitch + h * 16;
+#pragma unroll
+    for (int u = 0; u < kKB / 16; ++u) {
+      bf16x8 fa[4], fb[NJ];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8*>(A + i * 32 * kPitch + u * 32);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        fb[j] = *reinterpret_cast<const bf16x8*>(Bm + j * 32 * kPitch + u * 32);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // ------------------------------------------------------------ row state
+  // Thread t < 256 owns row t of the tile for the recorded-id cursor; each
+  // lane owns NJ rows (j) of the tile for the running statistics.
+  uint32_t* bm = reinterpret_cast<uint32_t*>(lds + kOffBm);
+  int* beg = reinterpret_cast<int*>(lds + kOffBeg);
+  const int64_t my_p = p0 + t;
+  int cur = 0, cnt = 0, nid = kNoIdx;
+  float sm[NJ], ss[NJ], sh[NJ];
+  int sam[NJ], sa_l[NJ];
+  if (!STORE) {
+    cnt = (t < kTP && my_p < P.n_rows) ? P.scount[my_p] : 0;
+    // first recorded id at or after this split's first vocabulary id
+    const int sv0 = c_begin * kTV;
+    int lo = 0, hi = cnt;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((int)(P.skey[my_p * P.k + mid] >> 32) < sv0) lo = mid + 1; else hi = mid;
+    }
+    cur = lo;
+    nid = cur < cnt ? (int)(P.skey[my_p * P.k + cur] >> 32) : kNoIdx;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t p = p0 + wp * kWR + j * 32 + lc;
+      sm[j] = -FLT_MAX; ss[j] = 0.f; sh[j] = 0.f; sam[j] = kNoIdx;
+      sa_l[j] = p < P.n_rows ? P.sa[p] : -1;
+    }
+  }
+  // Hit words of chunk ck for row t: bit (v - v0) of word (v - v0) / 32.
+  auto setup = [&](int ck) {
+    if (t >= kTP) return;
+    const int v0 = ck * kTV, v1 = v0 + kTV;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) bm[t * 8 + q] = 0u;
+    beg[t] = cur;
+    while (nid < v1) {
+      const int o = nid - v0;
+      bm[t * 8 + (o >> 5)] |= 1u << (o & 31);
+      ++cur;
+      nid = cur < cnt ? (int)(P.skey[my_p * P.k + cur] >> 32) : kNoIdx;
+    }
+  };
+
+  auto epilogue = [&](int ck) {
+    const int v0 = ck * kTV;
+    if (STORE) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int64_t p = p0 + wp * kWR + j * 32 + lc;
+        if (p >= P.n_rows) continue;
+        float* orow = P.out + p * P.os;
+#pragma unroll
+        for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int v = v0 + wv * 128 + bi * 32 + lm_row(i, h);
+            if (v < V) orow[v] = acc[bi][j][i];
+          }
+      }
+      return;
+    }
+    const bool ragged = v0 + kTV > V;
+    if (ragged) {
+      // row offset bi * 32 + 8 (i / 4) + i % 4 (a constant) against this
+      // lane's bound, so no per-element index is kept in registers
+      const int lim = V - v0 - wv * 128 - 4 * h;
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const bool out = bi * 32 + 8 * (i >> 2) + (i & 3) >= lim;
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) acc[bi][j][i] = out ? -INFINITY : acc[bi][j][i];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int ploc = wp * kWR + j * 32 + lc;
+      // chunk maximum of this lane's 64 logits of row ploc
+      float bmx = -INFINITY;
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) bmx = fmaxf(bmx, acc[bi][j][i]);
+      if (bmx > sm[j]) {
+        // first (lowest id) element equal to the new maximum
+        int e = 0;
+#pragma unroll
+        for (int bi = 3; bi >= 0; --bi)
+#pragma unroll
+          for (int i = 15; i >= 0; --i) e = acc[bi][j][i] == bmx ? bi * 16 + i : e;
+        sam[j] = v0 + wv * 128 + (e >> 4) * 32 + lm_row(e & 15, h);
+      }
+      const float mn = fmaxf(sm[j], bmx);
+      const float r = exp2_fast((sm[j] - mn) * c);
+      sh[j] = ss[j] > 0.f ? r * (sh[j] - (mn - sm[j]) * c * ss[j]) : 0.f;
+      ss[j] *= r;
+      sm[j] = mn;
+      const float mc = mn * c;
+      float s_acc = 0.f, h_acc = 0.f;
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) {
+        const int vb = v0 + wv * 128 + bi * 32;    // first id of the block
+        const uint32_t hw = bm[ploc * 8 + wv * 4 + bi];
+        uint32_t word = hw;
+        if (ragged) {
+          const int nv = V - vb;                    // valid ids in the block
+          word |= nv <= 0 ? 0xffffffffu : (nv >= 32 ? 0u : ~((1u << nv) - 1u));
+        }
+        const uint32_t wh = word >> (4 * h);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float y = fmaf(acc[bi][j][i], c, -mc);
+          const float e = exp2_fast(y);
+          const bool ex = (wh >> (8 * (i >> 2) + (i & 3))) & 1u;
+          s_acc += ex ? 0.f : e;
+          h_acc += ex ? 0.f : e * y;
+        }
+        // Captures: logits at recorded ids (rare) and at the sampled id.
+        uint32_t bits = hw & (0x0f0f0f0fu << (4 * h));   // this lane's rows
+        while (bits) {
+          const int o = __builtin_ctz(bits);
+          bits &= bits - 1u;
+          const int ih = (o >> 3) * 4 + (o & 3);
+          float z = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) z = i == ih ? acc[bi][j][i] : z;
+          const int64_t p = p0 + ploc;
+          const int v = vb + o;
+          for (int q = beg[ploc]; q < P.k; ++q) {
+            const long long kv = P.skey[p * P.k + q];
+            if ((int)(kv >> 32) == v) {
+              P.head_raw[p * P.k + (int)(kv & 0xffffffff)] = z;
+              break;
+            }
+          }
+        }
+        const unsigned ao = (unsigned)(sa_l[j] - vb);
+        if (ao < 32u && ((ao >> 2) & 1u) == (unsigned)h) {
+          const int ia = (int)((ao >> 3) * 4 + (ao & 3));
+          float za = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) za = i == ia ? acc[bi][j][i] : za;
+          P.za[p0 + ploc] = za;
+        }
+      }
+      ss[j] += s_acc;
+      sh[j] += h_acc;
+    }
+  };
+
+  // ------------------------------------------------------------ main loop
+  load(0);
+  store(0);
+  if (!STORE) setup(c_begin);
+  __syncthreads();
+  for (int g = 0; g < total; ++g) {
+    const int ks = g % ST;
+    if (!STORE && ks == 0 && g > 0) {
+      setup(c_begin + g / ST);
+      __syncthreads();
+    }
+    const bool more = g + 1 < total;
+    if (more) load(g + 1);
+    compute(g & 1);
+    if (more) store((g + 1) & 1);
+    if (ks == ST - 1) {
+      // after the store: no prefetched operands are live in registers
+      epilogue(c_begin + g / ST);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
+    }
+    __syncthreads();
+  }
+  if (STORE) return;
+
+  // ------------------------------------------------------------ merge
+  // lanes l and l ^ 32 hold the same rows; waves wv = 0, 1 hold the same rows
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const float m2 = __shfl_xor(sm[j], 32), s2 = __shfl_xor(ss[j], 32);
+    const float h2 = __shfl_xor(sh[j], 32);
+    const int a2 = __shfl_xor(sam[j], 32);
+    lm_merge(sm[j], ss[j], sh[j], sam[j], m2, s2, h2, a2, c);
+  }
+  float4* xch = reinterpret_cast<float4*>(lds);  // operand buffers are free now
+  if (wv == 1 && h == 0) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      xch[wp * kWR + j * 32 + lc] = make_float4(sm[j], ss[j], sh[j], __int_as_float(sam[j]));
+  }
+  __syncthreads();
+  if (wv == 0 && h == 0) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int ploc = wp * kWR + j * 32 + lc;
+      const float4 o = xch[ploc];
+      lm_merge(sm[j], ss[j], sh[j], sam[j], o.x, o.y, o.z, __float_as_int(o.w), c);
+      const int64_t p = p0 + ploc;
+      if (p < P.n_rows)
+        P.state[(int64_t)split * P.n_rows + p] =
+            make_float4(sm[j], ss[j], sh[j], __int_as_float(sam[j]));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Finalize: one wave per row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_lm_finalize(LmParams P) {
+  __shared__ uint32_t sh_status;
+  const int t = threadIdx.x, l = t & 63;
+  const int64_t p = (int64_t)blockIdx.x * 4 + (t >> 6);
+  if (t == 0) sh_status = 0u;
+  __syncthreads();
+  const int K = P.k;
+  const float c = P.c;
+  const float qnan = __builtin_nanf("");
+  if (p < P.n_rows) {
+    float* stats = P.row_stats + p * SC_NSTATS;
+    int32_t* ridx = P.row_idx + p * 2;
+    const int resp = P.resp_idx ? P.resp_idx[p] : 0;
+    if (resp < 0) {
+      if (l == 0) {
+        stats[SC_STAT_LSE] = 0.f; stats[SC_STAT_LOGP_A] = 0.f; stats[SC_STAT_TAIL] = 0.f;
+        stats[SC_STAT_P_H] = 0.f; stats[SC_STAT_ENTROPY] = 0.f;
+        ridx[0] = -1; ridx[1] = -1;
+      }
+      if (P.head_logp)
+        for (int k = l; k < K; k += kWave) P.head_logp[p * K + k] = 0.f;
+    } else {
+      uint32_t fl = P.sflags[p];
+      // merge the split states in a fixed butterfly order
+      float m = -FLT_MAX, s = 0.f, hy = 0.f;
+      int am = kNoIdx;
+      if (l < P.splits) {
+        const float4 st = P.state[(int64_t)l * P.n_rows + p];
+        m = st.x; s = st.y; hy = st.z; am = __float_as_int(st.w);
+      }
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o), h2 = __shfl_xor(hy, o);
+        const int a2 = __shfl_xor(am, o);
+        lm_merge(m, s, hy, am, m2, s2, h2, a2, c);
+      }
+      // recorded ids: their logits were captured by the main kernel
+      float sH = 0.f, hH = 0.f;
+      bool ninf = false;
+      int aslot = kNoIdx;
+      const int32_t a = P.sampled[p];
+      for (int k = l; k < K; k += kWave) {
+        const float z = fl ? 0.f : P.head_raw[p * K + k];
+        const float y = (z - m) * c;
+        const float e = exp2_fast(y);
+        ninf |= !(z > -INFINITY);
+        sH += e;
+        hH += e > 0.f ? e * y : 0.f;
+        if (P.head_ids[p * K + k] == a) aslot = min(aslot, k);
+      }
+      sH = wave_sum(sH);
+      hH = wave_sum(hH);
+#pragma unroll
+      for (int o = kWave / 2; o > 0; o >>= 1) aslot = min(aslot, __shfl_xor(aslot, o));
+      const float stot = s + sH;
+      const float log2s = log2f(stot);
+      const float za = fl ? 0.f : P.za[p];
+      if (!(stot < INFINITY) || !(m > -FLT_MAX) || !(m < INFINITY) || !(za > -INFINITY) ||
+          !(hy + hH == hy + hH) || wave_or(ninf ? 1u : 0u))
+        fl |= SC_DEV_NONFINITE;
+      const bool bad = fl != 0;
+      float ph = 0.f;
+      for (int k = l; k < K; k += kWave) {
+        const float z = bad ? 0.f : P.head_raw[p * K + k];
+        const float l2 = (z - m) * c - log2s;
+        ph += exp2_fast(l2 + 32.f) * 0x1p-32f;
+        if (P.head_logp) P.head_logp[p * K + k] = bad ? qnan : l2 * kLn2;
+      }
+      ph = wave_sum(ph);
+      if (l == 0) {
+        stats[SC_STAT_LSE] = bad ? qnan : (m * c + log2s) * kLn2;
+        stats[SC_STAT_LOGP_A] = bad ? qnan : ((za - m) * c - log2s) * kLn2;
+        stats[SC_STAT_TAIL] = bad ? qnan : s / stot;
+        stats[SC_STAT_P_H] = bad ? qnan : ph;
+        stats[SC_STAT_ENTROPY] = bad ? qnan : (log2s - (hy + hH) / stot) * kLn2;
+        ridx[0] = bad ? -1 : am;
+        ridx[1] = bad ? -1 : (aslot == kNoIdx ? -1 : aslot);
+        if (fl) atomicOr(&sh_status, fl);
+      }
+    }
+  }
+  __syncthreads();
+  if (t == 0 && sh_status && P.dev_status) atomicOr(P.dev_status, sh_status);
+}
+
+}  // namespace
+
+hipError_t launch_lmhead(const LmParams& P, bool store_logits, hipStream_t s) {
+  static bool attr_done[2] = {false, false};
+  const int per_round = 8 * P.lm_pt;                  // row tiles per group round
+  const int grid = ((P.n_ptiles + per_round - 1) / per_round) * 8 * P.lm_pt * P.splits;
+  if (store_logits) {
+    if (!attr_done[1]) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lm_main<true>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+      if (e != hipSuccess) return e;
+      attr_done[1] = true;
+    }
+    hipLaunchKernelGGL(k_lm_main<true>, dim3(grid), dim3(kB), kLds, s, P);
+    return hipGetLastError();
+  }
+  if (!attr_done[0]) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lm_main<false>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (e != hipSuccess) return e;
+    attr_done[0] = true;
+  }
+  hipLaunchKernelGGL(k_lm_stage, dim3((unsigned)P.n_rows), dim3(256), 0, s, P);
+  hipLaunchKernelGGL(k_lm_main<false>, dim3(grid), dim3(kB), kLds, s, P);
+  hipLaunchKernelGGL(k_lm_finalize, dim3((unsigned)((P.n_rows + 3) / 4)), dim3(256), 0, s, P);
+  return hipGetLastError();
+}
+
+}  // namespace sc

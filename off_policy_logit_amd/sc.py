@@ -47,6 +47,10 @@ _SIGS = {
     "sc_group_norm": [_vp, _i32, _i32, _i32, _f32, _vp, _vp],
     "sc_count_valid": [_vp, _i64, _vp, _i32, _vp],
     "sc_batch_sums": [_vp, _vp, _i64, _vp, _vp, _i32, _vp],
+    "sc_lmhead_workspace_size": [_i64, _i64, _i32],
+    "sc_logprobs_lmhead": [_vp, _i64, _i32, _i64, _vp, _i64, _i64, _vp, _i32, _vp,
+                           _vp, _f32, _vp, _vp, _vp, _vp, _i64, _vp, _vp],
+    "sc_lmhead_logits": [_vp, _i64, _i32, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
     "sc_status_string": [ctypes.c_int],
     "sc_version": [],
 }
@@ -70,7 +74,8 @@ def lib():
         for name, args in _SIGS.items():
             fn = getattr(L, name)
             fn.argtypes = args
-            fn.restype = ctypes.c_char_p if name == "sc_status_string" else ctypes.c_int
+            fn.restype = {"sc_status_string": ctypes.c_char_p,
+                          "sc_lmhead_workspace_size": ctypes.c_int64}.get(name, ctypes.c_int)
         _lib = L
     return _lib
 
@@ -255,3 +260,61 @@ def batch_sums(row_stats, resp_idx, n_valid, out=None, accumulate=False,
 
 def version():
     return lib().sc_version()
+
+
+# ---------------------------------------------------------------------------
+# Fused LM-head statistics
+# ---------------------------------------------------------------------------
+def lmhead_workspace_size(n_rows, vocab, k):
+    """sc_lmhead_workspace_size: bytes of scratch sc_logprobs_lmhead needs."""
+    size = lib().sc_lmhead_workspace_size(int(n_rows), int(vocab), int(k))
+    if size < 0:
+        _check(size)
+    return size
+
+
+def _bf16_matrix(t, name):
+    if t.dtype != torch.bfloat16 or t.dim() != 2 or t.stride(1) != 1:
+        raise TypeError(f"{name} must be a bf16 [rows, d] tensor with unit column stride")
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def logprobs_lmhead(hidden, weight, head_ids, sampled, resp_idx=None,
+                    temperature=1.0, out=None, workspace=None, dev_status=None,
+                    stream=None):
+    """sc_logprobs_lmhead: the outputs of logprobs() for logits hidden @ weight.T,
+    without materialising the logits."""
+    n, d, hs = _bf16_matrix(hidden, "hidden")
+    V, dw, ws = _bf16_matrix(weight, "weight")
+    if dw != d:
+        raise ValueError("hidden and weight disagree on d")
+    _need(head_ids, torch.int32, "head_ids")
+    _need(sampled, torch.int32, "sampled")
+    if resp_idx is not None:
+        _need(resp_idx, torch.int32, "resp_idx")
+    k = head_ids.shape[1]
+    out = out or _alloc_stats(n, k, hidden.device)
+    need = lmhead_workspace_size(n, V, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
+    _check(lib().sc_logprobs_lmhead(
+        _ptr(hidden), n, d, hs, _ptr(weight), V, ws, _ptr(head_ids), k,
+        _ptr(sampled), _ptr(resp_idx), float(temperature), _ptr(out["row_stats"]),
+        _ptr(out["row_idx"]), _ptr(out.get("head_logp")), _ptr(workspace),
+        workspace.numel(), _ptr(dev_status), _stream(stream)))
+    return out
+
+
+def lmhead_logits(hidden, weight, out=None, stream=None):
+    """sc_lmhead_logits: fp32 hidden @ weight.T from the fused kernel's GEMM."""
+    n, d, hs = _bf16_matrix(hidden, "hidden")
+    V, dw, ws = _bf16_matrix(weight, "weight")
+    if dw != d:
+        raise ValueError("hidden and weight disagree on d")
+    if out is None:
+        out = torch.empty(n, V, dtype=torch.float32, device=hidden.device)
+    if out.dtype != torch.float32 or out.dim() != 2 or out.stride(1) != 1:
+        raise TypeError("out must be a float32 [n, >= vocab] tensor with unit column stride")
+    _check(lib().sc_lmhead_logits(_ptr(hidden), n, d, hs, _ptr(weight), V, ws,
+                                  _ptr(out), out.stride(0), _stream(stream)))
+    return out

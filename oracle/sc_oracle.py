@@ -27,8 +27,8 @@ states, for one generated position:
 Readings taken where the page is silent (each is listed in the design notes):
 
 * p is the trainer policy and q the recorded behaviour probabilities (the
-  gradient flows through log p_a; the tail is proportional to the "current
-  policy").
+  gradient flows through log p_a; the tail follows the shape of the policy
+  being trained).
 * 1 - P_H is evaluated as the direct off-head sum tau = sum_{v not in H} p_v,
   equal in exact arithmetic and free of cancellation.
 * The behaviour estimate is mu_hat_v = q_k on H and rho * p_v off H.
@@ -55,6 +55,10 @@ mean (the paper's mean-only setup the release note mentions).
 
 bf16 rounding: round to nearest, ties to even (lecture notes "RL systems for
 agents", section 4, where the cast is described).
+
+LM head: the trainer's logits are the final hidden states times the
+vocabulary projection, z = X W^T (one row of W per vocabulary id); the fused
+LM-head path computes the same statistics from X and W without storing z.
 """
 from __future__ import annotations
 
@@ -331,3 +335,20 @@ def bf16_rne(x):
     mag = np.where(mag > max_bf16, np.inf, mag)
     out[fin] = np.sign(xf) * mag
     return out
+
+
+def lmhead_logits(hidden, weight):
+    """Trainer logits z = X W^T of the LM head, in float64.
+
+    hidden: (n, d) final hidden states, weight: (V, d) vocabulary projection
+    with one row per id (both given as exactly widened bf16 values).  The
+    Score Centering page's trainer scores the policy from these logits over
+    the full vocabulary (section "Score Centering"); the product is the
+    library matmul in float64, whose error on bf16 inputs (d <= 8192) is far
+    below any fp32 tolerance.
+    """
+    X = np.asarray(hidden, dtype=np.float64)
+    W = np.asarray(weight, dtype=np.float64)
+    if X.ndim != 2 or W.ndim != 2 or X.shape[1] != W.shape[1]:
+        raise ValueError("hidden (n, d) and weight (V, d) must agree on d")
+    return X @ W.T

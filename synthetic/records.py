@@ -24,6 +24,10 @@ Workloads (every draw is seeded):
   z = bf16(scale * (N(0, sd^2) + b_v)) with a Zipf(1.1) per-id bias
   b_v = -1.1 ln(rank_v) over a seeded permutation of ranks; rollout logits
   zr = z + N(0, noise^2) in fp32.
+* ``lmhead_weights`` / ``lmhead_chunk`` (fused LM-head workload, 64 x 8,800
+  positions in the lecture notes' repair batch, d = 4,096): hidden states
+  bf16(N(0, 1)), vocabulary projection bf16(N(0, 0.02^2)) (logit std about
+  1.28), the rollout scoring with bf16(W + N(0, 1e-3^2)).
 * In all of them H = top-K ids of the rollout softmax at temperature T,
   q = the rollout probabilities there (fp32), the sampled token is drawn from
   the rollout softmax by the Gumbel-max rule, and its rollout log-probability
@@ -233,3 +237,52 @@ def stress_chunk(device, chunk, sigma, chunk_rows=16_384, spec=None,
     out = {key: torch.cat([p[key] for p in parts]) for key in parts[0]}
     out["resp_idx"] = torch.zeros(chunk_rows, dtype=torch.int32, device=device)
     return out
+
+
+# --------------------------------------------------------------------------
+# LM-head workload: hidden states and vocabulary projection (bf16)
+# --------------------------------------------------------------------------
+def lmhead_weights(device, vocab=VOCAB, d=4096, seed=5, w_sd=0.02, drift=1e-3):
+    """Trainer vocabulary projection W = bf16(N(0, w_sd^2)) [vocab, d] and the
+    rollout engine's copy bf16(W + N(0, drift^2)) (its weights differ slightly,
+    as a low-precision rollout's do).  Logit std is about w_sd sqrt(d)."""
+    import torch
+    g = _gen(device, seed)
+    w = torch.empty(vocab, d, device=device, dtype=torch.bfloat16)
+    w_roll = torch.empty_like(w)
+    step = 8192
+    for r0 in range(0, vocab, step):
+        x = torch.randn(min(step, vocab - r0), d, generator=g, device=device) * w_sd
+        w[r0:r0 + x.shape[0]] = x.to(torch.bfloat16)
+        x = w[r0:r0 + x.shape[0]].float()
+        x += torch.randn(x.shape, generator=g, device=device) * drift
+        w_roll[r0:r0 + x.shape[0]] = x.to(torch.bfloat16)
+    return w, w_roll
+
+
+def lmhead_chunk(device, w_roll, rows, seed, temperature=1.0, k=TOPK,
+                 gen_rows=1024):
+    """Rows of the LM-head workload: hidden states X = bf16(N(0, 1)) [rows, d]
+    and the rollout's record (top-k ids and probabilities, sampled id and its
+    log-probability) from the rollout logits X W_roll^T at ``temperature``."""
+    import torch
+    vocab, d = w_roll.shape
+    g = _gen(device, seed)
+    hidden = torch.randn(rows, d, generator=g, device=device).to(torch.bfloat16)
+    wr = w_roll.float()
+    ids, probs, samp, rlp = [], [], [], []
+    for r0 in range(0, rows, gen_rows):
+        x = hidden[r0:r0 + gen_rows].float()
+        lr = torch.log_softmax((x @ wr.T) / temperature, dim=1)
+        top_lp, top_id = torch.topk(lr, k, dim=1)
+        u = torch.rand(lr.shape, generator=g, device=device).clamp_(min=1e-30)
+        a = torch.argmax(lr - torch.log(-torch.log(u)), dim=1)
+        ids.append(top_id.to(torch.int32))
+        probs.append(top_lp.exp().float())
+        samp.append(a.to(torch.int32))
+        rlp.append(lr.gather(1, a[:, None])[:, 0].float())
+        del lr, u
+    del wr
+    return dict(hidden=hidden, head_ids=torch.cat(ids).contiguous(),
+                head_probs=torch.cat(probs).contiguous(),
+                sampled=torch.cat(samp), rollout_logp=torch.cat(rlp).contiguous())

@@ -150,3 +150,59 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(sc, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         sc.lib()
+
+
+# --------------------------------------------------------------------------
+# Fused LM-head entry points
+# --------------------------------------------------------------------------
+def test_lmhead_workspace_size():
+    L = sc.lib()
+    assert L.sc_lmhead_workspace_size(-1, 100, 4) == ARG
+    assert L.sc_lmhead_workspace_size(10, 0, 1) == ARG
+    assert L.sc_lmhead_workspace_size(10, 100, 0) == ARG
+    assert L.sc_lmhead_workspace_size(10, 100, 101) == ARG
+    assert L.sc_lmhead_workspace_size(0, 100, 4) >= 0
+    small = L.sc_lmhead_workspace_size(1000, 4096, 128)
+    big = L.sc_lmhead_workspace_size(2000, 4096, 128)
+    # keys, recorded-id logits, per-split states and per-row scalars
+    assert small >= 1000 * (128 * 12 + 16 * 16 + 16) and big > small
+
+
+FAKE256 = ctypes.c_void_p(0x20000)
+
+
+def lmhead(**kw):
+    a = dict(x=FAKE, n=300, d=256, xs=256, w=FAKE, V=1000, ws=256, ids=FAKE, k=16,
+             sampled=FAKE, resp=NULL, T=1.0, stats=FAKE, idx=FAKE, hlp=NULL,
+             ws_ptr=FAKE256, ws_bytes=1 << 40, dev=NULL, stream=NULL)
+    a.update(kw)
+    return sc.lib().sc_logprobs_lmhead(
+        a["x"], a["n"], a["d"], a["xs"], a["w"], a["V"], a["ws"], a["ids"], a["k"],
+        a["sampled"], a["resp"], a["T"], a["stats"], a["idx"], a["hlp"], a["ws_ptr"],
+        a["ws_bytes"], a["dev"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=NULL), dict(w=NULL), dict(ids=NULL), dict(sampled=NULL), dict(stats=NULL),
+    dict(idx=NULL), dict(ws_ptr=NULL), dict(n=-1), dict(V=0), dict(d=0),
+    dict(xs=255), dict(ws=200), dict(xs=260), dict(x=FAKE2), dict(w=FAKE1),
+    dict(k=0), dict(k=1025, V=5000), dict(k=1001), dict(T=0.0), dict(T=float("inf")),
+    dict(ws_bytes=100), dict(ws_ptr=ctypes.c_void_p(0x20010)), dict(xs=4194312, d=256),
+])
+def test_lmhead_rejects_bad_arguments(kw):
+    assert lmhead(**kw) == ARG
+
+
+def test_lmhead_d_must_be_a_multiple_of_64():
+    assert lmhead(d=200, xs=200, ws=200) == UNSUP
+    assert lmhead(n=0) == OK
+
+
+def test_lmhead_logits_rejects_bad_arguments():
+    L = sc.lib()
+    f = L.sc_lmhead_logits
+    assert f(FAKE, 10, 256, 256, FAKE, 100, 256, NULL, 100, NULL) == ARG
+    assert f(FAKE, 10, 256, 256, FAKE, 100, 256, FAKE, 99, NULL) == ARG
+    assert f(NULL, 10, 256, 256, FAKE, 100, 256, FAKE, 100, NULL) == ARG
+    assert f(FAKE, 10, 100, 256, FAKE, 100, 256, FAKE, 100, NULL) == UNSUP
+    assert f(FAKE, 0, 256, 256, FAKE, 100, 256, FAKE, 100, NULL) == OK

@@ -567,3 +567,31 @@ def test_tiny_generator_shapes_and_record():
         assert 0.0 < d["head_probs"][i].sum() <= 1.0 + 1e-6
         assert np.all(np.diff(d["head_probs"][i]) <= 0)
     assert d["rewards"].shape == (32,)
+
+
+# --------------------------------------------------------------------------
+# LM-head logits z = X W^T
+# --------------------------------------------------------------------------
+def test_lmhead_logits_one_hot_rows_select_weight_columns():
+    # a one-hot hidden state e_j scores every id v by W[v, j]: catches a
+    # transposed operand or a swapped contraction axis
+    rng = np.random.default_rng(31)
+    V, d = 7, 5
+    W = rng.normal(0, 1, (V, d))
+    X = np.eye(d)
+    z = O.lmhead_logits(X, W)
+    assert z.shape == (d, V)
+    np.testing.assert_array_equal(z, W.T)
+
+
+def test_lmhead_logits_gram_diagonal_and_scaling():
+    rng = np.random.default_rng(32)
+    W = rng.normal(0, 1, (6, 9))
+    z = O.lmhead_logits(W, W)
+    np.testing.assert_allclose(np.diag(z), np.sum(W * W, axis=1), rtol=1e-14)
+    np.testing.assert_allclose(z, z.T, rtol=1e-14)
+    X = rng.normal(0, 1, (3, 9))
+    np.testing.assert_allclose(O.lmhead_logits(2.0 * X, W), 2.0 * O.lmhead_logits(X, W),
+                               rtol=1e-14)
+    with pytest.raises(ValueError):
+        O.lmhead_logits(X, W[:, :8])
