@@ -352,3 +352,42 @@ def lmhead_logits(hidden, weight):
     if X.ndim != 2 or W.ndim != 2 or X.shape[1] != W.shape[1]:
         raise ValueError("hidden (n, d) and weight (V, d) must agree on d")
     return X @ W.T
+
+
+def record_topk(z, temperature, k, sampled=None):
+    """The rollout engine's record of one position (rollout side of the method).
+
+    Score Centering page, section "Score Centering": each generated position
+    records the top K behaviour probabilities of the sampling call (their
+    original normalisation kept, so they may sum below one) and, separately,
+    the log-probability of the token actually sampled.
+
+    z: (V,) rollout logits, temperature T, k recorded candidates, sampled id
+    (or None).  The candidates are the k largest logits, ties to the lower
+    id, listed in that order (probability descending, since softmax at T > 0
+    keeps the order of the logits).  Returns dict(flags, head_ids, head_probs,
+    sampled_logp) with head_probs = softmax(z / T) at head_ids in float64.
+    A NaN or +inf logit, an all -inf row, a sampled id outside [0, V) or a
+    sampled id at a -inf logit is a data error: ids -1, floats NaN.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    V = z.shape[0]
+    if not 1 <= k <= V:
+        raise ValueError("k")
+    flags = 0
+    if np.any(np.isnan(z)) or np.any(np.isposinf(z)) or np.all(np.isneginf(z)):
+        flags |= DEV_NONFINITE
+    if sampled is not None:
+        if not 0 <= int(sampled) < V:
+            flags |= DEV_BAD_SAMPLED
+        elif np.isneginf(z[int(sampled)]):
+            flags |= DEV_NONFINITE
+    if flags:
+        return dict(flags=flags, head_ids=np.full(k, -1), head_probs=np.full(k, np.nan),
+                    sampled_logp=float("nan"))
+    logp, _ = trainer_log_softmax(z, temperature)
+    # lexsort: last key is the primary one (logit descending), then id ascending
+    order = np.lexsort((np.arange(V), -z))[:k]
+    return dict(flags=0, head_ids=order.astype(np.int64),
+                head_probs=np.exp(logp[order]),
+                sampled_logp=float(logp[int(sampled)]) if sampled is not None else float("nan"))

@@ -595,3 +595,62 @@ def test_lmhead_logits_gram_diagonal_and_scaling():
                                rtol=1e-14)
     with pytest.raises(ValueError):
         O.lmhead_logits(X, W[:, :8])
+
+
+# --------------------------------------------------------------------------
+# Rollout-side record: top-k candidates and the sampled token's log-prob
+# --------------------------------------------------------------------------
+def test_record_matches_torch_topk_on_distinct_logits():
+    rng = np.random.default_rng(41)
+    for T in (1.0, 0.6):
+        z = rng.normal(0, 3, 5000)
+        r = O.record_topk(z, T, 128, sampled=17)
+        lp = torch.log_softmax(torch.tensor(z, dtype=torch.float64) / T, 0)
+        top = torch.topk(lp, 128)
+        np.testing.assert_array_equal(r["head_ids"], top.indices.numpy())
+        np.testing.assert_allclose(r["head_probs"], top.values.exp().numpy(), rtol=1e-12)
+        assert abs(r["sampled_logp"] - float(lp[17])) < 1e-12
+        assert np.all(np.diff(r["head_probs"]) <= 0)
+
+
+def test_record_ties_go_to_the_lower_id_and_probs_keep_normalisation():
+    z = np.zeros(300)
+    r = O.record_topk(z, 1.0, 10)
+    np.testing.assert_array_equal(r["head_ids"], np.arange(10))
+    np.testing.assert_allclose(r["head_probs"], np.full(10, 1 / 300), rtol=1e-14)
+    # a tie group straddling the cut: ids 5, 9, 200 share the 2nd largest logit
+    z = np.full(400, -1.0)
+    z[[5, 9, 200]] = 2.0
+    z[300] = 3.0
+    r = O.record_topk(z, 1.0, 3)
+    np.testing.assert_array_equal(r["head_ids"], [300, 5, 9])
+    # k = V records everything: the probabilities sum to one
+    z = np.random.default_rng(2).normal(0, 1, 64)
+    r = O.record_topk(z, 0.8, 64)
+    assert abs(r["head_probs"].sum() - 1.0) < 1e-12
+    assert sorted(r["head_ids"].tolist()) == list(range(64))
+
+
+def test_record_shift_invariance_and_temperature_scaling():
+    rng = np.random.default_rng(43)
+    z = rng.normal(0, 2, 1000)
+    a = O.record_topk(z, 0.5, 50, sampled=3)
+    b = O.record_topk(z + 7.25, 0.5, 50, sampled=3)
+    c = O.record_topk(z / 0.5, 1.0, 50, sampled=3)
+    for o in (b, c):
+        np.testing.assert_array_equal(a["head_ids"], o["head_ids"])
+        np.testing.assert_allclose(a["head_probs"], o["head_probs"], rtol=1e-12)
+        assert abs(a["sampled_logp"] - o["sampled_logp"]) < 1e-12
+
+
+def test_record_flags_and_masked_logits():
+    z = np.zeros(10)
+    z[4] = np.nan
+    assert O.record_topk(z, 1.0, 3)["flags"] == O.DEV_NONFINITE
+    assert O.record_topk(np.full(5, -np.inf), 1.0, 2)["flags"] == O.DEV_NONFINITE
+    assert O.record_topk(np.zeros(5), 1.0, 2, sampled=5)["flags"] == O.DEV_BAD_SAMPLED
+    z = np.array([0.0, -np.inf, 1.0, -np.inf])
+    assert O.record_topk(z, 1.0, 2, sampled=1)["flags"] == O.DEV_NONFINITE
+    r = O.record_topk(z, 1.0, 4, sampled=0)      # -inf entries fill the tail, p = 0
+    np.testing.assert_array_equal(r["head_ids"], [2, 0, 1, 3])
+    assert r["head_probs"][2] == 0.0 and r["head_probs"][3] == 0.0
