@@ -49,6 +49,9 @@ BYTES_PER_POSITION = 2 * VOCAB + 8 * K + 16 + 2 * VOCAB + 8 * K + 64 + 8
 # Stats-only pass (sc_logprobs): logits 2V, ids 4K, sampled, resp_idx read;
 # log p at H 4K, 5 of the statistics and 2 indices written.
 BYTES_PER_POSITION_STATS = 2 * VOCAB + 4 * K + 8 + 4 * K + 20 + 8
+# Rollout-side record (sc_record): logits 2V and the sampled id read; ids 4K,
+# probabilities 4K and the sampled log-probability written.
+BYTES_PER_POSITION_RECORD = 2 * VOCAB + 4 + 8 * K + 4
 
 
 def source_digest():
@@ -256,6 +259,22 @@ def main():
     torch.cuda.synchronize()
     stats_ms = e0.elapsed_time(e1) / reps
 
+    # rollout-side record (sc_record) on the same logits, secondary line
+    rec = dict(head_ids=torch.empty(n, K, dtype=torch.int32, device=dev),
+               head_probs=torch.empty(n, K, device=dev),
+               sampled_logp=torch.empty(n, device=dev))
+    for _ in range(2):
+        sc.record(d["logits"], K, sampled=d["sampled"], dev_status=status, **rec)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        sc.record(d["logits"], K, sampled=d["sampled"], dev_status=status, **rec)
+    e1.record()
+    torch.cuda.synchronize()
+    rec_ms = e0.elapsed_time(e1) / reps
+    if int(status.item()) != 0:
+        raise RuntimeError(f"record device status {int(status.item())}")
+
     lm = None if args.no_lmhead else lmhead_measure(dev, max(3, args.steps // 10))
 
     bytes_launch = n * BYTES_PER_POSITION
@@ -292,6 +311,9 @@ def main():
             "stats_only_positions_per_s": round(n / (stats_ms * 1e-3), 1),
             "stats_only_kernel_ms": round(stats_ms, 4),
             "stats_only_GBps": round(n * BYTES_PER_POSITION_STATS / (stats_ms * 1e-3) / 1e9, 1),
+            "record_positions_per_s": round(n / (rec_ms * 1e-3), 1),
+            "record_kernel_ms": round(rec_ms, 4),
+            "record_GBps": round(n * BYTES_PER_POSITION_RECORD / (rec_ms * 1e-3) / 1e9, 1),
             "lmhead": lm,
         },
     }

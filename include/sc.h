@@ -302,6 +302,38 @@ int sc_lmhead_logits(const void* hidden, int64_t n_rows, int32_t d,
                      int64_t weight_stride, float* logits, int64_t logits_stride,
                      void* stream);
 
+/*
+ * sc_record -- the rollout engine's record of each generated position.
+ *
+ * Score Centering page, section "Score Centering": for every generated
+ * position the rollout records the top K behaviour probabilities of its
+ * sampling call (original normalisation kept, so they may sum below one) and,
+ * separately, the log-probability of the token it sampled.  This produces
+ * that record from the rollout logits: head_ids are the k largest logits
+ * (ties go to the lower id), listed largest first; head_probs their
+ * probabilities softmax(z / T) in fp32; sampled_logp = log softmax(z / T) at
+ * the sampled id.  The selection is exact (a decision on the input values),
+ * and head_probs uses the same fp32 arithmetic as sc_logprobs.
+ *
+ *   logits        device bf16/fp32 [n_rows, row_stride >= vocab]
+ *   temperature   finite, > 0
+ *   k             1 <= k <= min(vocab, 1024)
+ *   sampled       device int32 [n_rows] or NULL (then sampled_logp must be
+ *                 NULL too)
+ *   head_ids      device int32 [n_rows, k]  (written)
+ *   head_probs    device float [n_rows, k]  (written)
+ *   sampled_logp  device float [n_rows] or NULL (written)
+ *   dev_status    as for sc_logprobs: a NaN or +inf logit, an all -inf row,
+ *                 a sampled id outside [0, vocab) or at a -inf logit flags
+ *                 the row (ids -1, floats NaN)
+ * Rows whose top-k boundary sits inside a large group of equal logits take
+ * extra passes over the row (at most six) but give the same exact result.
+ */
+int sc_record(const void* logits, int logits_dtype, int64_t n_rows, int64_t vocab,
+              int64_t row_stride, float temperature, int32_t k,
+              const int32_t* sampled, int32_t* head_ids, float* head_probs,
+              float* sampled_logp, uint32_t* dev_status, void* stream);
+
 /* Library version, major * 10000 + minor * 100 + patch. */
 int sc_version(void);
 

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = [os.path.join(CSRC, "sc_api.cpp"), os.path.join(CSRC, "sc_kernels.hip"),
-           os.path.join(CSRC, "sc_lmhead.hip")]
+           os.path.join(CSRC, "sc_lmhead.hip"), os.path.join(CSRC, "sc_record.hip")]
 LIB = os.path.join(HERE, "libsc.so")
 ARCH = "gfx950"
 

@@ -399,6 +399,44 @@ int sc_lmhead_logits(const void* hidden, int64_t n_rows, int32_t d, int64_t hidd
   return e == hipSuccess ? SC_OK : SC_ERR_HIP;
 }
 
+int sc_record(const void* logits, int logits_dtype, int64_t n_rows, int64_t vocab,
+              int64_t row_stride, float temperature, int32_t k, const int32_t* sampled,
+              int32_t* head_ids, float* head_probs, float* sampled_logp,
+              uint32_t* dev_status, void* stream) {
+  if (!dtype_ok(logits_dtype)) return SC_ERR_ARG;
+  if (n_rows < 0 || n_rows > kMaxI32) return SC_ERR_ARG;
+  if (vocab < 1 || vocab > kMaxI32 - 64 || row_stride < vocab) return SC_ERR_ARG;
+  if (k < 1 || k > kMaxK || (int64_t)k > vocab) return SC_ERR_ARG;
+  if (!(std::isfinite(temperature) && temperature > 0.f)) return SC_ERR_ARG;
+  if (!logits || !head_ids || !head_probs) return SC_ERR_ARG;
+  if (!aligned(logits, esize(logits_dtype)) || !aligned(head_ids, 4) ||
+      !aligned(head_probs, 4) || (sampled && !aligned(sampled, 4)) ||
+      (sampled_logp && !aligned(sampled_logp, 4)) || (dev_status && !aligned(dev_status, 4)))
+    return SC_ERR_ARG;
+  if (sampled_logp && !sampled) return SC_ERR_ARG;
+  sc::RecParams P{};
+  P.logits = logits;
+  P.in_dtype = logits_dtype;
+  P.vector = vector_ok(logits, logits_dtype, row_stride) ? 1 : 0;
+  P.n_rows = n_rows;
+  P.vocab = vocab;
+  P.row_stride = row_stride;
+  P.c = (float)(1.4426950408889634 / (double)temperature);
+  P.k = k;
+  P.sampled = sampled;
+  P.head_ids = head_ids;
+  P.head_probs = head_probs;
+  P.sampled_logp = sampled_logp;
+  P.dev_status = dev_status;
+  if (sc::record_lds_bytes(k) > kMaxLds) return SC_ERR_UNSUPPORTED;
+  if (n_rows == 0) return SC_OK;
+  int cus = 0;
+  int st = cu_count(&cus);
+  if (st != SC_OK) return st;
+  hipError_t e = sc::launch_record(P, cus, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SC_OK : SC_ERR_HIP;
+}
+
 const char* sc_status_string(int status) {
   switch (status) {
     case SC_OK: return "SC_OK";

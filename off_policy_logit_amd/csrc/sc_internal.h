@@ -127,6 +127,24 @@ struct LmParams {
 };
 
 hipError_t launch_lmhead(const LmParams& P, bool store_logits, hipStream_t s);
+
+// Rollout-side record (sc_record): top-k of the rollout softmax per row.
+struct RecParams {
+  const void* logits;
+  int in_dtype;          // 0 fp32, 1 bf16
+  int vector;            // 1: 16-byte vector path
+  int64_t n_rows, vocab, row_stride;
+  float c;               // log2(e) / T
+  int32_t k;
+  const int32_t* sampled;
+  int32_t* head_ids;
+  float* head_probs;
+  float* sampled_logp;
+  uint32_t* dev_status;
+  int cap;               // per-wave candidate buffer (set by the launcher)
+};
+size_t record_lds_bytes(int k);
+hipError_t launch_record(RecParams P, int cus, hipStream_t s);
 hipError_t launch_group_norm(const float* r, int n_groups, int G, int mode,
                              float eps, float* adv, hipStream_t s);
 hipError_t launch_count_valid(const int32_t* resp, int64_t n, int64_t* out,

@@ -1,0 +1,448 @@
+// Rollout-side record of the SC correction for gfx950: per position, the
+// top-k candidate ids of the rollout softmax with their probabilities and the
+// log-probability of the sampled token (Score Centering page, section "Score
+// Centering": the rollout records the top K behaviour probabilities of the
+// sampling call, keeping their normalisation, and the sampled token's
+// log-probability separately).
+//
+// One workgroup per row (persistent grid).  Candidates are ordered by the
+// 64-bit key (order(z) << 32 | ~id): larger logit first, equal logits by
+// lower id, every key distinct.  The row is streamed once:
+//   * online max and sum of 2^((z - m) c) give the row's log-sum-exp;
+//   * a 4096-bin histogram of the key's top 12 bits (sign, exponent, 3
+//     mantissa bits) counts the elements at or above each wave's running
+//     lower bound b_w on the bin of the k-th largest key, and each wave
+//     appends those elements to its own LDS candidate buffer;
+//   * b_w is raised from the histogram as the stream goes (any partial count
+//     gives a valid lower bound), and the buffer is compacted to it.
+// After the stream the exact bin b* of the k-th largest key is read off the
+// histogram (exact above every b_w), the buffered keys at or above b* are
+// sorted (bitonic, LDS) and the first k are the record.  A row whose
+// candidates overflow a buffer or the sort array (heavy ties) takes the exact
+// fallback: radix selection over the remaining key bits with further passes
+// over the row, at most five, then one collection pass.  A wave whose buffer
+// overflowed keeps counting (so the histogram stays exact above every bound)
+// but stops buffering.
+#include <hip/hip_runtime.h>
+#include <float.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "sc.h"
+#include "sc_device.h"
+#include "sc_internal.h"
+
+namespace sc {
+namespace {
+
+#ifndef SC_RECORD_BLOCK
+#define SC_RECORD_BLOCK 256
+#endif
+#ifndef SC_RECORD_TILE
+#define SC_RECORD_TILE 4
+#endif
+constexpr int kRB = SC_RECORD_BLOCK;     // threads per workgroup
+constexpr int kRNW = kRB / kWave;        // waves
+constexpr int kHBits = 12;               // histogram bits of the key
+constexpr int kNBins = 1 << kHBits;
+constexpr int kSortMax = 2048;           // sort array (overlays the histogram)
+constexpr int kRU = SC_RECORD_TILE;      // vectors per thread per iteration
+static_assert(kSortMax * 8 == kNBins * 4, "sort array overlays the histogram");
+
+// Monotone unsigned key of a float (NaN excluded by the caller); -0 -> +0.
+SC_DEV uint32_t okey(float x) {
+  uint32_t b = __float_as_uint(x);
+  b = (b == 0x80000000u) ? 0u : b;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+SC_DEV float okey_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+SC_DEV unsigned long long key64(float x, uint32_t id) {
+  return ((unsigned long long)okey(x) << 32) | (unsigned long long)(~id);
+}
+SC_DEV int bin_of(uint32_t k) { return (int)(k >> (32 - kHBits)); }
+// Smallest float whose bin is >= b (so x >= bin_floor(b) <=> bin(x) >= b for
+// every non-NaN x); -inf below the -inf bin.
+SC_DEV float bin_floor(int b) {
+  const uint32_t kk = (uint32_t)b << (32 - kHBits);
+  if (kk <= 0x007fffffu) return -INFINITY;       // at or below the key of -inf
+  if (kk > 0xff800000u) return INFINITY;         // above +inf (NaN keys)
+  return okey_value(kk);
+}
+SC_DEV int lane_rank(unsigned long long bal) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+}
+
+template <typename T, bool VECTOR>
+__global__ __launch_bounds__(kRB) void k_record(RecParams P) {
+  using IO = RowIO<T, VECTOR>;
+  using Raw = typename IO::raw;
+  constexpr int N = IO::N;
+  constexpr int B = kRB;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int V = (int)P.vocab;
+  const int K = P.k;
+  const int cap = P.cap;
+  const float c = P.c;
+  const int n_full = V / N, rem = V - n_full * N;
+
+  extern __shared__ __align__(16) unsigned char lds[];
+  uint32_t* hist = reinterpret_cast<uint32_t*>(lds);                       // [kNBins]
+  unsigned long long* sarr = reinterpret_cast<unsigned long long*>(lds);   // [kSortMax]
+  unsigned long long* buf = reinterpret_cast<unsigned long long*>(lds + kNBins * 4) +
+                            (size_t)w * cap;                               // [cap] per wave
+  __shared__ float redf[4 * kRNW];
+  __shared__ int redi[kRNW];
+  // 0: flags, 1: overflow, 2: sort count, 3: status, 4: highest counted bin
+  __shared__ unsigned int sh_u[5];
+  __shared__ int sh_i[2];               // bin and count above it, from find_kth
+
+  const float qnan = __builtin_nanf("");
+  if (t == 0) sh_u[3] = 0u;
+
+  for (int64_t row = blockIdx.x; row < P.n_rows; row += gridDim.x) {
+    const T* zrow = reinterpret_cast<const T*>(P.logits) + row * P.row_stride;
+    __syncthreads();                     // previous row's LDS reads are done
+    for (int i = t; i < kNBins; i += B) hist[i] = 0u;
+    if (t == 0) { sh_u[0] = 0u; sh_u[1] = 0u; sh_u[2] = 0u; sh_u[4] = 0u; }
+    __syncthreads();
+
+    // ------------------------------------------------ exact bin of the k-th key
+    // Thread t sums bins [kNBins - PER (t + 1), kNBins - PER t); a block scan
+    // in thread order (descending bins) finds the bin where the count from the
+    // top reaches `need`; returns it and the count strictly above it.
+    constexpr int PER = kNBins / B;
+    auto find_kth = [&](int need, int& bin_out, int& above_out) {
+      const int hi = kNBins - PER * t - 1;
+      int sum = 0;
+#pragma unroll
+      for (int q = 0; q < PER; ++q) sum += (int)hist[hi - q];
+      int x = sum;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+      }
+      __syncthreads();
+      if (lane == kWave - 1) redi[w] = x;
+      __syncthreads();
+      int wave_off = 0;
+      for (int q = 0; q < w; ++q) wave_off += redi[q];
+      const int incl = wave_off + x, excl = incl - sum;
+      if (excl < need && incl >= need) {
+        int acc = excl;
+        for (int q = 0; q < PER; ++q) {
+          const int h = (int)hist[hi - q];
+          if (acc + h >= need) { sh_i[0] = hi - q; sh_i[1] = acc; break; }
+          acc += h;
+        }
+      }
+      __syncthreads();
+      bin_out = sh_i[0];
+      above_out = sh_i[1];
+    };
+    // -------------------------------------------------------------- stream
+    float m_t = -FLT_MAX, s_t = 0.f;
+    int b_w = 0;            // wave-uniform lower bound on the k-th key's bin
+    float thr = -INFINITY;  // bin_floor(b_w)
+    int cnt = 0;            // wave-uniform number of buffered keys
+    bool ovf = false;       // wave-uniform: this wave's buffer overflowed
+
+    // Raise b_w from the histogram (bins from the highest counted one down
+    // to b_w) and drop buffered keys below it.  Wave-local; counts that other
+    // waves are still adding only make the bound lower (still valid).
+    auto refresh = [&]() {
+      if (ovf) return;
+      int total = 0, found = -1;
+      // start at the highest bin any wave has reported (this wave's max
+      // included); missing a higher count only lowers the bound
+      const float wm = wave_max(m_t);
+      if (lane == 0) atomicMax(&sh_u[4], (unsigned)bin_of(okey(wm)));
+      const int top0 = (int)__atomic_load_n(&sh_u[4], __ATOMIC_RELAXED);
+      for (int top = top0; top >= b_w && found < 0; top -= kWave) {
+        const int bin = top - lane;
+        int x = bin >= b_w ? (int)__atomic_load_n(&hist[bin], __ATOMIC_RELAXED) : 0;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {   // inclusive scan, lane 0 = top bin
+          const int y = __shfl_up(x, o);
+          if (lane >= o) x += y;
+        }
+        const unsigned long long hit = __ballot(total + x >= K);
+        if (hit) found = top - __builtin_ctzll(hit);
+        total += __shfl(x, kWave - 1);
+      }
+      if (found > b_w) {
+        b_w = found;
+        thr = bin_floor(b_w);
+        int kept = 0;
+        for (int base = 0; base < cnt; base += kWave) {
+          const int i = base + lane;
+          const unsigned long long kv = i < cnt ? buf[i] : 0ull;
+          const bool keep = i < cnt && bin_of((uint32_t)(kv >> 32)) >= b_w;
+          const unsigned long long bal = __ballot(keep);
+          // every lane of the group has read before any lane writes
+          if (keep) buf[kept + lane_rank(bal)] = kv;
+          kept += __builtin_popcountll(bal);
+        }
+        cnt = kept;
+      }
+    };
+
+    // One element per lane (`real` false for padding).  All lanes of the wave
+    // call it together.
+    auto consider = [&](float x, int id, bool real) {
+      if (!__ballot(real && x >= thr)) return;
+      if (cnt > cap - kWave) refresh();
+      const uint32_t kx = okey(x);
+      const bool counted = real && bin_of(kx) >= b_w;
+      if (counted) atomicAdd(&hist[bin_of(kx)], 1u);
+      const bool cand = counted && !ovf;
+      const unsigned long long bal = __ballot(cand);
+      if (bal) {
+        const int pos = cnt + lane_rank(bal);
+        if (cand && pos < cap) buf[pos] = key64(x, (uint32_t)id);
+        cnt += __builtin_popcountll(bal);
+        if (cnt > cap) ovf = true;
+      }
+    };
+
+    // Online max / sum and the candidate filter for one vector per lane.
+    auto vec = [&](const float (&v)[N], int j, bool active) {
+      float vm = v[0];
+#pragma unroll
+      for (int i = 1; i < N; ++i) vm = fmaxf(vm, v[i]);
+      const float mn = fmaxf(m_t, vm);
+      s_t *= exp2_fast((m_t - mn) * c);
+      m_t = mn;
+#pragma unroll
+      for (int i = 0; i < N; ++i) s_t += exp2_fast((v[i] - m_t) * c);
+      const bool any = active && vm >= thr;
+      if (__ballot(any)) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) consider(v[i], j * N + i, active);
+      }
+    };
+
+    // Uniform trip count for every thread: tiles of kRU vectors per thread.
+    int iter = 0;
+    for (int j0 = 0; j0 < n_full; j0 += B * kRU, ++iter) {
+      if (iter > 0 && (iter < 4 || (iter & (iter + 1)) == 0)) refresh();  // tiles 1-3, 7, 15, ...
+      Raw r[kRU];
+#pragma unroll
+      for (int u = 0; u < kRU; ++u) {
+        const int j = j0 + u * B + t;
+        r[u] = j < n_full ? IO::template load<false>(zrow, j) : IO::ninf();
+      }
+      if (iter == 0 && K <= B) {
+        // Initial bound: the k-th largest of the B per-thread maxima of this
+        // tile is at most the row's k-th largest logit (they are k distinct
+        // elements), so its bin is a valid b_w.  The maxima are counted in
+        // the histogram only to find that bin, then removed again.
+        float tm = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kRU; ++u) {
+          float v[N];
+          IO::unpack(r[u], v);
+#pragma unroll
+          for (int i = 0; i < N; ++i) tm = fmaxf(tm, v[i]);
+        }
+        const int tb = bin_of(okey(tm));       // NaN maxima only lower the bound
+        atomicAdd(&hist[tb], 1u);
+        __syncthreads();
+        int b0 = 0, ab0 = 0;
+        find_kth(K, b0, ab0);
+        atomicSub(&hist[tb], 1u);
+        if (t == 0) atomicMax(&sh_u[4], (unsigned)bin_of(okey(tm)));
+        __syncthreads();
+        b_w = b0;
+        thr = bin_floor(b_w);
+      }
+#pragma unroll
+      for (int u = 0; u < kRU; ++u) {
+        const int j = j0 + u * B + t;
+        float v[N];
+        IO::unpack(r[u], v);
+        vec(v, j, j < n_full);
+      }
+    }
+    // the partial last vector (vocab not a multiple of N): its owner lane
+    if (rem > 0) {
+      const bool mine = t == (n_full % B);
+      float v[N];
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        v[i] = (mine && i < rem) ? load_elem(zrow, n_full * N + i) : -INFINITY;
+      float vm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < N; ++i) vm = fmaxf(vm, v[i]);
+      if (mine) {
+        const float mn = fmaxf(m_t, vm);
+        s_t *= exp2_fast((m_t - mn) * c);
+        m_t = mn;
+#pragma unroll
+        for (int i = 0; i < N; ++i) s_t += exp2_fast((v[i] - m_t) * c);
+      }
+#pragma unroll
+      for (int i = 0; i < N; ++i) consider(v[i], n_full * N + i, mine && i < rem);
+    }
+    if (ovf && lane == 0) atomicOr(&sh_u[1], 1u);
+
+    // row max and sum
+    float mv = m_t;
+    int dummy = 0;
+    block_argmax<B>(mv, dummy, redf, redi);
+    const float m = mv;
+    float part[1] = {s_t * exp2_fast((m_t - m) * c)};
+    block_sum<B, 1>(part, redf);
+    const float log2s = log2f(part[0]);
+    // a NaN logit makes the sum NaN (exp2 propagates it), +inf makes the max
+    // +inf, an all -inf row leaves the max at -FLT_MAX
+    if (t == 0 && (!(m > -FLT_MAX) || !(m < INFINITY) || !(part[0] < INFINITY)))
+      atomicOr(&sh_u[0], (unsigned)SC_DEV_NONFINITE);
+
+    if (t == 0) { sh_i[0] = 0; sh_i[1] = 0; }
+    int bstar = 0, above = 0;
+    find_kth(K, bstar, above);
+    int count_at = (int)hist[bstar];
+    const uint32_t flags0 = sh_u[0];
+    const bool fast = sh_u[1] == 0u && above + count_at <= kSortMax;
+    __syncthreads();                     // histogram reads done before the overlay
+
+    // --------------------------------------------------------- collect
+    int n_cand = 0;
+    if (flags0) {
+      n_cand = 0;
+    } else if (fast) {
+      const int nb = min(cnt, cap);
+      for (int i = lane; i < nb; i += kWave) {
+        const unsigned long long kv = buf[i];
+        if (bin_of((uint32_t)(kv >> 32)) >= bstar) {
+          const unsigned int pos = atomicAdd(&sh_u[2], 1u);
+          if (pos < (unsigned)kSortMax) sarr[pos] = kv;
+        }
+      }
+      __syncthreads();
+      n_cand = (int)sh_u[2];
+    } else {
+      // Exact fallback: radix selection over the remaining key bits, one
+      // more pass over the row per level, then a collection pass.
+      unsigned long long prefix = (unsigned long long)bstar;
+      int pbits = kHBits;
+      int need = K - above;
+      while (pbits < 64 && above + count_at > kSortMax) {
+        const int nb = min(kHBits, 64 - pbits);
+        const int shift = 64 - pbits - nb;
+        for (int i = t; i < kNBins; i += B) hist[i] = 0u;
+        __syncthreads();
+        for (int id = t; id < V; id += B) {
+          const unsigned long long kv = key64(load_elem(zrow, id), (uint32_t)id);
+          if ((kv >> (64 - pbits)) == prefix)
+            atomicAdd(&hist[(int)((kv >> shift) & ((1ull << nb) - 1ull))], 1u);
+        }
+        __syncthreads();
+        int d = 0, ab = 0;
+        find_kth(need, d, ab);
+        count_at = (int)hist[d];
+        above += ab;
+        need -= ab;
+        prefix = (prefix << nb) | (unsigned long long)d;
+        pbits += nb;
+        __syncthreads();
+      }
+      for (int id = t; id < V; id += B) {
+        const unsigned long long kv = key64(load_elem(zrow, id), (uint32_t)id);
+        if ((kv >> (64 - pbits)) >= prefix) {
+          const unsigned int pos = atomicAdd(&sh_u[2], 1u);
+          if (pos < (unsigned)kSortMax) sarr[pos] = kv;
+        }
+      }
+      __syncthreads();
+      n_cand = (int)sh_u[2];
+    }
+    n_cand = min(n_cand, kSortMax);
+
+    // ------------------------------------------- bitonic sort, descending
+    int P2 = 1;
+    while (P2 < n_cand) P2 <<= 1;
+    for (int i = n_cand + t; i < P2; i += B) sarr[i] = 0ull;
+    __syncthreads();
+    for (int k2 = 2; k2 <= P2; k2 <<= 1) {
+      for (int j = k2 >> 1; j > 0; j >>= 1) {
+        for (int i = t; i < P2; i += B) {
+          const int ij = i ^ j;
+          if (ij > i) {
+            const unsigned long long x = sarr[i], y = sarr[ij];
+            if ((x < y) == ((i & k2) == 0)) { sarr[i] = y; sarr[ij] = x; }
+          }
+        }
+        __syncthreads();
+      }
+    }
+
+    // ------------------------------------------------------------- outputs
+    uint32_t flags = flags0;
+    int32_t a = -1;
+    if (P.sampled) {
+      a = P.sampled[row];
+      if (a < 0 || a >= V) flags |= SC_DEV_BAD_SAMPLED;
+    }
+    float za = 0.f;
+    if (a >= 0 && a < V) {
+      za = load_elem(zrow, a);
+      if (za == -INFINITY) flags |= SC_DEV_NONFINITE;
+    }
+    for (int k = t; k < K; k += B) {
+      int32_t id = -1;
+      float q = qnan;
+      if (!flags) {
+        const unsigned long long kv = sarr[k];
+        id = (int32_t)(~(uint32_t)(kv & 0xffffffffull));
+        const float z = okey_value((uint32_t)(kv >> 32));
+        q = exp2_fast((z - m) * c - log2s + 32.f) * 0x1p-32f;   // subnormal-exact
+      }
+      P.head_ids[row * K + k] = id;
+      P.head_probs[row * K + k] = q;
+    }
+    if (t == 0) {
+      if (P.sampled_logp)
+        P.sampled_logp[row] = (flags || a < 0) ? qnan : ((za - m) * c - log2s) * kLn2;
+      if (flags) sh_u[3] |= flags;
+    }
+  }
+  __syncthreads();
+  if (t == 0 && sh_u[3] && P.dev_status) atomicOr(P.dev_status, sh_u[3]);
+}
+
+}  // namespace
+
+int record_cap(int k) { return k <= 256 ? 256 : 512; }
+
+size_t record_lds_bytes(int k) {
+  return (size_t)kNBins * 4 + (size_t)kRNW * record_cap(k) * 8;
+}
+
+// Persistent grid: resident workgroups per CU from the occupancy query
+// (registers and LDS), times the CU count, at most one per row.
+hipError_t launch_record(RecParams P, int cus, hipStream_t s) {
+  P.cap = record_cap(P.k);
+  const size_t lds = record_lds_bytes(P.k);
+  auto go = [&](auto kern) -> hipError_t {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    int per_cu = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kRB, lds);
+    if (e != hipSuccess) return e;
+    const int64_t grid = std::min<int64_t>(P.n_rows, (int64_t)cus * std::max(1, per_cu));
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kRB), lds, s, P);
+    return hipGetLastError();
+  };
+  if (P.in_dtype == 1)
+    return P.vector ? go(k_record<uint16_t, true>) : go(k_record<uint16_t, false>);
+  return P.vector ? go(k_record<float, true>) : go(k_record<float, false>);
+}
+
+}  // namespace sc

@@ -51,6 +51,8 @@ _SIGS = {
     "sc_logprobs_lmhead": [_vp, _i64, _i32, _i64, _vp, _i64, _i64, _vp, _i32, _vp,
                            _vp, _f32, _vp, _vp, _vp, _vp, _i64, _vp, _vp],
     "sc_lmhead_logits": [_vp, _i64, _i32, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
+    "sc_record": [_vp, ctypes.c_int, _i64, _i64, _i64, _f32, _i32, _vp, _vp, _vp, _vp,
+                  _vp, _vp],
     "sc_status_string": [ctypes.c_int],
     "sc_version": [],
 }
@@ -318,3 +320,22 @@ def lmhead_logits(hidden, weight, out=None, stream=None):
     _check(lib().sc_lmhead_logits(_ptr(hidden), n, d, hs, _ptr(weight), V, ws,
                                   _ptr(out), out.stride(0), _stream(stream)))
     return out
+
+
+def record(logits, k, sampled=None, temperature=1.0, head_ids=None, head_probs=None,
+           sampled_logp=None, dev_status=None, stream=None):
+    """sc_record: top-k candidate ids and probabilities of the rollout softmax
+    per row (ties to the lower id), and the sampled token's log-probability."""
+    n, V, stride = _rows(logits)
+    if sampled is not None:
+        _need(sampled, torch.int32, "sampled")
+    dev = logits.device
+    head_ids = torch.empty(n, k, dtype=torch.int32, device=dev) if head_ids is None else head_ids
+    head_probs = torch.empty(n, k, dtype=torch.float32, device=dev) if head_probs is None else head_probs
+    if sampled is not None and sampled_logp is None:
+        sampled_logp = torch.empty(n, dtype=torch.float32, device=dev)
+    _check(lib().sc_record(_ptr(logits), _dtype_code(logits), n, V, stride,
+                           float(temperature), int(k), _ptr(sampled), _ptr(head_ids),
+                           _ptr(head_probs), _ptr(sampled_logp), _ptr(dev_status),
+                           _stream(stream)))
+    return dict(head_ids=head_ids, head_probs=head_probs, sampled_logp=sampled_logp)

@@ -206,3 +206,26 @@ def test_lmhead_logits_rejects_bad_arguments():
     assert f(NULL, 10, 256, 256, FAKE, 100, 256, FAKE, 100, NULL) == ARG
     assert f(FAKE, 10, 100, 256, FAKE, 100, 256, FAKE, 100, NULL) == UNSUP
     assert f(FAKE, 0, 256, 256, FAKE, 100, 256, FAKE, 100, NULL) == OK
+
+
+def record(**kw):
+    a = dict(z=FAKE, dtype=sc.SC_BF16, n=4, V=1000, stride=1000, T=1.0, k=10, a=FAKE,
+             ids=FAKE, probs=FAKE, lp=FAKE, dev=NULL, stream=NULL)
+    a.update(kw)
+    return sc.lib().sc_record(a["z"], a["dtype"], a["n"], a["V"], a["stride"], a["T"],
+                              a["k"], a["a"], a["ids"], a["probs"], a["lp"], a["dev"],
+                              a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(z=NULL), dict(ids=NULL), dict(probs=NULL), dict(dtype=3), dict(n=-1), dict(V=0),
+    dict(stride=999), dict(k=0), dict(k=1001), dict(k=1025, V=5000, stride=5000),
+    dict(T=0.0), dict(T=float("nan")), dict(a=NULL), dict(z=FAKE1), dict(ids=FAKE2),
+])
+def test_record_rejects_bad_arguments(kw):
+    assert record(**kw) == ARG
+
+
+def test_record_zero_rows_and_optional_sampled():
+    assert record(n=0) == OK
+    assert record(n=0, a=NULL, lp=NULL) == OK
