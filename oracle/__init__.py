@@ -7,5 +7,6 @@ from .sc_oracle import (BATCH_KEYS, CLAMP, DEV_BAD_ID, IS_MIS, IS_NONE, IS_TIS,
                         is_weight, DEV_BAD_RESP, DEV_BAD_SAMPLED,
                         DEV_DUP_ID, DEV_NONFINITE, MODE_CORRECTION,
                         MODE_DLOGITS, MODE_SCORE, batch_sums, bf16_rne,
-                        group_norm, lmhead_logits, masked_row, record_topk,
+                        group_norm, lmhead_backward, lmhead_logits, masked_row,
+                        record_topk,
                         sc_row, trainer_log_softmax)

@@ -391,3 +391,18 @@ def record_topk(z, temperature, k, sampled=None):
     return dict(flags=0, head_ids=order.astype(np.int64),
                 head_probs=np.exp(logp[order]),
                 sampled_logp=float(logp[int(sampled)]) if sampled is not None else float("nan"))
+
+
+def lmhead_backward(hidden, weight, dlogits):
+    """Gradients of the step loss through the LM head z = X W^T, in float64.
+
+    dlogits: (n, V) gradient of the step loss with respect to the logits (the
+    dLogits rows of sc_row, zero on padding rows).  By the chain rule through
+    z = X W^T: dHidden = dZ W (n, d) and dW = dZ^T X (V, d).
+    """
+    X = np.asarray(hidden, dtype=np.float64)
+    W = np.asarray(weight, dtype=np.float64)
+    G = np.asarray(dlogits, dtype=np.float64)
+    if G.shape != (X.shape[0], W.shape[0]) or X.shape[1] != W.shape[1]:
+        raise ValueError("shapes")
+    return G @ W, G.T @ X

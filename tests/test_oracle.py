@@ -654,3 +654,33 @@ def test_record_flags_and_masked_logits():
     r = O.record_topk(z, 1.0, 4, sampled=0)      # -inf entries fill the tail, p = 0
     np.testing.assert_array_equal(r["head_ids"], [2, 0, 1, 3])
     assert r["head_probs"][2] == 0.0 and r["head_probs"][3] == 0.0
+
+
+def test_lmhead_backward_equals_autograd_of_printed_loss_through_the_head():
+    # end to end: the printed token loss of every row, on logits X W^T, summed
+    # over rows with the global token mean; torch autograd gives dX and dW
+    rng = np.random.default_rng(51)
+    n, V, d, T = 6, 12, 5, 0.8
+    X = rng.normal(0, 1, (n, d))
+    W = rng.normal(0, 0.7, (V, d))
+    Xt = torch.tensor(X, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    z = Xt @ Wt.T / 1.0
+    rows, total = [], 0.0
+    cases = []
+    for i in range(n):
+        K = int(rng.integers(1, V))
+        ids = rng.choice(V, K, replace=False)
+        q = rng.dirichlet(np.ones(K)) * rng.uniform(0.3, 0.99)
+        a = int(rng.integers(V))
+        A = float(rng.normal())
+        cases.append((ids, q, a, A))
+        total = total + _printed_loss(z[i], T, torch.tensor(ids), torch.tensor(q), a, A, n)
+    total.backward()
+    zn = O.lmhead_logits(X, W)
+    G = np.stack([O.sc_row(zn[i], T, ids, q, a, advantage=A, n_valid=n)["row"]
+                  for i, (ids, q, a, A) in enumerate(cases)])
+    dX, dW = O.lmhead_backward(X, W, G)
+    np.testing.assert_allclose(dX, Xt.grad.numpy(), rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dW, Wt.grad.numpy(), rtol=1e-9, atol=1e-11)
+    assert dX.shape == (n, d) and dW.shape == (V, d)
