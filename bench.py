@@ -160,14 +160,47 @@ def lmhead_measure(dev, reps):
         raise RuntimeError(f"lmhead device status {int(status.item())}")
     ms = e0.elapsed_time(e1) / reps
     tflops = 2.0 * LM_D * VOCAB * LM_ROWS / (ms * 1e-3) / 1e12
-    del w, c, ws
+
+    # backward through the head: dLogits recomputed chunk by chunk (2,048
+    # rows), dHidden = dZ W and dW = dZ^T X; 3 x 2 d V flop per position
+    resp = torch.zeros(LM_ROWS, dtype=torch.int32, device=dev)
+    adv = torch.ones(1, device=dev)
+    n_valid = torch.tensor([LM_ROWS], dtype=torch.int64, device=dev)
+    sc.center(out, c["head_ids"], c["head_probs"], c["sampled"], resp, adv,
+              n_valid=n_valid, rollout_logp=c["rollout_logp"], vocab=VOCAB)
+    dh = torch.empty(LM_ROWS, LM_D, dtype=torch.bfloat16, device=dev)
+    dW = torch.empty(VOCAB, LM_D, device=dev)
+    bws = torch.empty(sc.lib().sc_lmhead_backward_workspace_size(2048, VOCAB),
+                      dtype=torch.uint8, device=dev)
+
+    def back():
+        sc.lmhead_backward(c["hidden"], w, out, c["head_ids"], c["head_probs"], c["sampled"],
+                           resp, adv, n_valid, d_hidden=dh, d_weight=dW, chunk_rows=2048,
+                           workspace=bws)
+    back()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        back()
+    e1.record()
+    torch.cuda.synchronize()
+    bms = e0.elapsed_time(e1) / reps
+    btflops = 3 * 2.0 * LM_D * VOCAB * LM_ROWS / (bms * 1e-3) / 1e12
+    del w, c, ws, dh, dW, bws
     torch.cuda.empty_cache()
     return {"workload": f"{LM_ROWS} rows x V={VOCAB} x d={LM_D}, bf16 hidden and "
                         "projection, K=128, logits never stored",
             "kernel_ms": round(ms, 3), "positions_per_s": round(LM_ROWS / (ms * 1e-3), 1),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+            "backward": {"ms": round(bms, 3),
+                         "positions_per_s": round(LM_ROWS / (bms * 1e-3), 1),
+                         "note": "dLogits recompute (this library's MFMA kernel) + "
+                                 "dHidden and dW GEMMs (hipBLASLt), 2,048-row chunks",
+                         "roofline": {"bound": "mfma", "achieved": round(btflops, 1),
+                                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                      "frac": round(btflops / MFMA_BF16_PEAK_TFLOPS, 4)}}}
 
 
 def main():

@@ -20,7 +20,8 @@
  * ---------------------------------------
  * - Pointers named as device pointers address GPU memory owned by the caller.
  *   The library allocates nothing and keeps no state besides a cached query of
- *   the device's compute-unit count.
+ *   the device's compute-unit count (and, once sc_lmhead_backward has run on a
+ *   device, that device's hipBLASLt handle).
  * - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
  *   stream) and never synchronises.  Calls are thread-safe.
  * - Argument errors are returned as a negative sc_status BEFORE any HIP call is
@@ -301,6 +302,58 @@ int sc_lmhead_logits(const void* hidden, int64_t n_rows, int32_t d,
                      int64_t hidden_stride, const void* weight, int64_t vocab,
                      int64_t weight_stride, float* logits, int64_t logits_stride,
                      void* stream);
+
+/*
+ * LM-head backward.
+ *
+ * The gradient of the SC step loss (Score Centering page, section "Score
+ * Centering": the token loss, reduced over all generated tokens of the step)
+ * with respect to the logits is dZ = -A wt / (T N_valid) g per row (the
+ * SC_ROW_DLOGITS row of sc_center); through the LM head z = X W^T it gives
+ * dHidden = dZ W and dW = dZ^T X.  The logits are recomputed from X and W
+ * with the matrix cores of sc_logprobs_lmhead, so the [n_rows, vocab] logits
+ * are never stored; the statistics come from sc_logprobs_lmhead followed by
+ * sc_center (same head_ids, head_probs, sampled, resp_idx, advantages,
+ * temperature, n_valid; centering as given to sc_center, the importance
+ * weight read from row_stats).
+ *
+ * sc_lmhead_dlogits writes the bf16 dLogits rows themselves (round to
+ * nearest even), dlogits_stride >= vocab, a multiple of 4, 8-byte aligned;
+ * padding rows are zero, rows with NaN statistics NaN.
+ *
+ * sc_lmhead_backward processes chunk_rows rows at a time: their bf16
+ * dLogits go to the workspace (sc_lmhead_backward_workspace_size(chunk_rows,
+ * vocab) bytes, 256-byte aligned, caller-owned), then two GEMMs with fp32
+ * accumulation (hipBLASLt; the first call on a device creates its handle,
+ * kept for the process):
+ *   d_hidden   [n_rows, dh_stride >= d], bf16 or fp32 (dh_dtype), written
+ *   d_weight   fp32 [vocab, dw_stride >= d]; written, or added to when
+ *              accumulate != 0 (e.g. over several calls of one step)
+ * The same argument rules as sc_logprobs_lmhead apply to hidden and weight.
+ */
+int sc_lmhead_dlogits(const void* hidden, int64_t n_rows, int32_t d,
+                      int64_t hidden_stride, const void* weight, int64_t vocab,
+                      int64_t weight_stride, const int32_t* head_ids,
+                      const float* head_probs, int32_t k, const int32_t* sampled,
+                      const int32_t* resp_idx, const float* advantages,
+                      int32_t n_responses, float temperature, const int64_t* n_valid,
+                      const float* row_stats, const int32_t* row_idx,
+                      const float* head_logp, int centering, void* dlogits,
+                      int64_t dlogits_stride, void* stream);
+
+int64_t sc_lmhead_backward_workspace_size(int64_t chunk_rows, int64_t vocab);
+
+int sc_lmhead_backward(const void* hidden, int64_t n_rows, int32_t d,
+                       int64_t hidden_stride, const void* weight, int64_t vocab,
+                       int64_t weight_stride, const int32_t* head_ids,
+                       const float* head_probs, int32_t k, const int32_t* sampled,
+                       const int32_t* resp_idx, const float* advantages,
+                       int32_t n_responses, float temperature, const int64_t* n_valid,
+                       const float* row_stats, const int32_t* row_idx,
+                       const float* head_logp, int centering, void* d_hidden,
+                       int dh_dtype, int64_t dh_stride, float* d_weight,
+                       int64_t dw_stride, int accumulate, int64_t chunk_rows,
+                       void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * sc_record -- the rollout engine's record of each generated position.

@@ -380,7 +380,7 @@ int sc_logprobs_lmhead(const void* hidden, int64_t n_rows, int32_t d, int64_t hi
   P.head_logp = head_logp;
   P.dev_status = dev_status;
   if (n_rows == 0) return SC_OK;
-  hipError_t e = sc::launch_lmhead(P, false, static_cast<hipStream_t>(stream));
+  hipError_t e = sc::launch_lmhead(P, 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SC_OK : SC_ERR_HIP;
 }
 
@@ -395,8 +395,142 @@ int sc_lmhead_logits(const void* hidden, int64_t n_rows, int32_t d, int64_t hidd
   P.os = logits_stride;
   P.c = 1.f;
   if (n_rows == 0) return SC_OK;
-  hipError_t e = sc::launch_lmhead(P, true, static_cast<hipStream_t>(stream));
+  hipError_t e = sc::launch_lmhead(P, 1, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SC_OK : SC_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// LM-head backward: dLogits recomputed from the forward statistics
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kGemmWorkspace = 32u << 20;   // hipBLASLt workspace
+
+int64_t dz_stride(int64_t vocab) { return (vocab + 7) / 8 * 8; }
+
+int check_lm_dz(sc::LmParams& P, const int32_t* head_ids, const float* head_probs, int32_t k,
+                const int32_t* sampled, const int32_t* resp_idx, const float* advantages,
+                int32_t n_responses, float temperature, const int64_t* n_valid,
+                const float* row_stats, const int32_t* row_idx, const float* head_logp,
+                int centering) {
+  if (k < 1 || k > kMaxK || (int64_t)k > P.vocab) return SC_ERR_ARG;
+  if (!(std::isfinite(temperature) && temperature > 0.f)) return SC_ERR_ARG;
+  if (!head_ids || !head_probs || !sampled || !advantages || !n_valid || !row_stats ||
+      !row_idx || !head_logp || n_responses < 0)
+    return SC_ERR_ARG;
+  if (!aligned(head_ids, 4) || !aligned(head_probs, 4) || !aligned(sampled, 4) ||
+      !aligned(advantages, 4) || !aligned(n_valid, 8) || !aligned(row_stats, 4) ||
+      !aligned(row_idx, 4) || !aligned(head_logp, 4) || (resp_idx && !aligned(resp_idx, 4)))
+    return SC_ERR_ARG;
+  P.c = (float)(1.4426950408889634 / (double)temperature);
+  P.temperature = temperature;
+  P.head_ids = head_ids;
+  P.head_probs = head_probs;
+  P.k = k;
+  P.sampled = sampled;
+  P.resp_idx = resp_idx;
+  P.advantages = advantages;
+  P.n_responses = n_responses;
+  P.n_valid = n_valid;
+  P.stats_in = row_stats;
+  P.idx_in = row_idx;
+  P.head_logp_in = head_logp;
+  P.centering = centering ? 1 : 0;
+  return SC_OK;
+}
+
+// Row slice [r0, r0 + rows) of a dLogits problem.
+sc::LmParams lm_slice(const sc::LmParams& P, int64_t r0, int64_t rows) {
+  sc::LmParams Q = P;
+  Q.x = P.x + r0 * P.xs;
+  Q.n_rows = rows;
+  Q.n_ptiles = (int)((rows + sc::kLmTileP - 1) / sc::kLmTileP);
+  Q.head_ids = P.head_ids + r0 * P.k;
+  Q.head_probs = P.head_probs + r0 * P.k;
+  Q.sampled = P.sampled + r0;
+  Q.resp_idx = P.resp_idx ? P.resp_idx + r0 : nullptr;
+  Q.stats_in = P.stats_in + r0 * SC_NSTATS;
+  Q.idx_in = P.idx_in + r0 * 2;
+  Q.head_logp_in = P.head_logp_in + r0 * P.k;
+  return Q;
+}
+
+}  // namespace
+
+int sc_lmhead_dlogits(const void* hidden, int64_t n_rows, int32_t d, int64_t hidden_stride,
+                      const void* weight, int64_t vocab, int64_t weight_stride,
+                      const int32_t* head_ids, const float* head_probs, int32_t k,
+                      const int32_t* sampled, const int32_t* resp_idx, const float* advantages,
+                      int32_t n_responses, float temperature, const int64_t* n_valid,
+                      const float* row_stats, const int32_t* row_idx, const float* head_logp,
+                      int centering, void* dlogits, int64_t dlogits_stride, void* stream) {
+  sc::LmParams P{};
+  int st = check_lm(P, hidden, n_rows, d, hidden_stride, weight, vocab, weight_stride);
+  if (st != SC_OK) return st;
+  st = check_lm_dz(P, head_ids, head_probs, k, sampled, resp_idx, advantages, n_responses,
+                   temperature, n_valid, row_stats, row_idx, head_logp, centering);
+  if (st != SC_OK) return st;
+  if (!dlogits || !aligned(dlogits, 8) || dlogits_stride < vocab || dlogits_stride % 4)
+    return SC_ERR_ARG;
+  P.dz = static_cast<uint16_t*>(dlogits);
+  P.dzs = dlogits_stride;
+  if (n_rows == 0) return SC_OK;
+  hipError_t e = sc::launch_lmhead(P, 2, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SC_OK : SC_ERR_HIP;
+}
+
+int64_t sc_lmhead_backward_workspace_size(int64_t chunk_rows, int64_t vocab) {
+  if (chunk_rows < 1 || chunk_rows > kMaxI32 || vocab < 1 || vocab > kMaxI32 - sc::kLmTileV)
+    return SC_ERR_ARG;
+  return (int64_t)(up256((size_t)chunk_rows * dz_stride(vocab) * 2) + kGemmWorkspace);
+}
+
+int sc_lmhead_backward(const void* hidden, int64_t n_rows, int32_t d, int64_t hidden_stride,
+                       const void* weight, int64_t vocab, int64_t weight_stride,
+                       const int32_t* head_ids, const float* head_probs, int32_t k,
+                       const int32_t* sampled, const int32_t* resp_idx, const float* advantages,
+                       int32_t n_responses, float temperature, const int64_t* n_valid,
+                       const float* row_stats, const int32_t* row_idx, const float* head_logp,
+                       int centering, void* d_hidden, int dh_dtype, int64_t dh_stride,
+                       float* d_weight, int64_t dw_stride, int accumulate, int64_t chunk_rows,
+                       void* workspace, int64_t workspace_bytes, void* stream) {
+  sc::LmParams P{};
+  int st = check_lm(P, hidden, n_rows, d, hidden_stride, weight, vocab, weight_stride);
+  if (st != SC_OK) return st;
+  st = check_lm_dz(P, head_ids, head_probs, k, sampled, resp_idx, advantages, n_responses,
+                   temperature, n_valid, row_stats, row_idx, head_logp, centering);
+  if (st != SC_OK) return st;
+  if (!d_hidden || !dtype_ok(dh_dtype) || dh_stride < d || !aligned(d_hidden, esize(dh_dtype)))
+    return SC_ERR_ARG;
+  if (!d_weight || dw_stride < d || !aligned(d_weight, 4)) return SC_ERR_ARG;
+  if (chunk_rows < 1 || chunk_rows > kMaxI32 || !workspace || !aligned(workspace, 256))
+    return SC_ERR_ARG;
+  const int64_t need = sc_lmhead_backward_workspace_size(chunk_rows, vocab);
+  if (workspace_bytes < need) return SC_ERR_ARG;
+  if (n_rows == 0) return SC_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t dzs = dz_stride(vocab);
+  char* ws = static_cast<char*>(workspace);
+  P.dz = reinterpret_cast<uint16_t*>(ws);
+  P.dzs = dzs;
+  void* gws = ws + up256((size_t)chunk_rows * dzs * 2);
+  for (int64_t r0 = 0; r0 < n_rows; r0 += chunk_rows) {
+    const int64_t rows = std::min<int64_t>(chunk_rows, n_rows - r0);
+    const sc::LmParams Q = lm_slice(P, r0, rows);
+    hipError_t e = sc::launch_lmhead(Q, 2, s);
+    if (e != hipSuccess) return SC_ERR_HIP;
+    // dHidden rows: column-major (d x rows) = W^T (d x V) . dZ^T (V x rows)
+    char* dh = static_cast<char*>(d_hidden) + r0 * dh_stride * (int64_t)esize(dh_dtype);
+    e = sc::gemm_bf16(false, false, d, rows, vocab, weight, weight_stride, P.dz, dzs, 0.f, dh,
+                      dh_dtype == SC_BF16, dh_stride, gws, kGemmWorkspace, s);
+    if (e != hipSuccess) return SC_ERR_HIP;
+    // dW: column-major (d x V) += X^T (d x rows) . dZ (rows x V)
+    const float beta = (accumulate || r0 > 0) ? 1.f : 0.f;
+    e = sc::gemm_bf16(false, true, d, vocab, rows, Q.x, hidden_stride, P.dz, dzs, beta,
+                      d_weight, 0, dw_stride, gws, kGemmWorkspace, s);
+    if (e != hipSuccess) return SC_ERR_HIP;
+  }
+  return SC_OK;
 }
 
 int sc_record(const void* logits, int logits_dtype, int64_t n_rows, int64_t vocab,

@@ -117,6 +117,18 @@ struct LmParams {
   float4* state;         // [splits, n_rows] (max, tail sum, entropy sum, argmax)
   float* za;             // [n_rows] logit of the sampled id
   float* head_raw;       // [n_rows, k] logits of the recorded ids
+  // dLogits recomputation (sc_lmhead_dlogits / sc_lmhead_backward)
+  const float* head_probs;
+  const float* advantages;
+  int32_t n_responses;
+  const int64_t* n_valid;
+  float temperature;
+  int centering;
+  const float* stats_in;     // row statistics from sc_logprobs_lmhead + sc_center
+  const int32_t* idx_in;     // row_idx (a_slot in column 1)
+  const float* head_logp_in;
+  uint16_t* dz;              // bf16 [n_rows, dzs]
+  int64_t dzs;
   // outputs
   float* out;            // logits check: fp32 [n_rows, os]
   int64_t os;
@@ -126,7 +138,15 @@ struct LmParams {
   uint32_t* dev_status;
 };
 
-hipError_t launch_lmhead(const LmParams& P, bool store_logits, hipStream_t s);
+// mode 0: statistics (stage, main, finalize); 1: fp32 logits; 2: bf16 dLogits
+// (main, then the recorded / sampled ids).
+hipError_t launch_lmhead(const LmParams& P, int mode, hipStream_t s);
+
+// Library GEMM (hipBLASLt): D (col-major m x n) = op(A) op(B) + beta D, bf16
+// operands, fp32 accumulation, D fp32 or bf16.
+hipError_t gemm_bf16(bool ta, bool tb, int64_t m, int64_t n, int64_t k, const void* A,
+                     int64_t lda, const void* B, int64_t ldb, float beta, void* D,
+                     int d_bf16, int64_t ldd, void* ws, size_t ws_bytes, hipStream_t s);
 
 // Rollout-side record (sc_record): top-k of the rollout softmax per row.
 struct RecParams {

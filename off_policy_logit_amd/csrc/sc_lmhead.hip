@@ -19,8 +19,11 @@
 //                  sum, argmax) and captures the logits at H and at a.
 //   k_lm_finalize  per row: merge the split states in a fixed order, add the
 //                  recorded ids, write the same statistics as sc_logprobs.
-// k_lm_main<true> instead stores the logit tile (a check of the GEMM with
-// the identical accumulation order).
+// k_lm_main<1> instead stores the logit tile (a check of the GEMM with the
+// identical accumulation order); k_lm_main<2> recomputes the logits and
+// writes the bf16 dLogits of the SC step loss, alpha p_v, for every id, and
+// k_lm_dz_fix then writes the recorded and sampled ids (the backward pass:
+// dLogits for a bounded chunk of rows, consumed by the dHidden and dW GEMMs).
 #include <hip/hip_runtime.h>
 #include <float.h>
 #include <stdint.h>
@@ -129,8 +132,26 @@ __global__ __launch_bounds__(256) void k_lm_stage(LmParams P) {
 // ---------------------------------------------------------------------------
 // Main: GEMM tile loop with the statistics (or store) epilogue.
 // ---------------------------------------------------------------------------
-template <bool STORE>
+// Per-row factors of the dLogits row (Score Centering loss, global token
+// mean): scale = -A wt / (T N_valid) and the off-head factor alpha =
+// -scale (rho + 1 - S) (centering) or -scale; zero for padding rows, NaN for
+// rows whose statistics are NaN or whose response index is out of range.
+SC_DEV void lm_row_factors(const LmParams& P, int64_t p, float& scale, float& alpha) {
+  const int resp = P.resp_idx ? P.resp_idx[p] : 0;
+  if (resp < 0) { scale = 0.f; alpha = 0.f; return; }
+  if (resp >= P.n_responses) { scale = alpha = __builtin_nanf(""); return; }
+  const float* st = P.stats_in + p * SC_NSTATS;
+  const double sc = -(double)P.advantages[resp] * (double)st[SC_STAT_WEIGHT] /
+                    ((double)P.temperature * (double)P.n_valid[0]);
+  const double al = P.centering ? -sc * ((double)st[SC_STAT_RHO] + 1.0 - (double)st[SC_STAT_S])
+                                : -sc;
+  scale = (float)sc;
+  alpha = (float)al;
+}
+
+template <int MODE>
 __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
+  constexpr bool STORE = MODE != 0;
   extern __shared__ __align__(16) unsigned char lds[];
   const int t = threadIdx.x, l = t & 63, w = t >> 6;
   const int wv = w & 1, wp = w >> 1;   // wave's vocabulary half, row quarter
@@ -241,6 +262,22 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
   int cur = 0, cnt = 0, nid = kNoIdx;
   float sm[NJ], ss[NJ], sh[NJ];
   int sam[NJ], sa_l[NJ];
+  // dLogits mode: value = sign(alpha) 2^(z c + off) 2^-32 with
+  // off = log2|alpha| - lse log2(e) + 32 (subnormal results stay exact)
+  float dz_off[NJ];
+  bool dz_neg[NJ];
+  if (MODE == 2) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t p = p0 + wp * kWR + j * 32 + lc;
+      float sc = 0.f, al = 0.f;
+      if (p < P.n_rows) lm_row_factors(P, p, sc, al);
+      const float lse = p < P.n_rows ? P.stats_in[p * SC_NSTATS + SC_STAT_LSE] : 0.f;
+      dz_off[j] = log2f(fabsf(al)) - lse * kLog2e + 32.f;
+      dz_off[j] = (al != al) ? al : dz_off[j];
+      dz_neg[j] = al < 0.f;
+    }
+  }
   if (!STORE) {
     cnt = (t < kTP && my_p < P.n_rows) ? P.scount[my_p] : 0;
     // first recorded id at or after this split's first vocabulary id
@@ -276,6 +313,38 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
 
   auto epilogue = [&](int ck) {
     const int v0 = ck * kTV;
+    if (MODE == 2) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int64_t p = p0 + wp * kWR + j * 32 + lc;
+        if (p >= P.n_rows) continue;
+        uint16_t* orow = P.dz + p * P.dzs;
+#pragma unroll
+        for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            // rows 8 g4 + 4 h + (0..3) of the block: four consecutive ids
+            const int v = v0 + wv * 128 + bi * 32 + 8 * g4 + 4 * h;
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float y = exp2_fast(fmaf(acc[bi][j][4 * g4 + e], c, dz_off[j])) * 0x1p-32f;
+              x[e] = dz_neg[j] ? -y : y;
+            }
+            if (v + 3 < V) {
+              u32x2 wv2;
+              wv2[0] = pack_bf16x2(x[0], x[1]);
+              wv2[1] = pack_bf16x2(x[2], x[3]);
+              *reinterpret_cast<u32x2*>(orow + v) = wv2;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (v + e < V) orow[v + e] = (uint16_t)f32_to_bf16(x[e]);
+            }
+          }
+      }
+      return;
+    }
     if (STORE) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
@@ -527,30 +596,74 @@ __global__ __launch_bounds__(256) void k_lm_finalize(LmParams P) {
   if (t == 0 && sh_status && P.dev_status) atomicOr(P.dev_status, sh_status);
 }
 
+// ---------------------------------------------------------------------------
+// dLogits at the recorded ids and at the sampled id (one wave per row), after
+// k_lm_main<2> wrote alpha p_v everywhere: slot k gets
+// scale ([k = a_slot] - q_k - (1 - S) p_k) (centering) or scale ([..] - p_k);
+// a sampled id outside the recorded set gets alpha p_a + scale.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_lm_dz_fix(LmParams P) {
+  const int t = threadIdx.x, l = t & 63;
+  const int64_t p = (int64_t)blockIdx.x * 4 + (t >> 6);
+  if (p >= P.n_rows) return;
+  const int resp = P.resp_idx ? P.resp_idx[p] : 0;
+  if (resp < 0) return;
+  float scf = 0.f, alf = 0.f;
+  lm_row_factors(P, p, scf, alf);
+  const double scale = scf, alpha = alf;
+  const float* st = P.stats_in + p * SC_NSTATS;
+  const double oms = 1.0 - (double)st[SC_STAT_S];
+  const int K = P.k;
+  const int a_slot = P.idx_in[p * 2 + 1];
+  uint16_t* orow = P.dz + p * P.dzs;
+  for (int k = l; k < K; k += kWave) {
+    const int32_t id = P.head_ids[p * K + k];
+    if (id < 0 || id >= P.vocab) continue;
+    const double pk = exp((double)P.head_logp_in[p * K + k]);
+    const double ind = k == a_slot ? 1.0 : 0.0;
+    const double v = P.centering ? scale * (ind - (double)P.head_probs[p * K + k] - oms * pk)
+                                 : scale * (ind - pk);
+    orow[id] = (uint16_t)f32_to_bf16((float)v);
+  }
+  if (l == 0 && a_slot < 0) {
+    const int32_t a = P.sampled[p];
+    if (a >= 0 && a < P.vocab) {
+      const double pa = exp((double)st[SC_STAT_LOGP_A]);
+      orow[a] = (uint16_t)f32_to_bf16((float)(alpha * pa + scale));
+    }
+  }
+}
+
+template <int MODE>
+hipError_t set_lds_attr() {
+  static bool done = false;
+  if (done) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lm_main<MODE>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  if (e == hipSuccess) done = true;
+  return e;
+}
+
 }  // namespace
 
-hipError_t launch_lmhead(const LmParams& P, bool store_logits, hipStream_t s) {
-  static bool attr_done[2] = {false, false};
+hipError_t launch_lmhead(const LmParams& P, int mode, hipStream_t s) {
   const int per_round = 8 * P.lm_pt;                  // row tiles per group round
   const int grid = ((P.n_ptiles + per_round - 1) / per_round) * 8 * P.lm_pt * P.splits;
-  if (store_logits) {
-    if (!attr_done[1]) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lm_main<true>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-      if (e != hipSuccess) return e;
-      attr_done[1] = true;
-    }
-    hipLaunchKernelGGL(k_lm_main<true>, dim3(grid), dim3(kB), kLds, s, P);
+  hipError_t e = hipSuccess;
+  if (mode == 1) {
+    if ((e = set_lds_attr<1>()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_lm_main<1>, dim3(grid), dim3(kB), kLds, s, P);
     return hipGetLastError();
   }
-  if (!attr_done[0]) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lm_main<false>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    if (e != hipSuccess) return e;
-    attr_done[0] = true;
+  if (mode == 2) {
+    if ((e = set_lds_attr<2>()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_lm_main<2>, dim3(grid), dim3(kB), kLds, s, P);
+    hipLaunchKernelGGL(k_lm_dz_fix, dim3((unsigned)((P.n_rows + 3) / 4)), dim3(256), 0, s, P);
+    return hipGetLastError();
   }
+  if ((e = set_lds_attr<0>()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_lm_stage, dim3((unsigned)P.n_rows), dim3(256), 0, s, P);
-  hipLaunchKernelGGL(k_lm_main<false>, dim3(grid), dim3(kB), kLds, s, P);
+  hipLaunchKernelGGL(k_lm_main<0>, dim3(grid), dim3(kB), kLds, s, P);
   hipLaunchKernelGGL(k_lm_finalize, dim3((unsigned)((P.n_rows + 3) / 4)), dim3(256), 0, s, P);
   return hipGetLastError();
 }

@@ -53,6 +53,12 @@ _SIGS = {
     "sc_lmhead_logits": [_vp, _i64, _i32, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
     "sc_record": [_vp, ctypes.c_int, _i64, _i64, _i64, _f32, _i32, _vp, _vp, _vp, _vp,
                   _vp, _vp],
+    "sc_lmhead_dlogits": [_vp, _i64, _i32, _i64, _vp, _i64, _i64, _vp, _vp, _i32, _vp, _vp,
+                          _vp, _i32, _f32, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _i64, _vp],
+    "sc_lmhead_backward_workspace_size": [_i64, _i64],
+    "sc_lmhead_backward": [_vp, _i64, _i32, _i64, _vp, _i64, _i64, _vp, _vp, _i32, _vp, _vp,
+                           _vp, _i32, _f32, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
+                           ctypes.c_int, _i64, _vp, _i64, ctypes.c_int, _i64, _vp, _i64, _vp],
     "sc_status_string": [ctypes.c_int],
     "sc_version": [],
 }
@@ -77,7 +83,9 @@ def lib():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = {"sc_status_string": ctypes.c_char_p,
-                          "sc_lmhead_workspace_size": ctypes.c_int64}.get(name, ctypes.c_int)
+                          "sc_lmhead_workspace_size": ctypes.c_int64,
+                          "sc_lmhead_backward_workspace_size": ctypes.c_int64,
+                          }.get(name, ctypes.c_int)
         _lib = L
     return _lib
 
@@ -339,3 +347,64 @@ def record(logits, k, sampled=None, temperature=1.0, head_ids=None, head_probs=N
                            _ptr(head_probs), _ptr(sampled_logp), _ptr(dev_status),
                            _stream(stream)))
     return dict(head_ids=head_ids, head_probs=head_probs, sampled_logp=sampled_logp)
+
+
+def _lm_dz_args(hidden, weight, stats, head_ids, head_probs, sampled, resp_idx,
+                advantages, temperature, n_valid, centering):
+    n, d, hs = _bf16_matrix(hidden, "hidden")
+    V, dw, ws = _bf16_matrix(weight, "weight")
+    if dw != d:
+        raise ValueError("hidden and weight disagree on d")
+    for t, dt, name in ((head_ids, torch.int32, "head_ids"),
+                        (head_probs, torch.float32, "head_probs"),
+                        (sampled, torch.int32, "sampled"),
+                        (advantages, torch.float32, "advantages")):
+        _need(t, dt, name)
+    if resp_idx is not None:
+        _need(resp_idx, torch.int32, "resp_idx")
+    k = head_ids.shape[1]
+    return [_ptr(hidden), n, d, hs, _ptr(weight), V, ws, _ptr(head_ids), _ptr(head_probs), k,
+            _ptr(sampled), _ptr(resp_idx), _ptr(advantages), advantages.shape[0],
+            float(temperature), _ptr(n_valid), _ptr(stats["row_stats"]),
+            _ptr(stats["row_idx"]), _ptr(stats["head_logp"]), int(bool(centering))]
+
+
+def lmhead_dlogits(hidden, weight, stats, head_ids, head_probs, sampled, resp_idx,
+                   advantages, n_valid, temperature=1.0, centering=True, out=None,
+                   stream=None):
+    """sc_lmhead_dlogits: bf16 dLogits rows recomputed from hidden and weight;
+    stats is the dict filled by logprobs_lmhead() then center()."""
+    args = _lm_dz_args(hidden, weight, stats, head_ids, head_probs, sampled, resp_idx,
+                       advantages, temperature, n_valid, centering)
+    n, V = hidden.shape[0], weight.shape[0]
+    if out is None:
+        out = torch.empty(n, (V + 7) // 8 * 8, dtype=torch.bfloat16, device=hidden.device)[:, :V]
+    _check(lib().sc_lmhead_dlogits(*args, _ptr(out), out.stride(0), _stream(stream)))
+    return out
+
+
+def lmhead_backward(hidden, weight, stats, head_ids, head_probs, sampled, resp_idx,
+                    advantages, n_valid, temperature=1.0, centering=True, d_hidden=None,
+                    d_weight=None, accumulate=False, chunk_rows=2048, workspace=None,
+                    stream=None):
+    """sc_lmhead_backward: (d_hidden, d_weight) of the step loss through the
+    LM head, chunk_rows rows of dLogits at a time."""
+    args = _lm_dz_args(hidden, weight, stats, head_ids, head_probs, sampled, resp_idx,
+                       advantages, temperature, n_valid, centering)
+    n, d = hidden.shape
+    V = weight.shape[0]
+    dev = hidden.device
+    if d_hidden is None:
+        d_hidden = torch.empty(n, d, dtype=torch.float32, device=dev)
+    if d_weight is None:
+        d_weight = torch.zeros(V, d, dtype=torch.float32, device=dev)
+    need = lib().sc_lmhead_backward_workspace_size(int(chunk_rows), V)
+    if need < 0:
+        _check(need)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(lib().sc_lmhead_backward(
+        *args, _ptr(d_hidden), _dtype_code(d_hidden), d_hidden.stride(0), _ptr(d_weight),
+        d_weight.stride(0), int(bool(accumulate)), int(chunk_rows), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
+    return d_hidden, d_weight
