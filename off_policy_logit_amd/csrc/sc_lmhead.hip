@@ -41,8 +41,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kTV = kLmTileV;           // vocabulary ids per chunk (MFMA M)
 constexpr int kTP = kLmTileP;           // rows per tile (MFMA N)
 constexpr int kKB = kLmKStage;          // k per stage
-constexpr int kB = 512;                 // threads: 8 waves, 2 (vocab) x 4 (rows)
-constexpr int kWR = 64;                 // rows per wave (2 MFMA column blocks)
+#ifndef SC_LM_WAVE_ROWS
+#define SC_LM_WAVE_ROWS 64
+#endif
+constexpr int kWR = SC_LM_WAVE_ROWS;    // rows per wave (kWR / 32 MFMA column blocks)
+constexpr int kB = 2 * (kLmTileP / kWR) * 64;   // threads: 2 (vocab halves) x kTP / kWR waves
 constexpr int kPitch = kKB * 2 + 16;    // LDS bytes per tile row (bank rotation)
 constexpr int kBuf = kTV * kPitch;      // one operand buffer
 constexpr int kOffBm = 4 * kBuf;        // [kTP][8] hit words of the chunk
@@ -183,12 +186,13 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
   // operand per stage.  Rows past the end read row 0 of the tile (valid
   // memory); their results are masked or never written.
   constexpr int kLJ = kTV * kKB * 2 / 16 / kB;  // 16-byte loads per operand
+  constexpr int kRS = kB / 8;                    // rows covered by one load round
   const int lrow = t >> 3, lcol = t & 7;
   const char* xb = reinterpret_cast<const char*>(P.x) + p0 * P.xs * 2;
   uint32_t xoff[kLJ];
 #pragma unroll
   for (int j = 0; j < kLJ; ++j) {
-    const int r = lrow + 64 * j;
+    const int r = lrow + kRS * j;
     xoff[j] = (uint32_t)(((p0 + r < P.n_rows) ? r : 0) * P.xs * 2 + lcol * 16);
   }
   uint32_t woff[kLJ];
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
     wb = reinterpret_cast<const char*>(P.w) + v0 * P.ws * 2;
 #pragma unroll
     for (int j = 0; j < kLJ; ++j) {
-      const int r = lrow + 64 * j;
+      const int r = lrow + kRS * j;
       woff[j] = (uint32_t)(((v0 + r < V) ? r : 0) * P.ws * 2 + lcol * 16);
     }
   };
@@ -220,7 +224,7 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
     unsigned char* Bm = A + kBuf;
 #pragma unroll
     for (int j = 0; j < kLJ; ++j) {
-      const int o = (lrow + 64 * j) * kPitch + lcol * 16;
+      const int o = (lrow + kRS * j) * kPitch + lcol * 16;
       *reinterpret_cast<u32x4*>(A + o) = ra[j];
       *reinterpret_cast<u32x4*>(Bm + o) = rb[j];
     }

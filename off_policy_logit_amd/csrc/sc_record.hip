@@ -48,6 +48,7 @@ constexpr int kHBits = 12;               // histogram bits of the key
 constexpr int kNBins = 1 << kHBits;
 constexpr int kSortMax = 2048;           // sort array (overlays the histogram)
 constexpr int kRU = SC_RECORD_TILE;      // vectors per thread per iteration
+constexpr int kRankMax = 64;             // candidate sets ordered by rank (O(n^2))
 static_assert(kSortMax * 8 == kNBins * 4, "sort array overlays the histogram");
 
 // Monotone unsigned key of a float (NaN excluded by the caller); -0 -> +0.
@@ -98,6 +99,7 @@ __global__ __launch_bounds__(kRB) void k_record(RecParams P) {
   __shared__ int redi[kRNW];
   // 0: flags, 1: overflow, 2: sort count, 3: status, 4: highest counted bin
   __shared__ unsigned int sh_u[5];
+  __shared__ unsigned int wcnt[kRNW];   // keys appended to each wave's buffer
   __shared__ int sh_i[2];               // bin and count above it, from find_kth
 
   const float qnan = __builtin_nanf("");
@@ -108,6 +110,7 @@ __global__ __launch_bounds__(kRB) void k_record(RecParams P) {
     __syncthreads();                     // previous row's LDS reads are done
     for (int i = t; i < kNBins; i += B) hist[i] = 0u;
     if (t == 0) { sh_u[0] = 0u; sh_u[1] = 0u; sh_u[2] = 0u; sh_u[4] = 0u; }
+    if (t < kRNW) wcnt[t] = 0u;
     __syncthreads();
 
     // ------------------------------------------------ exact bin of the k-th key
@@ -148,14 +151,13 @@ __global__ __launch_bounds__(kRB) void k_record(RecParams P) {
     float m_t = -FLT_MAX, s_t = 0.f;
     int b_w = 0;            // wave-uniform lower bound on the k-th key's bin
     float thr = -INFINITY;  // bin_floor(b_w)
-    int cnt = 0;            // wave-uniform number of buffered keys
-    bool ovf = false;       // wave-uniform: this wave's buffer overflowed
 
     // Raise b_w from the histogram (bins from the highest counted one down
     // to b_w) and drop buffered keys below it.  Wave-local; counts that other
     // waves are still adding only make the bound lower (still valid).
     auto refresh = [&]() {
-      if (ovf) return;
+      const int cnt = (int)__atomic_load_n(&wcnt[w], __ATOMIC_RELAXED);
+      if (cnt > cap) return;                     // overflowed: the row takes the fallback
       int total = 0, found = -1;
       // start at the highest bin any wave has reported (this wave's max
       // included); missing a higher count only lowers the bound
@@ -187,26 +189,20 @@ __global__ __launch_bounds__(kRB) void k_record(RecParams P) {
           if (keep) buf[kept + lane_rank(bal)] = kv;
           kept += __builtin_popcountll(bal);
         }
-        cnt = kept;
+        if (lane == 0) wcnt[w] = (unsigned)kept;
       }
     };
 
-    // One element per lane (`real` false for padding).  All lanes of the wave
-    // call it together.
-    auto consider = [&](float x, int id, bool real) {
-      if (!__ballot(real && x >= thr)) return;
-      if (cnt > cap - kWave) refresh();
+    // A candidate (x >= thr, so its bin is >= b_w): counted in the histogram
+    // and appended to the wave's buffer by its own lane, with LDS atomics; no
+    // other lane takes part, so rare candidates cost little.  Past the
+    // buffer's capacity the count still grows (the row then takes the exact
+    // fallback) and the histogram stays exact.
+    auto push = [&](float x, int id) {
       const uint32_t kx = okey(x);
-      const bool counted = real && bin_of(kx) >= b_w;
-      if (counted) atomicAdd(&hist[bin_of(kx)], 1u);
-      const bool cand = counted && !ovf;
-      const unsigned long long bal = __ballot(cand);
-      if (bal) {
-        const int pos = cnt + lane_rank(bal);
-        if (cand && pos < cap) buf[pos] = key64(x, (uint32_t)id);
-        cnt += __builtin_popcountll(bal);
-        if (cnt > cap) ovf = true;
-      }
+      atomicAdd(&hist[bin_of(kx)], 1u);
+      const unsigned pos = atomicAdd(&wcnt[w], 1u);
+      if (pos < (unsigned)cap) buf[pos] = key64(x, (uint32_t)id);
     };
 
     // Online max / sum and the candidate filter for one vector per lane.
@@ -219,23 +215,34 @@ __global__ __launch_bounds__(kRB) void k_record(RecParams P) {
       m_t = mn;
 #pragma unroll
       for (int i = 0; i < N; ++i) s_t += exp2_fast((v[i] - m_t) * c);
-      const bool any = active && vm >= thr;
-      if (__ballot(any)) {
+      if (active && vm >= thr) {
 #pragma unroll
-        for (int i = 0; i < N; ++i) consider(v[i], j * N + i, active);
+        for (int i = 0; i < N; ++i)
+          if (v[i] >= thr) push(v[i], j * N + i);
       }
     };
 
     // Uniform trip count for every thread: tiles of kRU vectors per thread.
+    // The next tile is loaded before the current one is processed, so every
+    // wave keeps a tile of loads in flight while it computes.
     int iter = 0;
-    for (int j0 = 0; j0 < n_full; j0 += B * kRU, ++iter) {
-      if (iter > 0 && (iter < 4 || (iter & (iter + 1)) == 0)) refresh();  // tiles 1-3, 7, 15, ...
-      Raw r[kRU];
+    Raw nx[kRU];
+    auto load_tile = [&](Raw (&r)[kRU], int j0) {
 #pragma unroll
       for (int u = 0; u < kRU; ++u) {
         const int j = j0 + u * B + t;
-        r[u] = j < n_full ? IO::template load<false>(zrow, j) : IO::ninf();
+        r[u] = j < n_full ? IO::template load<true>(zrow, j) : IO::ninf();   // streamed once
       }
+    };
+    if (n_full > 0) load_tile(nx, 0);
+    for (int j0 = 0; j0 < n_full; j0 += B * kRU, ++iter) {
+      Raw r[kRU];
+#pragma unroll
+      for (int u = 0; u < kRU; ++u) r[u] = nx[u];
+      if (j0 + B * kRU < n_full) load_tile(nx, j0 + B * kRU);
+      if (iter > 0 && (iter < 4 || (iter & (iter + 1)) == 0 ||
+                       (int)__atomic_load_n(&wcnt[w], __ATOMIC_RELAXED) > cap / 2))
+        refresh();                             // tiles 1-3, 7, 15, ... or a filling buffer
       if (iter == 0 && K <= B) {
         // Initial bound: the k-th largest of the B per-thread maxima of this
         // tile is at most the row's k-th largest logit (they are k distinct
@@ -285,10 +292,14 @@ __global__ __launch_bounds__(kRB) void k_record(RecParams P) {
 #pragma unroll
         for (int i = 0; i < N; ++i) s_t += exp2_fast((v[i] - m_t) * c);
       }
+      if (mine && vm >= thr) {
 #pragma unroll
-      for (int i = 0; i < N; ++i) consider(v[i], n_full * N + i, mine && i < rem);
+        for (int i = 0; i < N; ++i)
+          if (i < rem && v[i] >= thr) push(v[i], n_full * N + i);
+      }
     }
-    if (ovf && lane == 0) atomicOr(&sh_u[1], 1u);
+    __syncthreads();                           // every push is done
+    if (lane == 0 && wcnt[w] > (unsigned)cap) atomicOr(&sh_u[1], 1u);
 
     // row max and sum
     float mv = m_t;
@@ -316,7 +327,7 @@ __global__ __launch_bounds__(kRB) void k_record(RecParams P) {
     if (flags0) {
       n_cand = 0;
     } else if (fast) {
-      const int nb = min(cnt, cap);
+      const int nb = min((int)wcnt[w], cap);
       for (int i = lane; i < nb; i += kWave) {
         const unsigned long long kv = buf[i];
         if (bin_of((uint32_t)(kv >> 32)) >= bstar) {
@@ -364,9 +375,23 @@ __global__ __launch_bounds__(kRB) void k_record(RecParams P) {
     }
     n_cand = min(n_cand, kSortMax);
 
-    // ------------------------------------------- bitonic sort, descending
+    // -------------------------------------------- order the candidates
+    // Small sets: each key's rank is the number of larger keys (all keys are
+    // distinct); the first k go to `ord` (the wave buffers, free now).
+    // Larger sets: bitonic sort of sarr in place.
+    unsigned long long* ord = reinterpret_cast<unsigned long long*>(lds + kNBins * 4);
+    const bool by_rank = n_cand <= kRankMax;
+    if (by_rank) {
+      for (int i = t; i < n_cand; i += B) {
+        const unsigned long long ki = sarr[i];
+        int rank = 0;
+        for (int j2 = 0; j2 < n_cand; ++j2) rank += sarr[j2] > ki ? 1 : 0;
+        if (rank < K) ord[rank] = ki;
+      }
+      __syncthreads();
+    }
     int P2 = 1;
-    while (P2 < n_cand) P2 <<= 1;
+    while (!by_rank && P2 < n_cand) P2 <<= 1;
     for (int i = n_cand + t; i < P2; i += B) sarr[i] = 0ull;
     __syncthreads();
     for (int k2 = 2; k2 <= P2; k2 <<= 1) {
@@ -398,7 +423,7 @@ __global__ __launch_bounds__(kRB) void k_record(RecParams P) {
       int32_t id = -1;
       float q = qnan;
       if (!flags) {
-        const unsigned long long kv = sarr[k];
+        const unsigned long long kv = by_rank ? ord[k] : sarr[k];
         id = (int32_t)(~(uint32_t)(kv & 0xffffffffull));
         const float z = okey_value((uint32_t)(kv >> 32));
         q = exp2_fast((z - m) * c - log2s + 32.f) * 0x1p-32f;   // subnormal-exact
@@ -418,7 +443,8 @@ __global__ __launch_bounds__(kRB) void k_record(RecParams P) {
 
 }  // namespace
 
-int record_cap(int k) { return k <= 256 ? 256 : 512; }
+// Per-wave buffer: room for the rank output (k keys over all waves) too.
+int record_cap(int k) { return k <= 256 ? 512 : 1024; }
 
 size_t record_lds_bytes(int k) {
   return (size_t)kNBins * 4 + (size_t)kRNW * record_cap(k) * 8;
