@@ -20,8 +20,7 @@
  * ---------------------------------------
  * - Pointers named as device pointers address GPU memory owned by the caller.
  *   The library allocates nothing and keeps no state besides a cached query of
- *   the device's compute-unit count (and, once sc_lmhead_backward has run on a
- *   device, that device's hipBLASLt handle).
+ *   the device's compute-unit count.
  * - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
  *   stream) and never synchronises.  Calls are thread-safe.
  * - Argument errors are returned as a negative sc_status BEFORE any HIP call is
@@ -323,9 +322,11 @@ int sc_lmhead_logits(const void* hidden, int64_t n_rows, int32_t d,
  *
  * sc_lmhead_backward processes chunk_rows rows at a time: their bf16
  * dLogits go to the workspace (sc_lmhead_backward_workspace_size(chunk_rows,
- * vocab) bytes, 256-byte aligned, caller-owned), then two GEMMs with fp32
- * accumulation (hipBLASLt; the first call on a device creates its handle,
- * kept for the process):
+ * vocab, d) bytes, 256-byte aligned, caller-owned; it also holds W^T and the
+ * chunk's transposed dLogits and hidden states), then the two products run
+ * on the same bf16 matrix-core loop as the forward, fp32 accumulation (the
+ * dHidden product has one 256-row tile per 256 rows of the chunk and d / 256
+ * vocabulary-side tiles, so chunks of >= 8,192 rows fill the GPU):
  *   d_hidden   [n_rows, dh_stride >= d], bf16 or fp32 (dh_dtype), written
  *   d_weight   fp32 [vocab, dw_stride >= d]; written, or added to when
  *              accumulate != 0 (e.g. over several calls of one step)
@@ -341,7 +342,7 @@ int sc_lmhead_dlogits(const void* hidden, int64_t n_rows, int32_t d,
                       const float* head_logp, int centering, void* dlogits,
                       int64_t dlogits_stride, void* stream);
 
-int64_t sc_lmhead_backward_workspace_size(int64_t chunk_rows, int64_t vocab);
+int64_t sc_lmhead_backward_workspace_size(int64_t chunk_rows, int64_t vocab, int32_t d);
 
 int sc_lmhead_backward(const void* hidden, int64_t n_rows, int32_t d,
                        int64_t hidden_stride, const void* weight, int64_t vocab,

@@ -13,8 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = [os.path.join(CSRC, "sc_api.cpp"), os.path.join(CSRC, "sc_kernels.hip"),
-           os.path.join(CSRC, "sc_lmhead.hip"), os.path.join(CSRC, "sc_record.hip"),
-           os.path.join(CSRC, "sc_gemm.cpp")]
+           os.path.join(CSRC, "sc_lmhead.hip"), os.path.join(CSRC, "sc_record.hip")]
 LIB = os.path.join(HERE, "libsc.so")
 ARCH = "gfx950"
 
@@ -33,7 +32,7 @@ def build(verbose=False):
     """Compile libsc.so; raises CalledProcessError with the compiler output."""
     fd, tmp = tempfile.mkstemp(prefix="libsc.", suffix=".so.tmp", dir=HERE)
     os.close(fd)
-    cmd = [hipcc(), *FLAGS, "-o", tmp, *SOURCES, "-lhipblaslt"]
+    cmd = [hipcc(), *FLAGS, "-o", tmp, *SOURCES]
     try:
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:

@@ -393,6 +393,7 @@ int sc_lmhead_logits(const void* hidden, int64_t n_rows, int32_t d, int64_t hidd
   if (!logits || !aligned(logits, 4) || logits_stride < vocab) return SC_ERR_ARG;
   P.out = logits;
   P.os = logits_stride;
+  P.out_vec = (logits_stride % 4 == 0) && aligned(logits, 16);
   P.c = 1.f;
   if (n_rows == 0) return SC_OK;
   hipError_t e = sc::launch_lmhead(P, 1, static_cast<hipStream_t>(stream));
@@ -404,9 +405,55 @@ int sc_lmhead_logits(const void* hidden, int64_t n_rows, int32_t d, int64_t hidd
 // ---------------------------------------------------------------------------
 namespace {
 
-constexpr size_t kGemmWorkspace = 32u << 20;   // hipBLASLt workspace
+int64_t pad64(int64_t x) { return (x + 63) / 64 * 64; }
 
-int64_t dz_stride(int64_t vocab) { return (vocab + 7) / 8 * 8; }
+// Backward workspace: W^T [d, Vp], the chunk's dLogits [chunk, Vp] and their
+// transpose [V, chunk_p], the chunk's hidden states transposed [d, chunk_p]
+// (Vp, chunk_p: multiples of 64, zero padded, so every GEMM's k extent is a
+// whole number of 64-wide stages).
+struct BwdLayout {
+  int64_t vp, cp;
+  size_t wt, dz, dzt, xt, total;
+};
+BwdLayout bwd_layout(int64_t chunk, int64_t vocab, int64_t d) {
+  BwdLayout L{};
+  L.vp = pad64(vocab);
+  L.cp = pad64(chunk);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += up256(bytes); return o; };
+  L.wt = take((size_t)d * L.vp * 2);
+  L.dz = take((size_t)chunk * L.vp * 2);
+  L.dzt = take((size_t)vocab * L.cp * 2);
+  L.xt = take((size_t)d * L.cp * 2);
+  L.total = off;
+  return L;
+}
+
+// C [n, os] = A [m, k] B [n, k]^T through the LM-head MFMA loop (A is its
+// vocabulary operand, B its row operand); k a multiple of 64.
+hipError_t gemm_nt(const uint16_t* A, int64_t m, int64_t as, const uint16_t* B, int64_t n,
+                   int64_t bs, int64_t k, float* out, uint16_t* out16, int64_t os, int accum,
+                   hipStream_t s) {
+  sc::LmParams G{};
+  G.x = B;
+  G.xs = bs;
+  G.w = A;
+  G.ws = as;
+  G.n_rows = n;
+  G.vocab = m;
+  G.d = (int)k;
+  G.splits = lm_splits(m);
+  G.n_chunks = (int)((m + sc::kLmTileV - 1) / sc::kLmTileV);
+  G.n_ptiles = (int)((n + sc::kLmTileP - 1) / sc::kLmTileP);
+  G.lm_sp = G.splits % 8 == 0 ? 8 : G.splits;
+  G.lm_pt = std::max(1, 32 / G.lm_sp);
+  G.out = out;
+  G.out16 = out16;
+  G.os = os;
+  G.out_accum = accum;
+  G.out_vec = (os % 4 == 0) && aligned(out16 ? (const void*)out16 : (const void*)out, 16);
+  return sc::launch_lmhead(G, 1, s);
+}
 
 int check_lm_dz(sc::LmParams& P, const int32_t* head_ids, const float* head_probs, int32_t k,
                 const int32_t* sampled, const int32_t* resp_idx, const float* advantages,
@@ -474,15 +521,17 @@ int sc_lmhead_dlogits(const void* hidden, int64_t n_rows, int32_t d, int64_t hid
     return SC_ERR_ARG;
   P.dz = static_cast<uint16_t*>(dlogits);
   P.dzs = dlogits_stride;
+  P.dz_cols = vocab;
   if (n_rows == 0) return SC_OK;
   hipError_t e = sc::launch_lmhead(P, 2, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SC_OK : SC_ERR_HIP;
 }
 
-int64_t sc_lmhead_backward_workspace_size(int64_t chunk_rows, int64_t vocab) {
-  if (chunk_rows < 1 || chunk_rows > kMaxI32 || vocab < 1 || vocab > kMaxI32 - sc::kLmTileV)
+int64_t sc_lmhead_backward_workspace_size(int64_t chunk_rows, int64_t vocab, int32_t d) {
+  if (chunk_rows < 1 || chunk_rows > kMaxI32 || vocab < 1 || vocab > kMaxI32 - sc::kLmTileV ||
+      d < 1)
     return SC_ERR_ARG;
-  return (int64_t)(up256((size_t)chunk_rows * dz_stride(vocab) * 2) + kGemmWorkspace);
+  return (int64_t)bwd_layout(chunk_rows, vocab, d).total;
 }
 
 int sc_lmhead_backward(const void* hidden, int64_t n_rows, int32_t d, int64_t hidden_stride,
@@ -505,29 +554,43 @@ int sc_lmhead_backward(const void* hidden, int64_t n_rows, int32_t d, int64_t hi
   if (!d_weight || dw_stride < d || !aligned(d_weight, 4)) return SC_ERR_ARG;
   if (chunk_rows < 1 || chunk_rows > kMaxI32 || !workspace || !aligned(workspace, 256))
     return SC_ERR_ARG;
-  const int64_t need = sc_lmhead_backward_workspace_size(chunk_rows, vocab);
-  if (workspace_bytes < need) return SC_ERR_ARG;
+  const BwdLayout L = bwd_layout(chunk_rows, vocab, d);
+  if (L.cp > kLmMaxStride || L.vp > kLmMaxStride) return SC_ERR_UNSUPPORTED;
+  if (workspace_bytes < 0 || (size_t)workspace_bytes < L.total) return SC_ERR_ARG;
   if (n_rows == 0) return SC_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t dzs = dz_stride(vocab);
   char* ws = static_cast<char*>(workspace);
-  P.dz = reinterpret_cast<uint16_t*>(ws);
-  P.dzs = dzs;
-  void* gws = ws + up256((size_t)chunk_rows * dzs * 2);
+  uint16_t* wt = reinterpret_cast<uint16_t*>(ws + L.wt);
+  uint16_t* dz = reinterpret_cast<uint16_t*>(ws + L.dz);
+  uint16_t* dzt = reinterpret_cast<uint16_t*>(ws + L.dzt);
+  uint16_t* xt = reinterpret_cast<uint16_t*>(ws + L.xt);
+  P.dz = dz;
+  P.dzs = L.vp;
+  P.dz_cols = L.vp;
+  // W^T [d, Vp], ids past the vocabulary zero
+  hipError_t e = sc::launch_transpose_bf16(P.w, vocab, d, weight_stride, wt, L.vp, L.vp, s);
+  if (e != hipSuccess) return SC_ERR_HIP;
   for (int64_t r0 = 0; r0 < n_rows; r0 += chunk_rows) {
     const int64_t rows = std::min<int64_t>(chunk_rows, n_rows - r0);
     const sc::LmParams Q = lm_slice(P, r0, rows);
-    hipError_t e = sc::launch_lmhead(Q, 2, s);
+    // the chunk's dLogits [rows, Vp] (columns >= V zero), their transpose
+    // [V, chunk_p] and the hidden states' [d, chunk_p] (columns >= rows zero)
+    if ((e = sc::launch_lmhead(Q, 2, s)) != hipSuccess) return SC_ERR_HIP;
+    if ((e = sc::launch_transpose_bf16(dz, rows, vocab, L.vp, dzt, L.cp, L.cp, s)) != hipSuccess)
+      return SC_ERR_HIP;
+    if ((e = sc::launch_transpose_bf16(Q.x, rows, d, hidden_stride, xt, L.cp, L.cp, s)) !=
+        hipSuccess)
+      return SC_ERR_HIP;
+    // dW [V, d] (+)= dZ^T X:  C[v][j] = sum_r dZ^T[v][r] X^T[j][r]
+    e = gemm_nt(xt, d, L.cp, dzt, vocab, L.cp, L.cp, d_weight, nullptr, dw_stride,
+                (accumulate || r0 > 0) ? 1 : 0, s);
     if (e != hipSuccess) return SC_ERR_HIP;
-    // dHidden rows: column-major (d x rows) = W^T (d x V) . dZ^T (V x rows)
+    // dHidden rows [rows, d] = dZ W:  C[r][j] = sum_v dZ[r][v] W^T[j][v]
     char* dh = static_cast<char*>(d_hidden) + r0 * dh_stride * (int64_t)esize(dh_dtype);
-    e = sc::gemm_bf16(false, false, d, rows, vocab, weight, weight_stride, P.dz, dzs, 0.f, dh,
-                      dh_dtype == SC_BF16, dh_stride, gws, kGemmWorkspace, s);
-    if (e != hipSuccess) return SC_ERR_HIP;
-    // dW: column-major (d x V) += X^T (d x rows) . dZ (rows x V)
-    const float beta = (accumulate || r0 > 0) ? 1.f : 0.f;
-    e = sc::gemm_bf16(false, true, d, vocab, rows, Q.x, hidden_stride, P.dz, dzs, beta,
-                      d_weight, 0, dw_stride, gws, kGemmWorkspace, s);
+    e = gemm_nt(wt, d, L.vp, dz, rows, L.vp, L.vp,
+                dh_dtype == SC_BF16 ? nullptr : reinterpret_cast<float*>(dh),
+                dh_dtype == SC_BF16 ? reinterpret_cast<uint16_t*>(dh) : nullptr, dh_stride, 0,
+                s);
     if (e != hipSuccess) return SC_ERR_HIP;
   }
   return SC_OK;

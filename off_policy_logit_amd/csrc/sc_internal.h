@@ -129,9 +129,13 @@ struct LmParams {
   const float* head_logp_in;
   uint16_t* dz;              // bf16 [n_rows, dzs]
   int64_t dzs;
-  // outputs
-  float* out;            // logits check: fp32 [n_rows, os]
+  int64_t dz_cols;           // columns [vocab, dz_cols) of dz are written as 0
+  // outputs of the store mode (logits check, or C = A B^T of the backward)
+  float* out;            // fp32 [n_rows, os], or
+  uint16_t* out16;       // bf16 [n_rows, os]
   int64_t os;
+  int out_accum;         // fp32 out: add to it
+  int out_vec;           // 16-byte aligned rows: vector stores
   float* row_stats;
   int32_t* row_idx;
   float* head_logp;
@@ -142,11 +146,10 @@ struct LmParams {
 // (main, then the recorded / sampled ids).
 hipError_t launch_lmhead(const LmParams& P, int mode, hipStream_t s);
 
-// Library GEMM (hipBLASLt): D (col-major m x n) = op(A) op(B) + beta D, bf16
-// operands, fp32 accumulation, D fp32 or bf16.
-hipError_t gemm_bf16(bool ta, bool tb, int64_t m, int64_t n, int64_t k, const void* A,
-                     int64_t lda, const void* B, int64_t ldb, float beta, void* D,
-                     int d_bf16, int64_t ldd, void* ws, size_t ws_bytes, hipStream_t s);
+// bf16 transpose: dst [cols, rpad] (row stride ds) = src [rows, cols]^T (row
+// stride ss); dst columns [rows, rpad) are written as 0.
+hipError_t launch_transpose_bf16(const uint16_t* src, int64_t rows, int64_t cols, int64_t ss,
+                                 uint16_t* dst, int64_t rpad, int64_t ds, hipStream_t s);
 
 // Rollout-side record (sc_record): top-k of the rollout softmax per row.
 struct RecParams {

@@ -20,7 +20,9 @@
 //   k_lm_finalize  per row: merge the split states in a fixed order, add the
 //                  recorded ids, write the same statistics as sc_logprobs.
 // k_lm_main<1> instead stores the logit tile (a check of the GEMM with the
-// identical accumulation order); k_lm_main<2> recomputes the logits and
+// identical accumulation order; with other operands it is the plain GEMM
+// C = A B^T of the backward, fp32 or bf16, optionally added to C);
+// k_lm_main<2> recomputes the logits and
 // writes the bf16 dLogits of the SC step loss, alpha p_v, for every id, and
 // k_lm_dz_fix then writes the recorded and sampled ids (the backward pass:
 // dLogits for a bounded chunk of rows, consumed by the dHidden and dW GEMMs).
@@ -342,25 +344,53 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
               *reinterpret_cast<u32x2*>(orow + v) = wv2;
             } else {
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
+              for (int e = 0; e < 4; ++e) {
                 if (v + e < V) orow[v + e] = (uint16_t)f32_to_bf16(x[e]);
+                else if (v + e < P.dz_cols) orow[v + e] = 0;
+              }
             }
           }
       }
       return;
     }
     if (STORE) {
+      // out[p][v]: four consecutive ids per (block, g4) group of this lane
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int64_t p = p0 + wp * kWR + j * 32 + lc;
         if (p >= P.n_rows) continue;
-        float* orow = P.out + p * P.os;
 #pragma unroll
         for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int v = v0 + wv * 128 + bi * 32 + lm_row(i, h);
-            if (v < V) orow[v] = acc[bi][j][i];
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int v = v0 + wv * 128 + bi * 32 + 8 * g4 + 4 * h;
+            float a4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a4[e] = acc[bi][j][4 * g4 + e];
+            if (P.out16) {
+              uint16_t* orow = P.out16 + p * P.os;
+              if (P.out_vec && v + 3 < V) {
+                u32x2 wv2;
+                wv2[0] = pack_bf16x2(a4[0], a4[1]);
+                wv2[1] = pack_bf16x2(a4[2], a4[3]);
+                *reinterpret_cast<u32x2*>(orow + v) = wv2;
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  if (v + e < V) orow[v + e] = (uint16_t)f32_to_bf16(a4[e]);
+              }
+            } else {
+              float* orow = P.out + p * P.os;
+              if (P.out_vec && v + 3 < V) {
+                f32x4 x = {a4[0], a4[1], a4[2], a4[3]};
+                if (P.out_accum) x += *reinterpret_cast<const f32x4*>(orow + v);
+                *reinterpret_cast<f32x4*>(orow + v) = x;
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  if (v + e < V) orow[v + e] = P.out_accum ? orow[v + e] + a4[e] : a4[e];
+              }
+            }
           }
       }
       return;
@@ -638,6 +668,27 @@ __global__ __launch_bounds__(256) void k_lm_dz_fix(LmParams P) {
   }
 }
 
+// bf16 transpose through a 64 x 64 LDS tile (rows padded to 66 elements).
+__global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ src,
+                                                        int64_t rows, int64_t cols, int64_t ss,
+                                                        uint16_t* __restrict__ dst, int64_t rpad,
+                                                        int64_t ds) {
+  __shared__ uint16_t tile[64][66];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t r = r0 + ty + 4 * i, cc = c0 + tx;
+    tile[ty + 4 * i][tx] = (r < rows && cc < cols) ? src[r * ss + cc] : (uint16_t)0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t cc = c0 + ty + 4 * i, r = r0 + tx;
+    if (cc < cols && r < rpad) dst[cc * ds + r] = tile[tx][ty + 4 * i];
+  }
+}
+
 template <int MODE>
 hipError_t set_lds_attr() {
   static bool done = false;
@@ -649,6 +700,13 @@ hipError_t set_lds_attr() {
 }
 
 }  // namespace
+
+hipError_t launch_transpose_bf16(const uint16_t* src, int64_t rows, int64_t cols, int64_t ss,
+                                 uint16_t* dst, int64_t rpad, int64_t ds, hipStream_t s) {
+  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rpad + 63) / 64));
+  hipLaunchKernelGGL(k_transpose_bf16, grid, dim3(256), 0, s, src, rows, cols, ss, dst, rpad, ds);
+  return hipGetLastError();
+}
 
 hipError_t launch_lmhead(const LmParams& P, int mode, hipStream_t s) {
   const int per_round = 8 * P.lm_pt;                  // row tiles per group round

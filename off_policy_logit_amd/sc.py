@@ -55,7 +55,7 @@ _SIGS = {
                   _vp, _vp],
     "sc_lmhead_dlogits": [_vp, _i64, _i32, _i64, _vp, _i64, _i64, _vp, _vp, _i32, _vp, _vp,
                           _vp, _i32, _f32, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _i64, _vp],
-    "sc_lmhead_backward_workspace_size": [_i64, _i64],
+    "sc_lmhead_backward_workspace_size": [_i64, _i64, _i32],
     "sc_lmhead_backward": [_vp, _i64, _i32, _i64, _vp, _i64, _i64, _vp, _vp, _i32, _vp, _vp,
                            _vp, _i32, _f32, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
                            ctypes.c_int, _i64, _vp, _i64, ctypes.c_int, _i64, _vp, _i64, _vp],
@@ -385,7 +385,7 @@ def lmhead_dlogits(hidden, weight, stats, head_ids, head_probs, sampled, resp_id
 
 def lmhead_backward(hidden, weight, stats, head_ids, head_probs, sampled, resp_idx,
                     advantages, n_valid, temperature=1.0, centering=True, d_hidden=None,
-                    d_weight=None, accumulate=False, chunk_rows=2048, workspace=None,
+                    d_weight=None, accumulate=False, chunk_rows=8192, workspace=None,
                     stream=None):
     """sc_lmhead_backward: (d_hidden, d_weight) of the step loss through the
     LM head, chunk_rows rows of dLogits at a time."""
@@ -398,7 +398,7 @@ def lmhead_backward(hidden, weight, stats, head_ids, head_probs, sampled, resp_i
         d_hidden = torch.empty(n, d, dtype=torch.float32, device=dev)
     if d_weight is None:
         d_weight = torch.zeros(V, d, dtype=torch.float32, device=dev)
-    need = lib().sc_lmhead_backward_workspace_size(int(chunk_rows), V)
+    need = lib().sc_lmhead_backward_workspace_size(int(chunk_rows), V, d)
     if need < 0:
         _check(need)
     if workspace is None:

@@ -229,3 +229,31 @@ def test_record_rejects_bad_arguments(kw):
 def test_record_zero_rows_and_optional_sampled():
     assert record(n=0) == OK
     assert record(n=0, a=NULL, lp=NULL) == OK
+
+
+def test_lmhead_backward_workspace_and_arguments():
+    L = sc.lib()
+    assert L.sc_lmhead_backward_workspace_size(0, 100, 64) == ARG
+    assert L.sc_lmhead_backward_workspace_size(10, 0, 64) == ARG
+    assert L.sc_lmhead_backward_workspace_size(10, 100, 0) == ARG
+    # W^T [d, Vp] + dZ [chunk, Vp] + dZ^T [V, chunk_p] + X^T [d, chunk_p], bf16
+    got = L.sc_lmhead_backward_workspace_size(100, 1000, 64)
+    assert got >= 2 * (64 * 1024 + 100 * 1024 + 1000 * 128 + 64 * 128)
+
+    def bwd(**kw):
+        a = dict(x=FAKE, n=300, d=256, xs=256, w=FAKE, V=1000, ws=256, ids=FAKE, q=FAKE, k=16,
+                 a=FAKE, resp=NULL, adv=FAKE, nresp=1, T=1.0, nv=FAKE, st=FAKE, idx=FAKE,
+                 hlp=FAKE, cen=1, dh=FAKE, dhd=sc.SC_F32, dhs=256, dw=FAKE, dws=256, acc=0,
+                 chunk=128, wsp=FAKE256, wsb=1 << 40, stream=NULL)
+        a.update(kw)
+        return L.sc_lmhead_backward(
+            a["x"], a["n"], a["d"], a["xs"], a["w"], a["V"], a["ws"], a["ids"], a["q"], a["k"],
+            a["a"], a["resp"], a["adv"], a["nresp"], a["T"], a["nv"], a["st"], a["idx"],
+            a["hlp"], a["cen"], a["dh"], a["dhd"], a["dhs"], a["dw"], a["dws"], a["acc"],
+            a["chunk"], a["wsp"], a["wsb"], a["stream"])
+    assert bwd(n=0) == OK
+    for kw in (dict(dh=NULL), dict(dw=NULL), dict(dhs=100), dict(dws=100), dict(chunk=0),
+               dict(wsp=NULL), dict(wsb=1000), dict(st=NULL), dict(idx=NULL), dict(hlp=NULL),
+               dict(adv=NULL), dict(nv=NULL), dict(dhd=7), dict(q=NULL)):
+        assert bwd(**kw) == ARG, kw
+    assert bwd(d=100, xs=104, ws=104) == UNSUP

@@ -1,6 +1,7 @@
 """GPU parity of the LM-head backward: bf16 dLogits recomputed by the MFMA
 kernel (sc_lmhead_dlogits) and the gradients dHidden = dZ W, dW = dZ^T X
-(sc_lmhead_backward) against the float64 oracle on the kernel's own logits.
+(sc_lmhead_backward, both products on the library's MFMA loop) against the
+float64 oracle on the kernel's own logits.
 
 Tolerances: dLogits rows as the other bf16 rows (one bf16 step of the RNE of
 the float64 value, >= 99.5% bit-equal; the kernel takes lse from the fp32
@@ -115,7 +116,7 @@ def test_lmhead_backward_matches_oracle(dh_dtype, chunk):
 
 
 def test_lmhead_backward_full_vocab_slice():
-    """The bench's launch: 16,384 rows, V = 248,320, d = 4,096, 2,048-row chunks."""
+    """The bench's launch: 16,384 rows, V = 248,320, d = 4,096, 8,192-row chunks."""
     n, V, d, T = 16_384, synthetic.VOCAB, 4096, 1.0
     say(f"lmhead backward full slice n={n} V={V} d={d}: forward")
     w, c, resp, adv, nv, st, _ = forward(n, V, d, T, 5, w_sd=0.02)
@@ -123,7 +124,7 @@ def test_lmhead_backward_full_vocab_slice():
     dh = torch.empty(n, d, dtype=torch.bfloat16, device=DEV)
     dW = torch.empty(V, d, device=DEV)
     sc.lmhead_backward(c["hidden"], w, st, c["head_ids"], c["head_probs"], c["sampled"],
-                       resp, adv, nv, temperature=T, d_hidden=dh, d_weight=dW, chunk_rows=2048)
+                       resp, adv, nv, temperature=T, d_hidden=dh, d_weight=dW, chunk_rows=8192)
     torch.cuda.synchronize()
     # sampled rows of dHidden against the oracle (row by row at full V)
     rng = np.random.default_rng(3)
