@@ -38,8 +38,11 @@ HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix peak
 LM_ROWS, LM_D = 16_384, 4096    # fused LM-head slice (64 x 8,800-token batch, d = 4,096)
 PROFILE = os.path.join(ROOT, "profiles", "sc_correct_quick_check_pmc.md")
+# Sources of the fused row kernel whose counters profiles/ holds (its launch
+# shape is set in sc_kernels.hip's template arguments and sc_internal.h's
+# macros; the latter file also carries unrelated structs, so it is left out).
 KERNEL_SOURCES = [os.path.join(ROOT, "off_policy_logit_amd", "csrc", f)
-                  for f in ("sc_kernels.hip", "sc_device.h", "sc_internal.h", "sc_api.cpp")]
+                  for f in ("sc_kernels.hip", "sc_device.h")]
 
 # Algorithmic bytes of one position through the fused kernel (sc_correct with
 # a bf16 dLogits row): logits 2V, head ids 4K, head probs 4K, sampled,
