@@ -573,16 +573,20 @@ int sc_lmhead_backward(const void* hidden, int64_t n_rows, int32_t d, int64_t hi
   for (int64_t r0 = 0; r0 < n_rows; r0 += chunk_rows) {
     const int64_t rows = std::min<int64_t>(chunk_rows, n_rows - r0);
     const sc::LmParams Q = lm_slice(P, r0, rows);
-    // the chunk's dLogits [rows, Vp] (columns >= V zero), their transpose
-    // [V, chunk_p] and the hidden states' [d, chunk_p] (columns >= rows zero)
-    if ((e = sc::launch_lmhead(Q, 2, s)) != hipSuccess) return SC_ERR_HIP;
-    if ((e = sc::launch_transpose_bf16(dz, rows, vocab, L.vp, dzt, L.cp, L.cp, s)) != hipSuccess)
-      return SC_ERR_HIP;
-    if ((e = sc::launch_transpose_bf16(Q.x, rows, d, hidden_stride, xt, L.cp, L.cp, s)) !=
+    // the chunk's dLogits [rows, Vp] (columns >= V zero) and their transpose
+    // [V, rows_p] from the same kernel, the hidden states' transpose
+    // [d, rows_p] (rows_p = rows rounded up to 64, columns >= rows zero)
+    const int64_t rp = pad64(rows);
+    sc::LmParams Qd = Q;
+    Qd.dzt = dzt;
+    Qd.dzts = L.cp;
+    Qd.dzt_cols = rp;
+    if ((e = sc::launch_lmhead(Qd, 2, s)) != hipSuccess) return SC_ERR_HIP;
+    if ((e = sc::launch_transpose_bf16(Q.x, rows, d, hidden_stride, xt, rp, L.cp, s)) !=
         hipSuccess)
       return SC_ERR_HIP;
-    // dW [V, d] (+)= dZ^T X:  C[v][j] = sum_r dZ^T[v][r] X^T[j][r]
-    e = gemm_nt(xt, d, L.cp, dzt, vocab, L.cp, L.cp, d_weight, nullptr, dw_stride,
+    // dW [V, d] (+)= dZ^T X:  C[v][j] = sum_r dZ^T[v][r] X^T[j][r], r < rows_p
+    e = gemm_nt(xt, d, L.cp, dzt, vocab, L.cp, rp, d_weight, nullptr, dw_stride,
                 (accumulate || r0 > 0) ? 1 : 0, s);
     if (e != hipSuccess) return SC_ERR_HIP;
     // dHidden rows [rows, d] = dZ W:  C[r][j] = sum_v dZ[r][v] W^T[j][v]

@@ -130,6 +130,9 @@ struct LmParams {
   uint16_t* dz;              // bf16 [n_rows, dzs]
   int64_t dzs;
   int64_t dz_cols;           // columns [vocab, dz_cols) of dz are written as 0
+  uint16_t* dzt;             // optional transpose: bf16 [vocab, dzts], columns
+  int64_t dzts;              //   [n_rows, dzt_cols) written as 0
+  int64_t dzt_cols;
   // outputs of the store mode (logits check, or C = A B^T of the backward)
   float* out;            // fp32 [n_rows, os], or
   uint16_t* out16;       // bf16 [n_rows, os]

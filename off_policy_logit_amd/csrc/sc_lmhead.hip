@@ -320,6 +320,27 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
   auto epilogue = [&](int ck) {
     const int v0 = ck * kTV;
     if (MODE == 2) {
+      if (P.dzt) {
+        // transposed copy: dzt[v][p]; lanes hold consecutive rows p, so each
+        // store instruction writes 64 contiguous bytes per id; rows past
+        // n_rows (up to dzt_cols) are written as 0
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int64_t p = p0 + wp * kWR + j * 32 + lc;
+          if (p >= P.dzt_cols) continue;
+          const bool live = p < P.n_rows;
+#pragma unroll
+          for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int v = v0 + wv * 128 + bi * 32 + lm_row(i, h);
+              if (v >= V) continue;
+              float y = exp2_fast(fmaf(acc[bi][j][i], c, dz_off[j])) * 0x1p-32f;
+              y = dz_neg[j] ? -y : y;
+              P.dzt[(int64_t)v * P.dzts + p] = live ? (uint16_t)f32_to_bf16(y) : (uint16_t)0;
+            }
+        }
+      }
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int64_t p = p0 + wp * kWR + j * 32 + lc;
@@ -658,24 +679,62 @@ __global__ __launch_bounds__(256) void k_lm_dz_fix(LmParams P) {
     const double v = P.centering ? scale * (ind - (double)P.head_probs[p * K + k] - oms * pk)
                                  : scale * (ind - pk);
     orow[id] = (uint16_t)f32_to_bf16((float)v);
+    if (P.dzt) P.dzt[(int64_t)id * P.dzts + p] = (uint16_t)f32_to_bf16((float)v);
   }
   if (l == 0 && a_slot < 0) {
     const int32_t a = P.sampled[p];
     if (a >= 0 && a < P.vocab) {
       const double pa = exp((double)st[SC_STAT_LOGP_A]);
-      orow[a] = (uint16_t)f32_to_bf16((float)(alpha * pa + scale));
+      const uint16_t va = (uint16_t)f32_to_bf16((float)(alpha * pa + scale));
+      orow[a] = va;
+      if (P.dzt) P.dzt[(int64_t)a * P.dzts + p] = va;
     }
   }
 }
 
-// bf16 transpose through a 64 x 64 LDS tile (rows padded to 66 elements).
+// bf16 transpose through a 64 x 64 LDS tile.  With 16-byte aligned rows
+// (vec) each thread moves 8 consecutive elements per access; otherwise one.
 __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ src,
                                                         int64_t rows, int64_t cols, int64_t ss,
                                                         uint16_t* __restrict__ dst, int64_t rpad,
-                                                        int64_t ds) {
-  __shared__ uint16_t tile[64][66];
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+                                                        int64_t ds, int vec) {
+  __shared__ __align__(16) uint16_t tile[64][72];   // 144-byte rows: 16-byte aligned, banks rotate
+  const int t = threadIdx.x;
   const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
+  if (vec) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = t + 256 * q, r = idx >> 3, c8 = (idx & 7) * 8;
+      const int64_t gr = r0 + r, gc = c0 + c8;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (gr < rows) {
+        if (gc + 7 < cols) {
+          x = *reinterpret_cast<const u32x4*>(src + gr * ss + gc);
+        } else {
+          uint16_t e[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) e[k] = gc + k < cols ? src[gr * ss + gc + k] : (uint16_t)0;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) x[k] = (uint32_t)e[2 * k] | ((uint32_t)e[2 * k + 1] << 16);
+        }
+      }
+      *reinterpret_cast<u32x4*>(&tile[r][c8]) = x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = t + 256 * q, cc = idx >> 3, r8 = (idx & 7) * 8;
+      const int64_t gc = c0 + cc, gr = r0 + r8;
+      if (gc >= cols || gr >= rpad) continue;
+      u32x4 x;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        x[k] = (uint32_t)tile[r8 + 2 * k][cc] | ((uint32_t)tile[r8 + 2 * k + 1][cc] << 16);
+      *reinterpret_cast<u32x4*>(dst + gc * ds + gr) = x;
+    }
+    return;
+  }
+  const int tx = t & 63, ty = t >> 6;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int64_t r = r0 + ty + 4 * i, cc = c0 + tx;
@@ -704,7 +763,11 @@ hipError_t set_lds_attr() {
 hipError_t launch_transpose_bf16(const uint16_t* src, int64_t rows, int64_t cols, int64_t ss,
                                  uint16_t* dst, int64_t rpad, int64_t ds, hipStream_t s) {
   const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rpad + 63) / 64));
-  hipLaunchKernelGGL(k_transpose_bf16, grid, dim3(256), 0, s, src, rows, cols, ss, dst, rpad, ds);
+  // the vector path needs 16-byte aligned rows and whole 64-row output tiles
+  const int vec = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 == 0) &&
+                  ss % 8 == 0 && ds % 8 == 0 && rpad % 64 == 0;
+  hipLaunchKernelGGL(k_transpose_bf16, grid, dim3(256), 0, s, src, rows, cols, ss, dst, rpad, ds,
+                     vec);
   return hipGetLastError();
 }
 
