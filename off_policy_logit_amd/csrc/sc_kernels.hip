@@ -266,7 +266,9 @@ void k_row(RowParams P) {
         s_t *= r;
         m_t = m_new;
       };
-      // exp sum and exp-weighted offset sum of one vector (-inf entries add 0)
+      // exp sum and exp-weighted offset sum of one vector.  A -inf entry
+      // makes its term 0 * -inf = NaN in acch; the stream leaves h_t NaN
+      // then and the thread recomputes it after the stream (see below).
       auto vec_sums = [&](const float (&v)[N], float& acc, float& acch) {
         acc = 0.f;
         acch = 0.f;
@@ -275,23 +277,41 @@ void k_row(RowParams P) {
           const float d = v[i] - m_t;
           const float e = exp2_fast(d * c);
           acc += e;
-          acch = fmaf(e, fmaxf(d, -FLT_MAX), acch);
+          acch = fmaf(e, d, acch);
         }
       };
       // Branch-free: marked vectors are summed too and the sum is dropped
-      // (they are resolved element by element after the stream).
+      // (they are resolved element by element after the stream).  The
+      // running max is raised once per group of kG vectors, so one rescale
+      // serves kG vectors.
+      constexpr int kG = kU >= 4 ? 4 : kU;
       auto process = [&](const Raw (&r)[kU], int j0) {
         const uint32_t bits = tile_bits(j0);
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          float v[N];
-          IO::unpack(r[u], v);
-          vec_update(v, j0 + u);
-          float acc, acch;
-          vec_sums(v, acc, acch);
-          const bool marked = (bits >> u) & 1u;
-          s_t += marked ? 0.f : acc;
-          h_t += marked ? 0.f : acch;
+        for (int u0 = 0; u0 < kU; u0 += kG) {
+          float v[kG][N];
+          float m_run = m_t;
+#pragma unroll
+          for (int u = 0; u < kG; ++u) {
+            IO::unpack(r[u0 + u], v[u]);
+            float vm = v[u][0];
+#pragma unroll
+            for (int i = 1; i < N; ++i) vm = fmaxf(vm, v[u][i]);
+            am_vec = vm > m_run ? j0 + u0 + u : am_vec;   // strictly: first of equal maxima
+            m_run = fmaxf(m_run, vm);
+          }
+          const float rs = exp2_fast((m_t - m_run) * c);
+          h_t = rs * (h_t - (m_run - m_t) * s_t);
+          s_t *= rs;
+          m_t = m_run;
+#pragma unroll
+          for (int u = 0; u < kG; ++u) {
+            float acc, acch;
+            vec_sums(v[u], acc, acch);
+            const bool marked = (bits >> (u0 + u)) & 1u;
+            s_t += marked ? 0.f : acc;
+            h_t += marked ? 0.f : acch;
+          }
         }
       };
       {
@@ -311,6 +331,24 @@ void k_row(RowParams P) {
           s_t += marked ? 0.f : acc;
           h_t += marked ? 0.f : acch;
         }
+      }
+      // A -inf logit among this thread's unmarked vectors left h_t NaN (its
+      // term 0 * -inf): recompute the entropy sum against the final m_t with
+      // the term clamped to 0, reading the thread's vectors again.  A NaN
+      // logit leaves s_t NaN as well (the row is flagged) and is left alone.
+      if (h_t != h_t && s_t == s_t) {
+        float hh = 0.f;
+        for (int j = 0; j < J; ++j) {
+          if ((bitmap[(j >> 5) * B + t] >> (j & 31)) & 1u) continue;
+          float v[N];
+          IO::unpack(load_one(j, std::false_type{}), v);
+#pragma unroll
+          for (int i = 0; i < N; ++i) {
+            const float d = v[i] - m_t;
+            hh = fmaf(exp2_fast(d * c), fmaxf(d, -FLT_MAX), hh);
+          }
+        }
+        h_t = hh;
       }
       list_marked();
       // The partial last vector (vocab not a multiple of N) always goes to the

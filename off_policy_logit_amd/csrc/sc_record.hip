@@ -77,8 +77,11 @@ SC_DEV int lane_rank(unsigned long long bal) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
 }
 
+// At most 128 VGPRs (four waves per SIMD): the row stream, the hot loop,
+// stays free of spills; the rare paths (fallback passes, sort) may spill.
 template <typename T, bool VECTOR>
-__global__ __launch_bounds__(kRB) void k_record(RecParams P) {
+__global__ __launch_bounds__(kRB) __attribute__((amdgpu_waves_per_eu(4)))
+void k_record(RecParams P) {
   using IO = RowIO<T, VECTOR>;
   using Raw = typename IO::raw;
   constexpr int N = IO::N;
