@@ -507,3 +507,37 @@ def test_stress_chunk(sigma):
     say(f"  clamp-active rows in chunk: {len(clamp)}; checking {len(rows)} rows")
     check_rows(f"stress sigma={sigma}", d, out, rows, np.array([1.0]), 16384, 1.0,
                O.MODE_SCORE, "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_masked_vocabulary_rows(dtype):
+    """Rows with a masked (-inf) share of the vocabulary: the statistics
+    stream drops those terms from the entropy sum through its recompute path
+    (every thread of these rows meets a -inf)."""
+    n, V, K = 24, 50_000, 64
+    say(f"masked-vocabulary rows n={n} V={V} K={K} {dtype}")
+    d, z = crafted(n, V, K, seed=9, dtype=dtype)
+    rng = np.random.default_rng(10)
+    ids = d["head_ids"].cpu().numpy()
+    a = d["sampled"].cpu().numpy()
+    for r in range(n):
+        frac = (0.0, 0.01, 0.4, 0.95)[r % 4]
+        mask = rng.random(V) < frac
+        mask[ids[r]] = False
+        mask[a[r]] = False
+        z[r, mask] = -np.inf
+    logits = torch.from_numpy(z).to(DEV)
+    d["logits"] = logits.to(torch.bfloat16) if dtype == "bf16" else logits
+    adv = torch.linspace(-1.0, 1.0, 6, device=DEV)
+    n_valid = sc.count_valid(d["resp_idx"])
+    out = run_correct(d, adv, n_valid, 1.0, O.MODE_DLOGITS, "bf16")
+    st = sc.logprobs(d["logits"], d["head_ids"], d["sampled"], d["resp_idx"])
+    torch.cuda.synchronize()
+    assert int(out["status"].item()) == 0
+    check_rows(f"masked {dtype}", d, out, np.arange(n), adv.cpu().numpy(), n, 1.0,
+               O.MODE_DLOGITS, "bf16", logits_h=z)
+    ent = st["row_stats"][:, sc.STAT["entropy"]].cpu().numpy()
+    for r in range(n):
+        o = O.sc_row(z[r].astype(np.float64), 1.0, ids[r], d["head_probs"][r].cpu().numpy(),
+                     a[r])
+        assert abs(ent[r] - o["entropy"]) <= 1e-5 + 1e-5 * abs(o["entropy"]), (r, ent[r])
