@@ -288,6 +288,26 @@ int lm_splits(int64_t vocab) {
 
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Grid order of the MFMA tile loop (needs P.splits): share the larger
+// operand's tiles.  With row tiles as the larger side, the 32 concurrent
+// workgroups of an XCD take lm_pt row tiles x lm_sp splits, lm_sp dividing
+// the split count: 8 when it can, every split when there are at most 32,
+// else the largest divisor below 8.
+void lm_order(sc::LmParams& P, int64_t rows, int64_t vocab) {
+  P.order = rows > vocab ? 1 : 0;
+  int sp = 1;
+  if (P.splits % 8 == 0) {
+    sp = 8;
+  } else if (P.splits <= 32) {
+    sp = P.splits;
+  } else {
+    for (int q = 7; q >= 1; --q)
+      if (P.splits % q == 0) { sp = q; break; }
+  }
+  P.lm_sp = sp;
+  P.lm_pt = std::max(1, 32 / sp);
+}
+
 // Workspace layout; returns its size and, when P is given, points P's
 // workspace arrays into `base`.
 size_t lm_workspace(int64_t n, int64_t vocab, int k, sc::LmParams* P, char* base) {
@@ -332,12 +352,9 @@ int check_lm(sc::LmParams& P, const void* hidden, int64_t n_rows, int32_t d,
   P.vocab = vocab;
   P.d = d;
   P.splits = lm_splits(vocab);
+  lm_order(P, n_rows, vocab);
   P.n_chunks = (int)((vocab + sc::kLmTileV - 1) / sc::kLmTileV);
   P.n_ptiles = (int)((n_rows + sc::kLmTileP - 1) / sc::kLmTileP);
-  // 32 concurrent workgroups per XCD: 4 row tiles x 8 splits when the split
-  // count allows, else every split of 32 / splits row tiles.
-  P.lm_sp = P.splits % 8 == 0 ? 8 : P.splits;
-  P.lm_pt = std::max(1, 32 / P.lm_sp);
   return SC_OK;
 }
 
@@ -443,10 +460,9 @@ hipError_t gemm_nt(const uint16_t* A, int64_t m, int64_t as, const uint16_t* B, 
   G.vocab = m;
   G.d = (int)k;
   G.splits = lm_splits(m);
+  lm_order(G, n, m);
   G.n_chunks = (int)((m + sc::kLmTileV - 1) / sc::kLmTileV);
   G.n_ptiles = (int)((n + sc::kLmTileP - 1) / sc::kLmTileP);
-  G.lm_sp = G.splits % 8 == 0 ? 8 : G.splits;
-  G.lm_pt = std::max(1, 32 / G.lm_sp);
   G.out = out;
   G.out16 = out16;
   G.os = os;

@@ -89,11 +89,11 @@ struct RowParams {
 hipError_t launch_row(const RowParams& P, int kind, int grid, hipStream_t s);
 
 // Fused LM-head statistics (sc_logprobs_lmhead / sc_lmhead_logits): tile of
-// 256 vocabulary ids x 256 rows, k stages of 64, at most 32 vocabulary splits.
+// 256 vocabulary ids x 256 rows, k stages of 64, at most 256 vocabulary splits.
 constexpr int kLmTileV = 256;
 constexpr int kLmTileP = 256;
 constexpr int kLmKStage = 64;
-constexpr int kLmMaxSplits = 32;
+constexpr int kLmMaxSplits = 256;
 
 struct LmParams {
   const uint16_t* x;     // hidden states, bf16 [n_rows, d], row stride xs
@@ -104,7 +104,8 @@ struct LmParams {
   int d;
   float c;               // log2(e) / T
   int splits, n_chunks, n_ptiles;
-  int lm_pt, lm_sp;      // row tiles x splits per XCD group (lm_sp divides splits)
+  int order;             // 0: row tiles vary fastest over the grid, 1: XCD groups
+  int lm_pt, lm_sp;      // order 1: row tiles x splits per XCD group (lm_sp divides splits)
   const int32_t* head_ids;
   int32_t k;
   const int32_t* sampled;

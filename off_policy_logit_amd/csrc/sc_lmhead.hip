@@ -162,18 +162,32 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
   const int wv = w & 1, wp = w >> 1;   // wave's vocabulary half, row quarter
   const int h = l >> 5, lc = l & 31;
 
-  // Work item.  Workgroups are dispatched round-robin over the 8 XCDs
-  // (blockIdx mod 8); each XCD's group of lm_pt * lm_sp concurrent workgroups
-  // covers lm_pt row tiles x lm_sp vocabulary splits, so every W chunk is
-  // read by lm_pt and every hidden-state tile by lm_sp workgroups sharing
-  // that XCD's L2 (instead of one of the two being read once per workgroup).
+  // Work item.  Workgroups are dispatched in index order, round-robin over
+  // the 8 XCDs (blockIdx mod 8), so the ~256 resident at a time take
+  // consecutive indices.
+  //  order 0 (W, the vocabulary-side operand, is the larger one): row tiles
+  //    vary fastest, so the resident blocks cover a few consecutive splits
+  //    (runs of 256-id chunks) for every row tile and each W chunk is read by
+  //    all row tiles at about the same time (one XCD's row tiles through its
+  //    L2, the XCDs through the memory-side cache); a block lives only a few
+  //    chunks, so the blocks sharing a chunk stay in step.
+  //  order 1 (the row-side operand is the larger one): each XCD's group of
+  //    lm_pt x lm_sp concurrent workgroups covers lm_pt row tiles x lm_sp
+  //    splits, so every chunk is read by lm_pt and every row tile by lm_sp
+  //    workgroups sharing that XCD's L2.
   const int b = blockIdx.x;
-  const int xcd = b & 7, idx = b >> 3;
-  const int grp = idx / (P.lm_pt * P.lm_sp), loc = idx % (P.lm_pt * P.lm_sp);
-  const int sg = P.splits / P.lm_sp;                 // split groups
-  const int split = (grp % sg) * P.lm_sp + loc % P.lm_sp;
-  const int ptile = ((grp / sg) * P.lm_pt + loc / P.lm_sp) * 8 + xcd;
-  if (ptile >= P.n_ptiles) return;
+  int split, ptile;
+  if (P.order == 0) {
+    split = b / P.n_ptiles;
+    ptile = b - split * P.n_ptiles;
+  } else {
+    const int xcd = b & 7, idx = b >> 3;
+    const int grp = idx / (P.lm_pt * P.lm_sp), loc = idx % (P.lm_pt * P.lm_sp);
+    const int sg = P.splits / P.lm_sp;                 // split groups
+    split = (grp % sg) * P.lm_sp + loc % P.lm_sp;
+    ptile = ((grp / sg) * P.lm_pt + loc / P.lm_sp) * 8 + xcd;
+  }
+  if (split >= P.splits || ptile >= P.n_ptiles) return;
   const int64_t p0 = (int64_t)ptile * kTP;
   const int c_begin = (int)((int64_t)split * P.n_chunks / P.splits);
   const int c_end = (int)((int64_t)(split + 1) * P.n_chunks / P.splits);
@@ -590,11 +604,12 @@ __global__ __launch_bounds__(256) void k_lm_finalize(LmParams P) {
     } else {
       uint32_t fl = P.sflags[p];
       // merge the split states in a fixed butterfly order
+      // (lane l takes splits l, l + 64, ... in order, then the butterfly)
       float m = -FLT_MAX, s = 0.f, hy = 0.f;
       int am = kNoIdx;
-      if (l < P.splits) {
-        const float4 st = P.state[(int64_t)l * P.n_rows + p];
-        m = st.x; s = st.y; hy = st.z; am = __float_as_int(st.w);
+      for (int q = l; q < P.splits; q += kWave) {
+        const float4 st = P.state[(int64_t)q * P.n_rows + p];
+        lm_merge(m, s, hy, am, st.x, st.y, st.z, __float_as_int(st.w), c);
       }
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
@@ -772,8 +787,11 @@ hipError_t launch_transpose_bf16(const uint16_t* src, int64_t rows, int64_t cols
 }
 
 hipError_t launch_lmhead(const LmParams& P, int mode, hipStream_t s) {
-  const int per_round = 8 * P.lm_pt;                  // row tiles per group round
-  const int grid = ((P.n_ptiles + per_round - 1) / per_round) * 8 * P.lm_pt * P.splits;
+  int grid = P.splits * P.n_ptiles;
+  if (P.order == 1) {
+    const int per_round = 8 * P.lm_pt;                // row tiles per group round
+    grid = ((P.n_ptiles + per_round - 1) / per_round) * 8 * P.lm_pt * P.splits;
+  }
   hipError_t e = hipSuccess;
   if (mode == 1) {
     if ((e = set_lds_attr<1>()) != hipSuccess) return e;
