@@ -38,7 +38,8 @@ def product_bound(x, w, d):
 
 
 @pytest.mark.parametrize("n,V,d,pad", [(600, 4099, 256, 0), (300, 3000, 4096, 0),
-                                       (37, 300, 64, 0), (513, 1031, 192, 64)])
+                                       (37, 300, 64, 0), (513, 1031, 192, 64),
+                                       (1100, 700, 128, 0)])
 def test_lmhead_logits_match_float64_product(n, V, d, pad):
     say(f"lmhead logits n={n} V={V} d={d} row padding={pad}")
     w_full = (torch.randn(V, d + pad, generator=gen(1), device=DEV) * 0.05).to(torch.bfloat16)
@@ -181,4 +182,22 @@ def test_lmhead_full_vocab_slice():
     for j, r in enumerate(rows):
         o = O.sc_row(zh[j], 1.0, idh[j], qh[j], ah[j])
         check_row(f"lmhead full row {r}", dict(stats=st[j], idx=ix[j], head_logp=hl[j]), o,
+                  stats_only=True)
+
+
+def test_lmhead_more_rows_than_vocabulary():
+    """Rows outnumber vocabulary ids: the tile loop's XCD-group order (split
+    counts that are not multiples of 8)."""
+    n, V, d, T = 2600, 1300, 128, 1.0
+    say(f"lmhead stats n={n} V={V} d={d} (more rows than ids)")
+    w, wr = synthetic.lmhead_weights(DEV, vocab=V, d=d, seed=21, w_sd=0.1)
+    c = synthetic.lmhead_chunk(DEV, wr, n, seed=22, temperature=T)
+    out = run_lmhead(c, w, None, T)
+    z = sc.lmhead_logits(c["hidden"], w)
+    torch.cuda.synchronize()
+    zh, idh, qh, ah = host(z), host(c["head_ids"]), host(c["head_probs"]), host(c["sampled"])
+    st, ix, hl = host(out["row_stats"]), host(out["row_idx"]), host(out["head_logp"])
+    for r in range(0, n, 37):
+        o = O.sc_row(zh[r], T, idh[r], qh[r], ah[r])
+        check_row(f"rows>ids row {r}", dict(stats=st[r], idx=ix[r], head_logp=hl[r]), o,
                   stats_only=True)
