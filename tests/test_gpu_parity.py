@@ -541,3 +541,20 @@ def test_masked_vocabulary_rows(dtype):
         o = O.sc_row(z[r].astype(np.float64), 1.0, ids[r], d["head_probs"][r].cpu().numpy(),
                      a[r])
         assert abs(ent[r] - o["entropy"]) <= 1e-5 + 1e-5 * abs(o["entropy"]), (r, ent[r])
+
+
+@pytest.mark.parametrize("dtype,K,T", [("f32", 128, 1.0), ("bf16", 1024, 0.6)])
+def test_full_vocabulary_fp32_and_k1024(dtype, K, T):
+    """Full-vocabulary rows (V = 248,320) on the paths the quick-check bench
+    does not take: fp32 logits (4 per 16-byte vector), and K = 1024 recorded
+    ids (the row kernels' LDS beyond 64 KB), at another temperature."""
+    n, V = 12, synthetic.VOCAB
+    say(f"full-vocabulary rows n={n} {dtype} K={K} T={T}")
+    d, z = crafted(n, V, K, seed=K + 3, dtype=dtype, scale=2.5)
+    adv = torch.tensor([0.8, -1.2, 0.3], device=DEV)
+    n_valid = sc.count_valid(d["resp_idx"])
+    out = run_correct(d, adv, n_valid, T, O.MODE_DLOGITS, "bf16")
+    torch.cuda.synchronize()
+    assert int(out["status"].item()) == 0
+    check_rows(f"full-V {dtype} K={K}", d, out, np.arange(n), adv.cpu().numpy(), n, T,
+               O.MODE_DLOGITS, "bf16", logits_h=z)
