@@ -718,14 +718,31 @@ __global__ __launch_bounds__(B) void k_batch_sums(const float* __restrict__ st,
 #pragma unroll
   for (int j = 0; j < NS + 2; ++j) v[j] = 0.0;
   float wmax = -INFINITY;
-  for (int64_t i = threadIdx.x; i < n; i += B) {
-    if (resp[i] < 0) continue;
-    const float* s = st + i * C_N;
+  // Rows t, t + B, ... in order; R rows' loads are issued together (a padding
+  // row's statistics are read too and then skipped), so the loop waits on
+  // memory once per R rows instead of twice per row.
+  constexpr int R = 4;
+  for (int64_t i0 = threadIdx.x; i0 < n; i0 += (int64_t)R * B) {
+    int rv[R];
+    float x[R][NS + 1];
 #pragma unroll
-    for (int j = 0; j < NS; ++j) v[j] += (double)s[SUMS[j]];
-    v[NS] += 1.0;
-    v[NS + 1] += (s[C_LOSS] != s[C_LOSS]) ? 1.0 : 0.0;
-    wmax = fmaxf(wmax, s[C_W]);
+    for (int q = 0; q < R; ++q) {
+      const int64_t i = i0 + (int64_t)q * B;
+      rv[q] = i < n ? resp[i] : -1;
+      const float* s = st + (i < n ? i : 0) * C_N;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) x[q][j] = s[SUMS[j]];
+      x[q][NS] = s[C_W];
+    }
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      if (rv[q] < 0) continue;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) v[j] += (double)x[q][j];
+      v[NS] += 1.0;
+      v[NS + 1] += (x[q][0] != x[q][0]) ? 1.0 : 0.0;   // x[q][0] is the loss
+      wmax = fmaxf(wmax, x[q][NS]);
+    }
   }
   block_sum<B, NS + 2>(v, red);
   int dummy = 0;
