@@ -208,20 +208,52 @@ void k_record(RecParams P) {
       if (pos < (unsigned)cap) buf[pos] = key64(x, (uint32_t)id);
     };
 
-    // Online max / sum and the candidate filter for one vector per lane.
-    auto vec = [&](const float (&v)[N], int j, bool active) {
-      float vm = v[0];
+    // Element i (run time) of a packed vector: a select chain.
+    auto elem_rt = [](const Raw& w, int i) -> float {
+      float x = IO::elem(w, 0);
 #pragma unroll
-      for (int i = 1; i < N; ++i) vm = fmaxf(vm, v[i]);
-      const float mn = fmaxf(m_t, vm);
-      s_t *= exp2_fast((m_t - mn) * c);
-      m_t = mn;
+      for (int q = 1; q < N; ++q) x = (i == q) ? IO::elem(w, q) : x;
+      return x;
+    };
+    // One tile of kRU vectors per lane: the maxima, one rescale of the running
+    // sum, the exp sums.  Vectors whose maximum reaches the bound are only
+    // flagged here; their elements are tested and pushed afterwards by the
+    // lanes that hold them (few once the bound has risen).
+    auto tile = [&](const Raw (&r)[kRU], int j0) {
+      float v[kRU][N];
+      float m_run = m_t;
+      uint32_t cmask = 0u;
 #pragma unroll
-      for (int i = 0; i < N; ++i) s_t += exp2_fast((v[i] - m_t) * c);
-      if (active && vm >= thr) {
+      for (int u = 0; u < kRU; ++u) {
+        IO::unpack(r[u], v[u]);
+        float vm = v[u][0];
 #pragma unroll
-        for (int i = 0; i < N; ++i)
-          if (v[i] >= thr) push(v[i], j * N + i);
+        for (int i = 1; i < N; ++i) vm = fmaxf(vm, v[u][i]);
+        m_run = fmaxf(m_run, vm);
+        const bool act = j0 + u * B + t < n_full;
+        cmask |= (act && vm >= thr) ? (1u << u) : 0u;
+      }
+      s_t *= exp2_fast((m_t - m_run) * c);
+      m_t = m_run;
+#pragma unroll
+      for (int u = 0; u < kRU; ++u)
+#pragma unroll
+        for (int i = 0; i < N; ++i) s_t += exp2_fast((v[u][i] - m_t) * c);
+      if (cmask) {
+#pragma unroll
+        for (int u = 0; u < kRU; ++u) {
+          if (!((cmask >> u) & 1u)) continue;
+          float x[N];
+          IO::unpack(r[u], x);
+          uint32_t em = 0u;
+#pragma unroll
+          for (int i = 0; i < N; ++i) em |= (x[i] >= thr) ? (1u << i) : 0u;
+          const int jv = j0 + u * B + t;
+          for (; em; em &= em - 1u) {
+            const int i = __builtin_ctz(em);
+            push(elem_rt(r[u], i), jv * N + i);
+          }
+        }
       }
     };
 
@@ -270,13 +302,7 @@ void k_record(RecParams P) {
         b_w = b0;
         thr = bin_floor(b_w);
       }
-#pragma unroll
-      for (int u = 0; u < kRU; ++u) {
-        const int j = j0 + u * B + t;
-        float v[N];
-        IO::unpack(r[u], v);
-        vec(v, j, j < n_full);
-      }
+      tile(r, j0);
     }
     // the partial last vector (vocab not a multiple of N): its owner lane
     if (rem > 0) {
