@@ -117,15 +117,16 @@ void k_record(RecParams P) {
     __syncthreads();
 
     // ------------------------------------------------ exact bin of the k-th key
-    // Thread t sums bins [kNBins - PER (t + 1), kNBins - PER t); a block scan
-    // in thread order (descending bins) finds the bin where the count from the
-    // top reaches `need`; returns it and the count strictly above it.
+    // Thread t sums bins [lo, lo + PER), lo = kNBins - PER (t + 1); a block
+    // scan in thread order (descending bins) finds the bin where the count
+    // from the top reaches `need`; returns it and the count strictly above it.
+    // (Bins are addressed as lo + q, one base register plus constant offsets.)
     constexpr int PER = kNBins / B;
     auto find_kth = [&](int need, int& bin_out, int& above_out) {
-      const int hi = kNBins - PER * t - 1;
+      const int lo = kNBins - PER * (t + 1);
       int sum = 0;
 #pragma unroll
-      for (int q = 0; q < PER; ++q) sum += (int)hist[hi - q];
+      for (int q = 0; q < PER; ++q) sum += (int)hist[lo + q];
       int x = sum;
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
@@ -140,9 +141,10 @@ void k_record(RecParams P) {
       const int incl = wave_off + x, excl = incl - sum;
       if (excl < need && incl >= need) {
         int acc = excl;
-        for (int q = 0; q < PER; ++q) {
-          const int h = (int)hist[hi - q];
-          if (acc + h >= need) { sh_i[0] = hi - q; sh_i[1] = acc; break; }
+#pragma unroll 1
+        for (int q = PER - 1; q >= 0; --q) {   // one thread, once per call
+          const int h = (int)hist[lo + q];
+          if (acc + h >= need) { sh_i[0] = lo + q; sh_i[1] = acc; break; }
           acc += h;
         }
       }
@@ -155,9 +157,16 @@ void k_record(RecParams P) {
     int b_w = 0;            // wave-uniform lower bound on the k-th key's bin
     float thr = -INFINITY;  // bin_floor(b_w)
 
-    // Raise b_w from the histogram (bins from the highest counted one down
-    // to b_w) and drop buffered keys below it.  Wave-local; counts that other
-    // waves are still adding only make the bound lower (still valid).
+    // Raise b_w from the histogram and drop buffered keys below it.
+    // Wave-local; counts that other waves are still adding only make the
+    // bound lower (still valid: every count read is part of the final one).
+    // Logits of both signs leave long runs of empty bins between them (the
+    // small magnitudes), so the scan is two-level: each lane sums one group
+    // of 32 bins (64 groups, 2,048 bins per step, from the highest bin any
+    // wave has reported down to b_w's group); a wave scan finds the group
+    // where the count from the top reaches k, then a scan of that group's
+    // bins finds the bin.
+    constexpr int kGB = 32;                      // bins per group
     auto refresh = [&]() {
       const int cnt = (int)__atomic_load_n(&wcnt[w], __ATOMIC_RELAXED);
       if (cnt > cap) return;                     // overflowed: the row takes the fallback
@@ -167,16 +176,42 @@ void k_record(RecParams P) {
       const float wm = wave_max(m_t);
       if (lane == 0) atomicMax(&sh_u[4], (unsigned)bin_of(okey(wm)));
       const int top0 = (int)__atomic_load_n(&sh_u[4], __ATOMIC_RELAXED);
-      for (int top = top0; top >= b_w && found < 0; top -= kWave) {
-        const int bin = top - lane;
-        int x = bin >= b_w ? (int)__atomic_load_n(&hist[bin], __ATOMIC_RELAXED) : 0;
+      const int gw = b_w / kGB;
+      for (int g0 = top0 / kGB; g0 >= gw && found < 0; g0 -= kWave) {
+        const int g = g0 - lane;
+        int gs = 0;
+        if (g >= gw) {
+          // 16-byte reads, the chunk order rotated by lane (fewer bank conflicts)
+          const uint4* hp = reinterpret_cast<const uint4*>(hist + g * kGB);
 #pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {   // inclusive scan, lane 0 = top bin
+          for (int q = 0; q < kGB / 4; ++q) {
+            const uint4 v4 = hp[(q + lane) & (kGB / 4 - 1)];
+            gs += (int)(v4.x + v4.y + v4.z + v4.w);
+          }
+        }
+        int x = gs;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {   // inclusive scan, lane 0 = top group
           const int y = __shfl_up(x, o);
           if (lane >= o) x += y;
         }
         const unsigned long long hit = __ballot(total + x >= K);
-        if (hit) found = top - __builtin_ctzll(hit);
+        if (hit) {
+          const int lg = __builtin_ctzll(hit);
+          const int grp = g0 - lg;
+          const int above = total + __shfl(x - gs, lg);   // counted above the group
+          // lane i < 32 takes bin grp * 32 + 31 - i (descending)
+          int y = lane < kGB ? (int)__atomic_load_n(&hist[grp * kGB + kGB - 1 - lane],
+                                                    __ATOMIC_RELAXED) : 0;
+#pragma unroll
+          for (int o = 1; o < kGB; o <<= 1) {
+            const int yy = __shfl_up(y, o);
+            if (lane >= o) y += yy;
+          }
+          // counts only grow, so the group's bins reach k again
+          const unsigned long long hit2 = __ballot(lane < kGB && above + y >= K);
+          found = hit2 ? grp * kGB + kGB - 1 - __builtin_ctzll(hit2) : -1;
+        }
         total += __shfl(x, kWave - 1);
       }
       if (found > b_w) {
