@@ -48,7 +48,7 @@ constexpr int kHBits = 12;               // histogram bits of the key
 constexpr int kNBins = 1 << kHBits;
 constexpr int kSortMax = 2048;           // sort array (overlays the histogram)
 constexpr int kRU = SC_RECORD_TILE;      // vectors per thread per iteration
-constexpr int kRankMax = 64;             // candidate sets ordered by rank (O(n^2))
+constexpr int kRankMax = kRB;            // candidate sets ordered by rank (O(n^2))
 static_assert(kSortMax * 8 == kNBins * 4, "sort array overlays the histogram");
 
 // Monotone unsigned key of a float (NaN excluded by the caller); -0 -> +0.
@@ -446,10 +446,20 @@ void k_record(RecParams P) {
     unsigned long long* ord = reinterpret_cast<unsigned long long*>(lds + kNBins * 4);
     const bool by_rank = n_cand <= kRankMax;
     if (by_rank) {
+      // zero keys pad the set to a multiple of 4 (a zero key is below every
+      // real one), so every thread reads it 32 bytes at a time
+      const int n4 = (n_cand + 3) & ~3;
+      if (t < n4 - n_cand) sarr[n_cand + t] = 0ull;
+      __syncthreads();
       for (int i = t; i < n_cand; i += B) {
         const unsigned long long ki = sarr[i];
         int rank = 0;
-        for (int j2 = 0; j2 < n_cand; ++j2) rank += sarr[j2] > ki ? 1 : 0;
+        for (int j2 = 0; j2 < n4; j2 += 4) {
+          const ulonglong2 a0 = *reinterpret_cast<const ulonglong2*>(sarr + j2);
+          const ulonglong2 a1 = *reinterpret_cast<const ulonglong2*>(sarr + j2 + 2);
+          rank += (a0.x > ki ? 1 : 0) + (a0.y > ki ? 1 : 0) + (a1.x > ki ? 1 : 0) +
+                  (a1.y > ki ? 1 : 0);
+        }
         if (rank < K) ord[rank] = ki;
       }
       __syncthreads();
