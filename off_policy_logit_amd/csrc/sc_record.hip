@@ -310,9 +310,9 @@ void k_record(RecParams P) {
 #pragma unroll
       for (int u = 0; u < kRU; ++u) r[u] = nx[u];
       if (j0 + B * kRU < n_full) load_tile(nx, j0 + B * kRU);
-      if (iter > 0 && (iter < 4 || (iter & (iter + 1)) == 0 ||
+      if (iter > 0 && ((iter & (iter + 1)) == 0 ||
                        (int)__atomic_load_n(&wcnt[w], __ATOMIC_RELAXED) > cap / 2))
-        refresh();                             // tiles 1-3, 7, 15, ... or a filling buffer
+        refresh();                             // tiles 1, 3, 7, 15, ... or a filling buffer
       if (iter == 0 && K <= B) {
         // Initial bound: the k-th largest of the B per-thread maxima of this
         // tile is at most the row's k-th largest logit (they are k distinct
