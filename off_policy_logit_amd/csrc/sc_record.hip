@@ -17,7 +17,8 @@
 //     gives a valid lower bound), and the buffer is compacted to it.
 // After the stream the exact bin b* of the k-th largest key is read off the
 // histogram (exact above every b_w), the buffered keys at or above b* are
-// sorted (bitonic, LDS) and the first k are the record.  A row whose
+// ordered (by rank for at most 256 keys, else a bitonic sort in LDS) and the
+// first k are the record.  A row whose
 // candidates overflow a buffer or the sort array (heavy ties) takes the exact
 // fallback: radix selection over the remaining key bits with further passes
 // over the row, at most five, then one collection pass.  A wave whose buffer
