@@ -8,17 +8,14 @@
 namespace sc {
 
 // Launch shape of each row kernel (compile-time; overridable for sweeps):
-// threads per workgroup, 16-byte vectors per thread per tile, resident
-// workgroups per compute unit, and the occupancy target (waves per SIMD, which
-// caps VGPRs at 512 / value).
+// threads per workgroup, 16-byte vectors per thread per tile, and the
+// occupancy target (waves per SIMD, which caps VGPRs at 512 / value).  The
+// grid has one workgroup per row.
 #ifndef SC_STATS_BLOCK
 #define SC_STATS_BLOCK 256
 #endif
 #ifndef SC_STATS_TILE
 #define SC_STATS_TILE 8
-#endif
-#ifndef SC_STATS_WGS
-#define SC_STATS_WGS 8
 #endif
 #ifndef SC_STATS_WAVES
 #define SC_STATS_WAVES 4
@@ -29,9 +26,6 @@ namespace sc {
 #ifndef SC_CENTER_TILE
 #define SC_CENTER_TILE 8
 #endif
-#ifndef SC_CENTER_WGS
-#define SC_CENTER_WGS 4
-#endif
 #ifndef SC_CENTER_WAVES
 #define SC_CENTER_WAVES 4
 #endif
@@ -41,14 +35,10 @@ namespace sc {
 #ifndef SC_FUSED_TILE
 #define SC_FUSED_TILE 8
 #endif
-#ifndef SC_FUSED_WGS
-#define SC_FUSED_WGS 4
-#endif
 #ifndef SC_FUSED_WAVES
 #define SC_FUSED_WAVES 4
 #endif
 constexpr int kKindBlock[3] = {SC_STATS_BLOCK, SC_CENTER_BLOCK, SC_FUSED_BLOCK};
-constexpr int kKindWgs[3] = {SC_STATS_WGS, SC_CENTER_WGS, SC_FUSED_WGS};
 
 // Everything a row kernel needs, passed by value.
 struct RowParams {
@@ -171,7 +161,7 @@ struct RecParams {
   int cap;               // per-wave candidate buffer (set by the launcher)
 };
 size_t record_lds_bytes(int k);
-hipError_t launch_record(RecParams P, int cus, hipStream_t s);
+hipError_t launch_record(RecParams P, hipStream_t s);
 hipError_t launch_group_norm(const float* r, int n_groups, int G, int mode,
                              float eps, float* adv, hipStream_t s);
 hipError_t launch_count_valid(const int32_t* resp, int64_t n, int64_t* out,

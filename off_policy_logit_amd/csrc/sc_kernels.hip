@@ -5,7 +5,8 @@
 // proportional to the trainer policy), section "Training" (group standard
 // deviation normalisation), and the rollout_corr/k3_kl diagnostic.
 //
-// One workgroup owns one logits row at a time (persistent grid over rows).
+// One workgroup per logits row (the kernel also loops over rows when the grid
+// is smaller than the row count).
 // Per row:
 //   stage     recorded ids -> LDS id set (id -> slot) and a bitmap over the
 //             row's 16-byte vectors marking those that hold a recorded id or

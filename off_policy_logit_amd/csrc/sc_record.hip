@@ -5,7 +5,7 @@
 // sampling call, keeping their normalisation, and the sampled token's
 // log-probability separately).
 //
-// One workgroup per row (persistent grid).  Candidates are ordered by the
+// One workgroup per row.  Candidates are ordered by the
 // 64-bit key (order(z) << 32 | ~id): larger logit first, equal logits by
 // lower id, every key distinct.  The row is streamed once:
 //   * online max and sum of 2^((z - m) c) give the row's log-sum-exp;
@@ -525,20 +525,18 @@ size_t record_lds_bytes(int k) {
   return (size_t)kNBins * 4 + (size_t)kRNW * record_cap(k) * 8;
 }
 
-// Persistent grid: resident workgroups per CU from the occupancy query
-// (registers and LDS), times the CU count, at most one per row.
-hipError_t launch_record(RecParams P, int cus, hipStream_t s) {
+// One workgroup per row: rows take different times (their candidate
+// counts differ), and the hardware's dispatch of the next workgroup to
+// whichever slot frees up balances them (a persistent grid of the resident
+// count, rows assigned in turn, took 10% longer).
+hipError_t launch_record(RecParams P, hipStream_t s) {
   P.cap = record_cap(P.k);
   const size_t lds = record_lds_bytes(P.k);
   auto go = [&](auto kern) -> hipError_t {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    int per_cu = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kRB, lds);
-    if (e != hipSuccess) return e;
-    const int64_t grid = std::min<int64_t>(P.n_rows, (int64_t)cus * std::max(1, per_cu));
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kRB), lds, s, P);
+    hipLaunchKernelGGL(kern, dim3((unsigned)P.n_rows), dim3(kRB), lds, s, P);
     return hipGetLastError();
   };
   if (P.in_dtype == 1)
