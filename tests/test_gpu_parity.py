@@ -558,3 +558,19 @@ def test_full_vocabulary_fp32_and_k1024(dtype, K, T):
     assert int(out["status"].item()) == 0
     check_rows(f"full-V {dtype} K={K}", d, out, np.arange(n), adv.cpu().numpy(), n, T,
                O.MODE_DLOGITS, "bf16", logits_h=z)
+
+
+def test_many_rows_one_workgroup_each():
+    """200,003 short rows: the grid has one workgroup per row, far past
+    65,535; the first, the last and sampled rows against the oracle."""
+    n, V, K = 200_003, 72, 8
+    say(f"many rows n={n} V={V} K={K} bf16")
+    d, z = crafted(n, V, K, seed=17, dtype="bf16")
+    adv = torch.linspace(-1.5, 1.5, n // 4 + 1, device=DEV)
+    n_valid = sc.count_valid(d["resp_idx"])
+    out = run_correct(d, adv, n_valid, 1.0, O.MODE_SCORE, "bf16")
+    torch.cuda.synchronize()
+    assert int(out["status"].item()) == 0
+    rows = sample_rows(n, 40, 23, extra=(0, 1, n - 2, n - 1))
+    check_rows("many rows", d, out, rows, adv.cpu().numpy(), n, 1.0, O.MODE_SCORE, "bf16",
+               logits_h=z[rows], min_equal=0.99)

@@ -185,3 +185,20 @@ def test_record_sign_and_magnitude_regimes(dtype, k):
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     check(f"regimes {dtype} k={k}", host(zt), 1.0, k, sampled, out)
+
+
+def test_record_many_rows():
+    """200,003 short rows (one workgroup each, a grid far past 65,535)."""
+    n, V, k = 200_003, 300, 16
+    rng = np.random.default_rng(31)
+    z = rng.normal(0, 2, (n, V)).astype(np.float32)
+    sampled = rng.integers(0, V, n).astype(np.int32)
+    say(f"record many rows n={n} V={V} k={k}")
+    zt = torch.from_numpy(z).to(DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = sc.record(zt, k, sampled=torch.from_numpy(sampled).to(DEV), dev_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    rows = np.unique(np.concatenate([rng.choice(n, 40, replace=False), [0, 1, n - 2, n - 1]]))
+    sub = torch.as_tensor(rows, device=DEV)
+    check("many rows", z[rows], 1.0, k, sampled[rows], out, rows=rows)
