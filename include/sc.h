@@ -52,7 +52,7 @@ extern "C" {
 enum sc_status {
   SC_OK = 0,
   SC_ERR_ARG = -1,          /* invalid argument (checked before any HIP call) */
-  SC_ERR_UNSUPPORTED = -2,  /* valid but outside what this build supports      */
+  SC_ERR_UNSUPPORTED = -2,  /* valid but outside what the library supports    */
   SC_ERR_HIP = -3           /* a HIP runtime call or kernel launch failed       */
 };
 

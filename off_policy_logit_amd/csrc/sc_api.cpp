@@ -627,7 +627,7 @@ const char* sc_status_string(int status) {
   switch (status) {
     case SC_OK: return "SC_OK";
     case SC_ERR_ARG: return "SC_ERR_ARG: invalid argument";
-    case SC_ERR_UNSUPPORTED: return "SC_ERR_UNSUPPORTED: outside what this build supports";
+    case SC_ERR_UNSUPPORTED: return "SC_ERR_UNSUPPORTED: outside what the library supports";
     case SC_ERR_HIP: return "SC_ERR_HIP: HIP runtime call or kernel launch failed";
     default: return "unknown sc_status";
   }
