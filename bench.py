@@ -295,6 +295,25 @@ def main():
     torch.cuda.synchronize()
     stats_ms = e0.elapsed_time(e1) / reps
 
+    # two-call path: sc_logprobs, then sc_center streaming the logits again
+    # for the dLogits row (the same outputs as the fused kernel)
+    def two_call():
+        sc.logprobs(d["logits"], d["head_ids"], d["sampled"], d["resp_idx"], out=st)
+        sc.center(st, d["head_ids"], d["head_probs"], d["sampled"], d["resp_idx"], adv,
+                  n_valid=n_valid, rollout_logp=d["rollout_logp"], logits=d["logits"],
+                  row_out=dlogits, row_mode=sc.ROW_DLOGITS, coef=coef, dev_status=status)
+    for _ in range(2):
+        two_call()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        two_call()
+    e1.record()
+    torch.cuda.synchronize()
+    two_ms = e0.elapsed_time(e1) / reps
+    if int(status.item()) != 0:
+        raise RuntimeError(f"two-call device status {int(status.item())}")
+
     # rollout-side record (sc_record) on the same logits, secondary line
     rec = dict(head_ids=torch.empty(n, K, dtype=torch.int32, device=dev),
                head_probs=torch.empty(n, K, device=dev),
@@ -347,6 +366,8 @@ def main():
             "stats_only_positions_per_s": round(n / (stats_ms * 1e-3), 1),
             "stats_only_kernel_ms": round(stats_ms, 4),
             "stats_only_GBps": round(n * BYTES_PER_POSITION_STATS / (stats_ms * 1e-3) / 1e9, 1),
+            "two_call_positions_per_s": round(n / (two_ms * 1e-3), 1),
+            "two_call_ms": round(two_ms, 4),
             "record_positions_per_s": round(n / (rec_ms * 1e-3), 1),
             "record_kernel_ms": round(rec_ms, 4),
             "record_GBps": round(n * BYTES_PER_POSITION_RECORD / (rec_ms * 1e-3) / 1e9, 1),
