@@ -574,3 +574,19 @@ def test_many_rows_one_workgroup_each():
     rows = sample_rows(n, 40, 23, extra=(0, 1, n - 2, n - 1))
     check_rows("many rows", d, out, rows, adv.cpu().numpy(), n, 1.0, O.MODE_SCORE, "bf16",
                logits_h=z[rows], min_equal=0.99)
+
+
+@pytest.mark.parametrize("V", [1, 2, 7, 8, 9, 17])
+def test_tiny_vocabularies(V):
+    """Degenerate row lengths: fewer elements than one 16-byte vector, exactly
+    one, one plus a partial one; K up to V (K = V makes the tail empty)."""
+    for K in sorted({1, min(V, 3), V}):
+        say(f"tiny vocabulary V={V} K={K}")
+        d, z = crafted(16, V, K, seed=V * 7 + K, dtype="f32")
+        adv = torch.linspace(-1.0, 1.0, 4, device=DEV)
+        n_valid = sc.count_valid(d["resp_idx"])
+        out = run_correct(d, adv, n_valid, 1.0, O.MODE_SCORE, "f32")
+        torch.cuda.synchronize()
+        assert int(out["status"].item()) == 0
+        check_rows(f"tiny V={V} K={K}", d, out, np.arange(16), adv.cpu().numpy(), 16, 1.0,
+                   O.MODE_SCORE, "f32", logits_h=z)

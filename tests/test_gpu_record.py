@@ -202,3 +202,16 @@ def test_record_many_rows():
     rows = np.unique(np.concatenate([rng.choice(n, 40, replace=False), [0, 1, n - 2, n - 1]]))
     sub = torch.as_tensor(rows, device=DEV)
     check("many rows", z[rows], 1.0, k, sampled[rows], out, rows=rows)
+
+
+@pytest.mark.parametrize("V", [1, 2, 7, 8, 9, 17])
+def test_record_tiny_vocabularies(V):
+    rng = np.random.default_rng(V)
+    z = rng.normal(0, 2, (16, V)).astype(np.float32)
+    sampled = rng.integers(0, V, 16).astype(np.int32)
+    for k in sorted({1, min(V, 3), V}):
+        say(f"record tiny vocabulary V={V} k={k}")
+        out = sc.record(torch.from_numpy(z).to(DEV), k,
+                        sampled=torch.from_numpy(sampled).to(DEV))
+        torch.cuda.synchronize()
+        check(f"tiny V={V} k={k}", z, 1.0, k, sampled, out)
