@@ -295,6 +295,19 @@ def main():
     torch.cuda.synchronize()
     stats_ms = e0.elapsed_time(e1) / reps
 
+    # reference rate of the memory system for the same traffic shape: a plain
+    # device copy of the logits into the dLogits buffer (reads and writes the
+    # fused kernel's algorithmic bytes, with no arithmetic)
+    dlogits.copy_(d["logits"])
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dlogits.copy_(d["logits"])
+    e1.record()
+    torch.cuda.synchronize()
+    copy_ms = e0.elapsed_time(e1) / reps
+    copy_bytes = 2 * d["logits"].numel() * d["logits"].element_size()
+
     # two-call path: sc_logprobs, then sc_center streaming the logits again
     # for the dLogits row (the same outputs as the fused kernel)
     def two_call():
@@ -366,6 +379,8 @@ def main():
             "stats_only_positions_per_s": round(n / (stats_ms * 1e-3), 1),
             "stats_only_kernel_ms": round(stats_ms, 4),
             "stats_only_GBps": round(n * BYTES_PER_POSITION_STATS / (stats_ms * 1e-3) / 1e9, 1),
+            "copy_same_bytes_ms": round(copy_ms, 4),
+            "copy_GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1),
             "two_call_positions_per_s": round(n / (two_ms * 1e-3), 1),
             "two_call_ms": round(two_ms, 4),
             "record_positions_per_s": round(n / (rec_ms * 1e-3), 1),
