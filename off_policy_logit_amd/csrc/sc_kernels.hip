@@ -90,27 +90,10 @@ void k_row(RowParams P) {
 
   if (t == 0) sh_status = 0;
 
-  // The next row's response index, sampled id and (for K <= B) recorded ids
-  // are loaded one row ahead, so the stage does not wait on them.
-  int64_t row = blockIdx.x;
-  int nx_resp = 0, nx_a = 0, nx_id = -1;
-  if (row < P.n_rows) {
-    nx_resp = P.resp_idx ? P.resp_idx[row] : 0;
-    nx_a = P.sampled[row];
-    if (t < K) nx_id = P.head_ids[row * K + t];
-  }
-  for (; row < P.n_rows; row += gridDim.x) {
-    const int resp = nx_resp;
-    const int32_t a = nx_a;
-    const int my_id = nx_id;
-    {
-      const int64_t nr = row + gridDim.x;
-      if (nr < P.n_rows) {
-        nx_resp = P.resp_idx ? P.resp_idx[nr] : 0;
-        nx_a = P.sampled[nr];
-        if (t < K) nx_id = P.head_ids[nr * K + t];
-      }
-    }
+  for (int64_t row = blockIdx.x; row < P.n_rows; row += gridDim.x) {
+    const int resp = P.resp_idx ? P.resp_idx[row] : 0;
+    const int32_t a = P.sampled[row];
+    const int my_id = t < K ? P.head_ids[row * K + t] : -1;   // slot t (K <= B)
     float* stats = P.row_stats + row * C_N;
     int32_t* ridx = P.row_idx + row * 2;
 
