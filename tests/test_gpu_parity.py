@@ -590,3 +590,28 @@ def test_tiny_vocabularies(V):
         assert int(out["status"].item()) == 0
         check_rows(f"tiny V={V} K={K}", d, out, np.arange(16), adv.cpu().numpy(), 16, 1.0,
                    O.MODE_SCORE, "f32", logits_h=z)
+
+
+def test_seeded_random_shapes():
+    """24 seeded draws of (rows, V, K, dtype, stride, T, row mode, output
+    dtype), every row against the oracle."""
+    rng = np.random.default_rng(2026)
+    for case in range(24):
+        V = int(rng.choice([5, 33, 257, 1000, 2049, 4096, 7001, 12289]))
+        K = int(min(V, rng.choice([1, 2, 16, 64, 128, 200, 300])))
+        n = int(rng.choice([1, 3, 16, 37, 64]))
+        dtype = str(rng.choice(["bf16", "f32"]))
+        stride = None if rng.random() < 0.6 else V + int(rng.integers(1, 9))
+        T = float(rng.choice([1.0, 0.7, 1.3]))
+        mode = int(rng.choice([O.MODE_DLOGITS, O.MODE_SCORE, O.MODE_CORRECTION]))
+        out_dtype = str(rng.choice(["bf16", "f32"]))
+        tag = f"random {case}: n={n} V={V} K={K} {dtype} stride={stride} T={T} mode={mode} out={out_dtype}"
+        say(tag)
+        d, z = crafted(n, V, K, seed=case, dtype=dtype, stride=stride)
+        adv = torch.linspace(-1.2, 1.3, (n + 3) // 4, device=DEV)
+        n_valid = sc.count_valid(d["resp_idx"])
+        out = run_correct(d, adv, n_valid, T, mode, out_dtype)
+        torch.cuda.synchronize()
+        assert int(out["status"].item()) == 0
+        check_rows(tag, d, out, np.arange(n), adv.cpu().numpy(), n, T, mode, out_dtype,
+                   logits_h=z, min_equal=0.98 if V < 300 else 0.995)

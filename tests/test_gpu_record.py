@@ -215,3 +215,25 @@ def test_record_tiny_vocabularies(V):
                         sampled=torch.from_numpy(sampled).to(DEV))
         torch.cuda.synchronize()
         check(f"tiny V={V} k={k}", z, 1.0, k, sampled, out)
+
+
+def test_record_seeded_random_shapes():
+    """24 seeded draws of (rows, V, k, dtype, stride, T), every row against
+    the oracle."""
+    rng = np.random.default_rng(2027)
+    for case in range(24):
+        V = int(rng.choice([5, 33, 257, 1000, 2049, 4096, 7001, 12289]))
+        k = int(min(V, rng.choice([1, 8, 128, 256, 300])))
+        n = int(rng.choice([1, 3, 16, 37]))
+        dtype = torch.bfloat16 if rng.random() < 0.5 else torch.float32
+        stride = V if rng.random() < 0.6 else V + int(rng.integers(1, 9))
+        T = float(rng.choice([1.0, 0.7, 1.3]))
+        say(f"record random {case}: n={n} V={V} k={k} {dtype} stride={stride} T={T}")
+        z = rng.normal(0, float(rng.choice([0.5, 2.0, 6.0])), (n, V)).astype(np.float32)
+        buf = torch.zeros(n, stride, dtype=dtype, device=DEV)
+        buf[:, :V] = torch.from_numpy(z).to(DEV).to(dtype)
+        zt = buf[:, :V]
+        sampled = rng.integers(0, V, n).astype(np.int32)
+        out = sc.record(zt, k, sampled=torch.from_numpy(sampled).to(DEV), temperature=T)
+        torch.cuda.synchronize()
+        check(f"random {case}", host(zt), T, k, sampled, out)
