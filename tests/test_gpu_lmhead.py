@@ -201,3 +201,24 @@ def test_lmhead_more_rows_than_vocabulary():
         o = O.sc_row(zh[r], T, idh[r], qh[r], ah[r])
         check_row(f"rows>ids row {r}", dict(stats=st[r], idx=ix[r], head_logp=hl[r]), o,
                   stats_only=True)
+
+
+def test_lmhead_logits_seeded_random_shapes():
+    """12 seeded draws of (rows, V, d, row padding): the GEMM against the
+    float64 product (grid order and split count vary with the shape)."""
+    rng = np.random.default_rng(404)
+    for case in range(12):
+        n = int(rng.choice([1, 7, 255, 256, 257, 700, 1300]))
+        V = int(rng.choice([1, 63, 256, 257, 999, 2305, 5000]))
+        d = int(rng.choice([64, 128, 320, 1024]))
+        pad = int(rng.choice([0, 8, 64]))
+        say(f"lmhead random {case}: n={n} V={V} d={d} pad={pad}")
+        w_full = (torch.randn(V, d + pad, generator=gen(10 + case), device=DEV) * 0.05).to(torch.bfloat16)
+        x_full = torch.randn(n, d + pad, generator=gen(50 + case), device=DEV).to(torch.bfloat16)
+        w, x = w_full[:, :d], x_full[:, :d]
+        z = sc.lmhead_logits(x, w)
+        torch.cuda.synchronize()
+        xh, wh = x.float().cpu().numpy(), w.float().cpu().numpy()
+        err = np.abs(z.cpu().numpy().astype(np.float64) - O.lmhead_logits(xh, wh))
+        tol = product_bound(xh, wh, d)
+        assert np.all(err <= tol), (case, float(err.max()), float((err - tol).max()))
