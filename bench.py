@@ -132,6 +132,54 @@ def cpu_baseline(rows, min_seconds=10.0, max_passes=200):
 # ---------------------------------------------------------------------------
 # GPU
 # ---------------------------------------------------------------------------
+def full_step_measure(dev, reps):
+    """One 16,384-position chunk of the full-step workload (4 responses x
+    4,096 tokens, lengths uniform in [256, 4,096], the rest padding): exact
+    count, the fused kernel with bf16 dLogits, step sums, timed together."""
+    import torch
+    import synthetic
+    from off_policy_logit_amd import sc
+    lengths = synthetic.full_step_lengths()
+    c = synthetic.full_step_chunk(dev, 0, lengths)
+    rows = c["logits"].shape[0]
+    n_valid = torch.empty(1, dtype=torch.int64, device=dev)
+    sc.count_valid(c["resp_idx"], out=n_valid)
+    valid = int(n_valid.item())
+    g = torch.Generator().manual_seed(12)
+    adv = torch.randn(int(c["resp_idx"].max().item()) + 1, generator=g).to(dev)
+    dz = torch.empty_like(c["logits"])
+    batch = torch.empty(sc.NBATCH, dtype=torch.float64, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = sc.correct(c["logits"], c["head_ids"], c["head_probs"], c["sampled"], c["resp_idx"],
+                     adv, n_valid=n_valid, rollout_logp=c["rollout_logp"], row_out=dz,
+                     dev_status=status)
+
+    def run():
+        sc.count_valid(c["resp_idx"], out=n_valid)
+        sc.correct(c["logits"], c["head_ids"], c["head_probs"], c["sampled"], c["resp_idx"],
+                   adv, n_valid=n_valid, rollout_logp=c["rollout_logp"], row_out=dz,
+                   out=out, coef=out["coef"], dev_status=status)
+        sc.batch_sums(out["row_stats"], c["resp_idx"], n_valid, out=batch)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError(f"full-step device status {int(status.item())}")
+    ms = e0.elapsed_time(e1) / reps
+    # valid rows move the fused kernel's bytes; padding rows only write a zero row
+    bytes_ = valid * BYTES_PER_POSITION + (rows - valid) * (2 * VOCAB + 8 * K + 72)
+    del c, dz, out
+    torch.cuda.empty_cache()
+    return {"workload": f"full-step chunk 0: {rows} positions, {valid} valid, V={VOCAB}, K={K}",
+            "ms": round(ms, 4), "valid_positions_per_s": round(valid / (ms * 1e-3), 1),
+            "GBps": round(bytes_ / (ms * 1e-3) / 1e9, 1)}
+
+
 def lmhead_measure(dev, reps):
     """Fused LM-head statistics (sc_logprobs_lmhead) on a 16,384-row slice at
     V = 248,320, d = 4,096: event-timed average of the three kernels, in
@@ -343,6 +391,7 @@ def main():
     if int(status.item()) != 0:
         raise RuntimeError(f"record device status {int(status.item())}")
 
+    full = full_step_measure(dev, max(5, args.steps // 5))
     lm = None if args.no_lmhead else lmhead_measure(dev, max(3, args.steps // 10))
 
     bytes_launch = n * BYTES_PER_POSITION
@@ -386,6 +435,7 @@ def main():
             "record_positions_per_s": round(n / (rec_ms * 1e-3), 1),
             "record_kernel_ms": round(rec_ms, 4),
             "record_GBps": round(n * BYTES_PER_POSITION_RECORD / (rec_ms * 1e-3) / 1e9, 1),
+            "full_step_chunk": full,
             "lmhead": lm,
         },
     }

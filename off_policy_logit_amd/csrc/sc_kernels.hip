@@ -114,9 +114,17 @@ void k_row(RowParams P) {
         if (KIND != KIND_CENTER && P.head_logp) P.head_logp[row * K + k] = 0.f;
         if (KIND != KIND_LOGPROBS && P.coef) P.coef[row * K + k] = 0.f;
       }
-      if (has_out) {
+      if (has_out) {   // a zero row, in whole vectors where the row allows
         TO* orow = reinterpret_cast<TO*>(P.row_out) + row * P.out_stride;
-        for (int i = t; i < V; i += B) store_elem(orow, i, 0.f);
+        int i0 = 0;
+        if (VECTOR) {
+          float zero[N];
+#pragma unroll
+          for (int i = 0; i < N; ++i) zero[i] = 0.f;
+          for (int j = t; j < n_full; j += B) RowOut<TO, N>::store(orow, j, zero);
+          i0 = n_full * N;
+        }
+        for (int i = i0 + t; i < V; i += B) store_elem(orow, i, 0.f);
       }
       continue;
     }
