@@ -615,3 +615,24 @@ def test_seeded_random_shapes():
         assert int(out["status"].item()) == 0
         check_rows(tag, d, out, np.arange(n), adv.cpu().numpy(), n, T, mode, out_dtype,
                    logits_h=z, min_equal=0.98 if V < 300 else 0.995)
+
+
+@pytest.mark.parametrize("dtype,out_dtype", [("f32", "f32"), ("f32", "bf16"), ("bf16", "f32")])
+def test_padding_rows_every_output_layout(dtype, out_dtype):
+    """Padding rows (resp_idx = -1) write an all-zero row in every input /
+    output dtype pair (16-byte vector zero fill), next to valid rows that
+    match the oracle."""
+    n, V, K = 24, 4099, 32
+    say(f"padding rows {dtype} -> {out_dtype}")
+    d, z = crafted(n, V, K, seed=61, dtype=dtype)
+    resp = d["resp_idx"].clone()
+    resp[1::3] = -1
+    d["resp_idx"] = resp
+    adv = torch.linspace(-1.0, 1.0, n // 4, device=DEV)
+    n_valid = sc.count_valid(d["resp_idx"])
+    out = run_correct(d, adv, n_valid, 1.0, O.MODE_DLOGITS, out_dtype)
+    torch.cuda.synchronize()
+    assert int(out["status"].item()) == 0
+    assert int(n_valid.item()) == n - len(range(1, n, 3))
+    check_rows(f"padding {dtype}->{out_dtype}", d, out, np.arange(n), adv.cpu().numpy(),
+               int(n_valid.item()), 1.0, O.MODE_DLOGITS, out_dtype, logits_h=z)
