@@ -633,6 +633,6 @@ const char* sc_status_string(int status) {
   }
 }
 
-int sc_version(void) { return 100; }
+int sc_version(void) { return 101; }
 
 }  // extern "C"

@@ -763,14 +763,11 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restri
   }
 }
 
+// Set on every launch: no cached flag, so concurrent callers share no state.
 template <int MODE>
 hipError_t set_lds_attr() {
-  static bool done = false;
-  if (done) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lm_main<MODE>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-  if (e == hipSuccess) done = true;
-  return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lm_main<MODE>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
 }
 
 }  // namespace
