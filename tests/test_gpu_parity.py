@@ -385,6 +385,45 @@ def test_count_valid_and_batch_sums():
     assert b[B("max_w")] == np.float32(means["max_w"])
 
 
+def test_empty_chunks_in_the_step_reductions():
+    """A chunk with no rows adds nothing to the count or the step sums, and a
+    fresh (non-accumulating) pass over no rows gives what the oracle's step
+    reduction gives over an empty set: zero count and sums, no maximum
+    weight."""
+    say("count_valid / batch_sums with empty chunks")
+    rng = np.random.default_rng(12)
+    n = 3000
+    resp = torch.from_numpy(rng.integers(-1, 5, n).astype(np.int32)).to(DEV)
+    st = torch.from_numpy(rng.normal(0, 1, (n, sc.NSTATS)).astype(np.float32)).to(DEV)
+    st[:, sc.STAT["w"]] = st[:, sc.STAT["w"]].exp()
+    no_resp = torch.empty(0, dtype=torch.int32, device=DEV)
+    no_st = torch.empty(0, sc.NSTATS, device=DEV)
+
+    nv = torch.full((1,), 77, dtype=torch.int64, device=DEV)
+    sc.count_valid(no_resp, out=nv)
+    assert int(nv.item()) == 0
+    sc.count_valid(resp, out=nv, accumulate=True)
+    expect = int((resp >= 0).sum().item())
+    sc.count_valid(no_resp, out=nv, accumulate=True)
+    assert int(nv.item()) == expect
+
+    one = sc.batch_sums(st, resp, nv)
+    both = sc.batch_sums(st, resp, nv)
+    sc.batch_sums(no_st, no_resp, nv, out=both, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(one, both)
+
+    fresh = torch.full((sc.NBATCH,), 5.0, dtype=torch.float64, device=DEV)
+    sc.batch_sums(no_st, no_resp, nv, out=fresh)
+    f = fresh.cpu().numpy()
+    sums, means = O.batch_sums([], expect)
+    B = sc.BATCH.index
+    assert f[B("rows")] == 0 and f[B("flagged")] == 0
+    assert f[B("max_w")] == means["max_w"]
+    for key in O.BATCH_KEYS:
+        assert f[B("sum_" + key)] == sums[key] and f[B("mean_" + key)] == means[key], key
+
+
 # ---------------------------------------------------------------------------
 # Full-size workloads (V = 248,320), sampled rows
 # ---------------------------------------------------------------------------
