@@ -253,7 +253,16 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
 
+  // Issue priority: a wave raises its priority while it runs a stage's
+  // fragment reads and MFMAs, so that when the SIMD's other wave is in its
+  // loads, LDS stores or epilogue the MFMA stream is served first.  Per k
+  // step, one of the compiler's strategies for interleaving LDS reads with
+  // MFMAs replaces its default order (strategy 0 for the statistics kernel,
+  // 1 for the store epilogues: the faster of the two for each).  Together
+  // they made the 16,384-row slice 6-8% faster; the MFMA order, and so
+  // every result, is unchanged.
   auto compute = [&](int buf) {
+    __builtin_amdgcn_s_setprio(1);
     const unsigned char* A = lds + buf * 2 * kBuf + (wv * 128 + lc) * kPitch + h * 16;
     const unsigned char* Bm = lds + buf * 2 * kBuf + kBuf + (wp * kWR + lc) * kPitch + h * 16;
 #pragma unroll
@@ -270,7 +279,10 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      if constexpr (MODE == 0) __builtin_amdgcn_iglp_opt(0);
+      else __builtin_amdgcn_iglp_opt(1);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // ------------------------------------------------------------ row state
