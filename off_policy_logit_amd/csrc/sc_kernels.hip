@@ -44,6 +44,20 @@ enum { F_BAD_ID = 1, F_DUP_ID = 2, F_BAD_SAMPLED = 4, F_NONFINITE = 8, F_BAD_RES
 enum { M_DLOGITS = 0, M_SCORE = 1, M_CORRECTION = 2 };
 
 // kU: 16-byte vectors per thread per pipelined tile (divides 32).
+// Keep a when c, else b (whole raw vectors; selects, no branch).
+SC_DEV u32x4 keep_if(bool c, const u32x4& a, const u32x4& b) {
+  u32x4 o;
+  o.x = c ? a.x : b.x; o.y = c ? a.y : b.y; o.z = c ? a.z : b.z; o.w = c ? a.w : b.w;
+  return o;
+}
+SC_DEV f32x4 keep_if(bool c, const f32x4& a, const f32x4& b) {
+  f32x4 o;
+  o.x = c ? a.x : b.x; o.y = c ? a.y : b.y; o.z = c ? a.z : b.z; o.w = c ? a.w : b.w;
+  return o;
+}
+SC_DEV uint32_t keep_if(bool c, uint32_t a, uint32_t b) { return c ? a : b; }
+SC_DEV float keep_if(bool c, float a, float b) { return c ? a : b; }
+
 template <typename TI, typename TO, bool VECTOR, int B, int KIND, int kU, int WAVES>
 __global__ __launch_bounds__(B) __attribute__((amdgpu_waves_per_eu(WAVES)))
 void k_row(RowParams P) {
@@ -246,12 +260,14 @@ void k_row(RowParams P) {
       // the first of equal maxima is kept).
       float m_t = -FLT_MAX, s_t = 0.f, h_t = 0.f;
       int am_vec = -1;
+      Raw am_raw = IO::ninf();  // the vector that raised m_t, kept in registers
       int am_direct = -1;
-      auto vec_update = [&](const float (&v)[N], int j) {
+      auto vec_update = [&](const float (&v)[N], const Raw& rv, int j) {
         float vm = v[0];
 #pragma unroll
         for (int i = 1; i < N; ++i) vm = fmaxf(vm, v[i]);
         const float m_new = fmaxf(m_t, vm);
+        am_raw = keep_if(vm > m_t, rv, am_raw);
         am_vec = vm > m_t ? j : am_vec;
         const float r = exp2_fast((m_t - m_new) * c);
         h_t = r * (h_t - (m_new - m_t) * s_t);
@@ -289,6 +305,7 @@ void k_row(RowParams P) {
             float vm = v[u][0];
 #pragma unroll
             for (int i = 1; i < N; ++i) vm = fmaxf(vm, v[u][i]);
+            am_raw = keep_if(vm > m_run, r[u0 + u], am_raw);
             am_vec = vm > m_run ? j0 + u0 + u : am_vec;   // strictly: first of equal maxima
             m_run = fmaxf(m_run, vm);
           }
@@ -315,8 +332,9 @@ void k_row(RowParams P) {
         }
         for (int j = Jt; j < J; ++j) {
           float v[N];
-          IO::unpack(load_one(j, nt), v);
-          vec_update(v, j);
+          const Raw rv = load_one(j, nt);
+          IO::unpack(rv, v);
+          vec_update(v, rv, j);
           float acc, acch;
           vec_sums(v, acc, acch);
           const bool marked = (bitmap[(j >> 5) * B + t] >> (j & 31)) & 1u;
@@ -364,15 +382,14 @@ void k_row(RowParams P) {
         append(n_full, v);
       }
       // Element index of my maximum: the first element equal to m_t in the
-      // vector that raised it (read again, one vector per thread and row).
+      // vector that raised it (kept in registers during the stream).
       int am_t = 0x7fffffff;
       if (am_direct >= 0) {
         am_t = am_direct;
       } else if (am_vec >= 0) {
-        const Raw rv = IO::template load<false>(zrow, (int64_t)am_vec * B + t);
 #pragma unroll
         for (int i = N - 1; i >= 0; --i)
-          if (IO::elem(rv, i) == m_t) am_t = (int)((am_vec * B + t) * N + i);
+          if (IO::elem(am_raw, i) == m_t) am_t = (int)((am_vec * B + t) * N + i);
       }
 
       // ---------------------------------------------------------- finalize
