@@ -675,3 +675,45 @@ def test_padding_rows_every_output_layout(dtype, out_dtype):
     assert int(n_valid.item()) == n - len(range(1, n, 3))
     check_rows(f"padding {dtype}->{out_dtype}", d, out, np.arange(n), adv.cpu().numpy(),
                int(n_valid.item()), 1.0, O.MODE_DLOGITS, out_dtype, logits_h=z)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_argmax_ties_first_index(dtype):
+    """Equal maxima planted in one 16-byte vector, in two vectors of one
+    thread, across threads and in the partial last vector: the argmax is the
+    first of them (the oracle's smallest index of the maximum), from both
+    sc_logprobs and sc_correct."""
+    say(f"argmax ties dtype={dtype}")
+    rng = np.random.default_rng(21)
+    n, V, K = 48, 4099, 16
+    z = rng.normal(0, 1, (n, V)).astype(np.float32)
+    top = 8.0                                    # exact in bf16
+    N = 8 if dtype == "bf16" else 4              # elements per 16-byte vector
+    patterns = [(5, 6), (3, 3 + N * 256), (3, 3 + N * 384 + N), (N * 7 + 1, N * 7),
+                (V - 1, V - 2), (V - 3, 0), (1000, 1001, 1002), (2 * N, 2 * N + N * 300)]
+    for r in range(n):
+        for p in patterns[r % len(patterns)]:
+            z[r, p] = top
+    if dtype == "bf16":
+        zt = torch.from_numpy(z).to(torch.bfloat16)
+        zh = zt.float().numpy()
+    else:
+        zt = torch.from_numpy(z)
+        zh = z
+    ids = np.stack([rng.choice(V, K, replace=False) for _ in range(n)]).astype(np.int32)
+    q = rng.dirichlet(np.ones(K), n).astype(np.float32) * 0.9
+    a = rng.integers(0, V, n).astype(np.int32)
+    resp = np.zeros(n, dtype=np.int32)
+    d = to_dev(dict(logits=zt, head_ids=ids, head_probs=q, sampled=a, resp_idx=resp))
+    st = sc.logprobs(d["logits"], d["head_ids"], d["sampled"], d["resp_idx"])
+    adv = torch.ones(1, device=DEV)
+    nv = sc.count_valid(d["resp_idx"])
+    out = sc.correct(d["logits"], d["head_ids"], d["head_probs"], d["sampled"],
+                     d["resp_idx"], adv, n_valid=nv)
+    torch.cuda.synchronize()
+    got_s = st["row_idx"][:, 0].cpu().numpy()
+    got_c = out["row_idx"][:, 0].cpu().numpy()
+    for r in range(n):
+        o = O.sc_row(zh[r], 1.0, ids[r], q[r], a[r])
+        assert o["argmax"] == min(patterns[r % len(patterns)]), r
+        assert got_s[r] == o["argmax"] and got_c[r] == o["argmax"], (r, got_s[r], got_c[r], o["argmax"])
