@@ -101,7 +101,9 @@ enum sc_stat {
   SC_STAT_W = 12,       /* importance ratio w = p(a) / mu(a)                   */
   SC_STAT_WEIGHT = 13,  /* stop-gradient weight wt applied (sc_is_mode)        */
   SC_STAT_REV_KL = 14,  /* KL(p || mu_hat)                                     */
-  SC_STAT_RESERVED = 15,
+  SC_STAT_LSE_LO = 15,  /* LSE's float64 value minus its fp32 value: the two
+                           columns together carry the log-sum-exp to sc_center
+                           at double precision                               */
   SC_NSTATS = 16
 };
 
@@ -132,8 +134,8 @@ enum sc_batch {
  *                 padding; NULL means every row is valid
  *   temperature   T > 0; p = softmax(z / T)
  * Outputs (device, written for every row):
- *   row_stats     float [n_rows, SC_NSTATS]: columns LSE, LOGP_A, TAIL, P_H,
- *                 ENTROPY (the other columns are left untouched)
+ *   row_stats     float [n_rows, SC_NSTATS]: columns LSE, LSE_LO, LOGP_A, TAIL,
+ *                 P_H, ENTROPY (the other columns are left untouched)
  *   row_idx       int32 [n_rows, SC_NIDX]: argmax of the raw logits (lowest
  *                 index among equal maxima) and the slot k with H_k = a (-1 if
  *                 a is not recorded)
@@ -153,8 +155,10 @@ int sc_logprobs(const void* logits, int logits_dtype, int64_t n_rows,
  * Score Centering section: P_H, Q_H, rho, the token loss with stop-gradient
  * coefficients c = q - rho p on H, the tail proportional to p, global
  * generated-token reduction with padding masked; rollout_corr/k3_kl.
- * Reads row_stats columns LSE, LOGP_A, TAIL and row_idx / head_logp as written
- * by sc_logprobs on the same rows; writes columns P_H .. K3 and W .. REV_KL.
+ * Reads row_stats columns LSE, LSE_LO, LOGP_A, TAIL and row_idx / head_logp as
+ * written by sc_logprobs (or sc_logprobs_lmhead) on the same rows; writes
+ * columns P_H .. K3 and W .. REV_KL.  With row_out, the row maximum is read
+ * back from the logits at the recorded argmax.
  * When row_out is not NULL the logits are streamed once more to write it.
  *
  *   logits, logits_dtype, row_stride   as for sc_logprobs; may be NULL when

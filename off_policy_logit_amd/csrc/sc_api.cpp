@@ -45,7 +45,9 @@ int check_rows(sc::RowParams& P, const void* logits, bool logits_needed, int log
   P.k = k;
   P.sampled = sampled;
   P.temperature = temperature;
-  P.c = (float)(1.4426950408889634 / (double)temperature);
+  P.c64 = 1.4426950408889634 / (double)temperature;
+  P.c_hi = (float)P.c64;
+  P.c_lo = (float)(P.c64 - (double)P.c_hi);
   P.row_stats = row_stats;
   P.row_idx = row_idx;
   return SC_OK;
@@ -62,25 +64,15 @@ int layout(sc::RowParams& P, int kind) {
   while (hs < 2 * P.k) { hs <<= 1; ++hbits; }
   P.hs = hs;
   P.hshift = 32 - hbits;
-  P.ke = P.k + 2;
-  int vs = 2, vbits = 1;
-  while (vs < 2 * P.ke) { vs <<= 1; ++vbits; }
-  P.vs = vs;
-  P.vshift = 32 - vbits;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = (off + bytes + 15) & ~size_t(15); return (int)o; };
   P.off_bitmap = take((size_t)P.bm_wpt * B * 4);
   P.off_hkey = take((size_t)hs * 4);
   P.off_hval = take((size_t)hs * 4);
   P.off_headz = take((size_t)P.k * 4);
-  P.off_headp = take((size_t)P.k * 4);
+  P.off_headp = take((size_t)P.k * 8);
+  P.off_headlp = take((size_t)P.k * 8);
   P.off_hout = take((size_t)P.k * 4);
-  P.off_entvec = take((size_t)P.ke * 4);
-  P.off_entval = take((size_t)P.ke * N * 4);
-  P.off_entslot = take((size_t)P.ke * N * 4);
-  P.off_vkey = take((size_t)vs * 4);
-  P.off_vval = take((size_t)vs * 4);
-  P.off_hid = take((size_t)P.k * 4);
   P.lds_bytes = off;
   return off <= kMaxLds ? SC_OK : SC_ERR_UNSUPPORTED;
 }

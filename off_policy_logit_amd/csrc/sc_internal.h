@@ -55,7 +55,8 @@ struct RowParams {
   const float* advantages;
   int32_t n_responses;
   float temperature;
-  float c;               // log2(e) / T
+  double c64;            // log2(e) / T
+  float c_hi, c_lo;      // c64 = c_hi + c_lo (c_hi = c64 rounded to fp32)
   const int64_t* n_valid;
   float* row_stats;
   int32_t* row_idx;
@@ -70,9 +71,8 @@ struct RowParams {
   int centering;         // 0: centering term dropped
   uint32_t* dev_status;
   // LDS layout (bytes into dynamic shared memory)
-  int hs, hshift, vs, vshift, bm_wpt, ke;
-  int off_bitmap, off_hkey, off_hval, off_headz, off_headp, off_hout;
-  int off_entvec, off_entval, off_entslot, off_vkey, off_vval, off_hid;
+  int hs, hshift, bm_wpt;
+  int off_bitmap, off_hkey, off_hval, off_headz, off_headp, off_headlp, off_hout;
   size_t lds_bytes;
 };
 

@@ -12,17 +12,21 @@
 //             row's 16-byte vectors marking those that hold a recorded id or
 //             the sampled id; range and duplicate checks.
 //   pass 1    one coalesced stream of the row: per-thread running max of the
-//             raw logits (with its lowest index), and the sum of
-//             2^((z - m) log2(e) / T) over unmarked vectors (the off-head tail,
-//             summed directly, never as 1 - P_H).  Marked vectors are copied
-//             to a short LDS list instead.
-//   finalize  workgroup max / argmax / tail sum, the marked vectors resolved
-//             element by element (recorded logits, the sampled logit, their
-//             tail members), lse, log p at H and at a, P_H, tau; then Q_H,
+//             raw logits (with its lowest index), and the off-head tail sum
+//             2^(z c - E_t) (c = log2(e) / T) over the unmarked vectors,
+//             summed directly (never as 1 - P_H) in float64, relative to an
+//             integer exponent E_t that follows the thread's largest unmarked
+//             logit, so that the terms that dominate the tail are computed
+//             from small exponents.
+//   finalize  workgroup max / argmax; each thread resolves its own marked
+//             vectors element by element (recorded logits, the sampled logit,
+//             the tail members among them, in float64); the head terms in
+//             float64; lse, log p at H and at a, P_H, tau, entropy; then Q_H,
 //             rho, c, S, loss, TV, KL(mu_hat || p), K3 in float64.
 //   pass 2    (optional) the row streamed again to write one output element
-//             per vocabulary id: off-head ids get alpha * p_v (a single exp2 of
-//             a fused multiply-add), marked vectors take the exact per-id value.
+//             per vocabulary id: off-head ids get alpha * p_v from one exp2 of
+//             an exactly formed exponent, marked vectors take their values
+//             from float64.
 #include "sc_device.h"
 #include "sc_internal.h"
 
@@ -37,13 +41,15 @@ enum KernelKind { KIND_LOGPROBS = 0, KIND_CENTER = 1, KIND_CORRECT = 2 };
 enum {
   C_LSE = 0, C_LOGP_A = 1, C_TAIL = 2, C_P_H = 3, C_Q_H = 4, C_RHO = 5,
   C_S = 6, C_LOSS = 7, C_TV = 8, C_KL = 9, C_K3 = 10, C_ENT = 11, C_W = 12,
-  C_WT = 13, C_RKL = 14, C_RES = 15, C_N = 16
+  C_WT = 13, C_RKL = 14, C_LSE_LO = 15, C_N = 16
 };
 enum { IS_NONE = 0, IS_TIS = 1, IS_MIS = 2 };
 enum { F_BAD_ID = 1, F_DUP_ID = 2, F_BAD_SAMPLED = 4, F_NONFINITE = 8, F_BAD_RESP = 16 };
 enum { M_DLOGITS = 0, M_SCORE = 1, M_CORRECTION = 2 };
 
-// kU: 16-byte vectors per thread per pipelined tile (divides 32).
+constexpr double kLn2d = 0.6931471805599453;
+constexpr double kLog2ed = 1.4426950408889634;
+
 // Keep a when c, else b (whole raw vectors; selects, no branch).
 SC_DEV u32x4 keep_if(bool c, const u32x4& a, const u32x4& b) {
   u32x4 o;
@@ -58,6 +64,61 @@ SC_DEV f32x4 keep_if(bool c, const f32x4& a, const f32x4& b) {
 SC_DEV uint32_t keep_if(bool c, uint32_t a, uint32_t b) { return c ? a : b; }
 SC_DEV float keep_if(bool c, float a, float b) { return c ? a : b; }
 
+// Reference exponent of a running maximum x: ceil(x c_hi), an integer held in
+// a float, clamped to +-2^60 so that it stays finite while nothing finite has
+// been seen (x = -FLT_MAX) or when x is +inf (such a row is flagged).
+SC_DEV float ref_exp(float x, float c_hi) {
+  return fminf(fmaxf(ceilf(x * c_hi), -0x1p60f), 0x1p60f);
+}
+
+// Per-row constants of the pass-2 value sign(alpha) 2^((z - m) c - G):
+// G = Gint + gq + glo with Gint an integer, gq on the 2^-14 grid in (-1, 0]
+// and |glo| < 2^-14.
+struct Pass2 {
+  float m, c_hi, c_lo;
+  float gq;      // gq (as above)
+  float nglo;    // -glo ln 2
+  float scl;     // sign(alpha) 2^-Gint (NaN for a flagged row, +-0 when all values underflow)
+  float scl_lo;  // scl 2^-64, for exponents moved up by 64 (subnormal results)
+};
+
+// Pass-2 value of one logit z.  d = z - m is exact for bf16 z and m (else its
+// rounding error de comes from a two-sum).  P = RN(d c_hi) and its exact
+// residual Pe = d c_hi - P (one fma); yh = P - gq is exact because gq lies on
+// a grid no finer than P's (|P| < 2^10) and shrinks |P|.  The small remainder
+// k = ln 2 (Pe + d c_lo - glo) (|k| < 2^-14) is applied as 2^yh (1 + k), and
+// the power of two comes last, in one multiply (a single rounding when the
+// result is subnormal).  CAREFUL adds what rare rows need: -inf logits give 0
+// (not NaN), fp32 logits take the two-sum, and exponents below -96 are moved
+// up by 64 (back in the final multiply) so that the exp2 instruction, which
+// flushes results below 2^-126, keeps them.
+template <bool CAREFUL>
+SC_DEV float p2_value(float z, const Pass2& Q) {
+#pragma clang fp contract(off)
+  float d = z - Q.m;
+  float de = 0.f;
+  if (CAREFUL) {
+    const float zz = d + Q.m;          // two-sum of z and -m
+    const float mm = d - zz;
+    de = (z - zz) - (Q.m + mm);
+    de = d >= -0x1p20f ? de : 0.f;     // -inf (or a NaN row): no residual
+    d = fmaxf(d, -0x1p20f);
+  }
+  const float P = d * Q.c_hi;
+  const float Pe = fmaf(d, Q.c_hi, -P);
+  float yh = P - Q.gq;
+  float scl = Q.scl;
+  if (CAREFUL) {
+    const bool low = yh < -96.f;
+    yh = low ? yh + 64.f : yh;         // exact: the magnitude shrinks
+    scl = low ? Q.scl_lo : scl;
+  }
+  const float r = CAREFUL ? fmaf(de, Q.c_hi, Pe) : Pe;
+  const float k = fmaf(fmaf(d, Q.c_lo, r), kLn2, Q.nglo);
+  const float e = exp2_fast(yh);
+  return fmaf(e, k, e) * scl;
+}
+
 template <typename TI, typename TO, bool VECTOR, int B, int KIND, int kU, int WAVES>
 __global__ __launch_bounds__(B) __attribute__((amdgpu_waves_per_eu(WAVES)))
 void k_row(RowParams P) {
@@ -66,6 +127,7 @@ void k_row(RowParams P) {
   using Raw = typename IO::raw;
   constexpr int N = IO::N;
   constexpr int NW = B / kWave;
+  constexpr bool kBf16In = std::is_same<TI, uint16_t>::value;
   const bool has_out = (KIND != KIND_LOGPROBS) && P.row_out != nullptr;
   const int t = threadIdx.x;
   const int K = P.k;
@@ -73,30 +135,25 @@ void k_row(RowParams P) {
   const int n_full = V / N;                 // full vectors per row
   const int rem = V - n_full * N;        // elements of the partial vector
   const int J = n_full > t ? (n_full - 1 - t) / B + 1 : 0;  // my vectors
-  const float c = P.c;                          // log2(e) / T
+  const float c_hi = P.c_hi, c_lo = P.c_lo;
+  const double c64 = P.c64;
 
   extern __shared__ __align__(16) unsigned char lds[];
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(lds + P.off_bitmap);
   int* hkey = reinterpret_cast<int*>(lds + P.off_hkey);
   int* hval = reinterpret_cast<int*>(lds + P.off_hval);
-  float* headz = reinterpret_cast<float*>(lds + P.off_headz);  // logits at H
-  float* headp = reinterpret_cast<float*>(lds + P.off_headp);  // p at H
-  float* hout = reinterpret_cast<float*>(lds + P.off_hout);    // log p / output at H
-  int* ent_vec = reinterpret_cast<int*>(lds + P.off_entvec);
-  float* ent_val = reinterpret_cast<float*>(lds + P.off_entval);
-  int* ent_slot = reinterpret_cast<int*>(lds + P.off_entslot);  // slot or -1 per listed element
-  int* vkey = reinterpret_cast<int*>(lds + P.off_vkey);          // listed vector -> entry
-  int* vval = reinterpret_cast<int*>(lds + P.off_vval);
-  int* hid = reinterpret_cast<int*>(lds + P.off_hid);            // recorded id of each slot
+  float* headz = reinterpret_cast<float*>(lds + P.off_headz);     // logits at H
+  double* headp = reinterpret_cast<double*>(lds + P.off_headp);   // p at H
+  double* headlp = reinterpret_cast<double*>(lds + P.off_headlp); // log p at H
+  float* hout = reinterpret_cast<float*>(lds + P.off_hout);       // output value at H
 
-  __shared__ float redf[4 * NW];
+  __shared__ float redf[NW];
   __shared__ int redi[NW];
   __shared__ double redd[4 * NW];
-  __shared__ unsigned long long redu[2 * NW];
-  __shared__ int sh_ent;
   __shared__ uint32_t sh_flags;
   __shared__ float sh_za;
   __shared__ uint32_t sh_status;
+  __shared__ int sh_ninf;
 
   const uint32_t hmask = (uint32_t)P.hs - 1;
   const int hshift = P.hshift;
@@ -118,11 +175,12 @@ void k_row(RowParams P) {
       if (t == 0) {
         if (KIND != KIND_CENTER) {
           stats[C_LSE] = 0.f; stats[C_LOGP_A] = 0.f; stats[C_TAIL] = 0.f;
+          stats[C_LSE_LO] = 0.f;
           ridx[0] = -1; ridx[1] = -1;
         }
         if (KIND == KIND_LOGPROBS) { stats[C_P_H] = 0.f; stats[C_ENT] = 0.f; }
         if (KIND != KIND_LOGPROBS)
-          for (int col = C_P_H; col <= C_RES; ++col) stats[col] = 0.f;
+          for (int col = C_P_H; col <= C_RKL; ++col) stats[col] = 0.f;
       }
       for (int k = t; k < K; k += B) {
         if (KIND != KIND_CENTER && P.head_logp) P.head_logp[row * K + k] = 0.f;
@@ -165,59 +223,40 @@ void k_row(RowParams P) {
     auto tile_bits = [&](int j0) -> uint32_t {
       return (bitmap[(j0 >> 5) * B + t] >> (j0 & 31)) & ((1u << kU) - 1u);
     };
-    auto append = [&](int n, const float (&v)[N]) {
-      const int e = atomicAdd(&sh_ent, 1);
-      if (e < P.ke) {
-        idset_insert(vkey, vval, (uint32_t)P.vs - 1, P.vshift, (int32_t)n, e);
-        ent_vec[e] = (int)n;
-#pragma unroll
-        for (int i = 0; i < N; ++i) ent_val[e * N + i] = v[i];
-      }
+    auto is_marked = [&](int j) -> bool {
+      return (bitmap[(j >> 5) * B + t] >> (j & 31)) & 1u;
     };
-
-    // List this thread's marked vectors (read again: the stream skipped them).
-    auto list_marked = [&]() {
+    // Calls f(n, v, cnt) for each marked vector n of this thread (v: its
+    // values widened to fp32, cnt: its elements) and, for the thread that
+    // owns it, the partial last vector (never in the bitmap).  The vectors
+    // are read again: a marked vector's elements are resolved one by one.
+    auto for_marked = [&](auto&& f) {
       for (int w = 0; w < P.bm_wpt; ++w) {
         uint32_t word = bitmap[w * B + t];
         while (word) {
           const int j = w * 32 + __builtin_ctz(word);
           word &= word - 1u;
           float v[N];
-          IO::unpack(IO::template load<false>(zrow, (int64_t)j * B + t), v);
-          append(j * B + t, v);
+          IO::unpack(load_one(j, std::false_type{}), v);
+          f(j * B + t, v, N);
         }
       }
-    };
-
-    // Map recorded ids and the sampled id onto the listed vectors: ent_slot
-    // gets the slot of every recorded element (-1 elsewhere), headz the
-    // recorded logits and sh_za the sampled logit.  Ends with a barrier.
-    auto resolve_slots = [&](int n_ent) {
-      for (int i = t; i < n_ent * N; i += B) ent_slot[i] = -1;
-      __syncthreads();
-      for (int k = t; k < K; k += B) {
-        const int id = hid[k];
-        if (id < 0 || id >= V) continue;
-        const int e = idset_find(vkey, vval, (uint32_t)P.vs - 1, P.vshift, id / N);
-        if (e < 0) continue;
-        headz[k] = ent_val[e * N + id % N];
-        ent_slot[e * N + id % N] = k;
+      if (rem > 0 && t == (int)(n_full % B)) {
+        float v[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+          v[i] = i < rem ? load_elem(zrow, (int64_t)n_full * N + i) : -INFINITY;
+        f(n_full, v, rem);
       }
-      if (t == 0 && a_ok) {
-        const int e = idset_find(vkey, vval, (uint32_t)P.vs - 1, P.vshift, a / N);
-        if (e >= 0) sh_za = ent_val[e * N + a % N];
-      }
-      __syncthreads();
     };
 
     // ------------------------------------------------------------ stage
     if (need_stage) {
       for (int w = 0; w < P.bm_wpt; ++w) bitmap[w * B + t] = 0u;
       for (int i = t; i < P.hs; i += B) hkey[i] = -1;
-      for (int i = t; i < P.vs; i += B) vkey[i] = -1;
       for (int k = t; k < K; k += B) headz[k] = qnan;
     }
-    if (t == 0) { sh_ent = 0; sh_flags = 0; sh_za = qnan; }
+    if (t == 0) { sh_flags = 0; sh_za = qnan; sh_ninf = 0; }
     __syncthreads();
     if (need_stage) {
       uint32_t fl = 0;
@@ -231,7 +270,6 @@ void k_row(RowParams P) {
       };
       for (int k = t; k < K; k += B) {
         const int32_t id = k == t ? my_id : P.head_ids[row * K + k];
-        hid[k] = id;
         if (id < 0 || id >= V) {
           fl |= F_BAD_ID;
         } else {
@@ -246,59 +284,65 @@ void k_row(RowParams P) {
       __syncthreads();
     }
 
-    float m = 0.f;        // row max of raw logits (pass-1 kernels)
-    float log2s = 0.f;    // log2 sum_v 2^((z_v - m) c)
-    float lse = 0.f, logp_a = 0.f, tau = 0.f, entropy = 0.f;
+    float m = 0.f;          // row max of raw logits
+    float E_row = 0.f;      // ceil(m c_hi): exponent reference of the row's sums
+    double l2s = 0.0;       // log2 sum_v 2^(z_v c - E_row)
+    double lse = 0.0, logp_a = 0.0, tau = 0.0, P_H = 0.0, entropy = 0.0;
     int argmax = -1, a_slot = -1;
 
     if (KIND != KIND_CENTER) {
       // ---------------------------------------------------------- pass 1
-      // Online update per vector: running max m_t (starts at -FLT_MAX so
-      // that all-(-inf) vectors rescale by 2^0 and add 2^-inf = 0), tail sum
-      // s_t relative to m_t, h_t = sum 2^((z - m_t) c) (z - m_t) for the
-      // entropy, and the index of the vector that raised m_t (strictly, so
-      // the first of equal maxima is kept).
-      float m_t = -FLT_MAX, s_t = 0.f, h_t = 0.f;
+      // m_t: running max of every vector (argmax; starts at -FLT_MAX so that
+      // all -inf vectors never count); am_raw / am_vec: the vector that last
+      // raised it (strictly, so the first of equal maxima is kept).  r_t:
+      // running max of the unmarked vectors, E_t = ref_exp(r_t): the exponent
+      // reference of s_t = sum 2^(z c - E_t) (float64) and of
+      // h_t = sum 2^(z c - E_t) (z c - E_t) over unmarked vectors.  When E_t
+      // rises by D, s_t scales by 2^-D and h_t by 2^-D after subtracting
+      // D s_t, both exactly.
+      float m_t = -FLT_MAX, r_t = -FLT_MAX, E_t = ref_exp(-FLT_MAX, c_hi);
+      double s_t = 0.0;
+      float h_t = 0.f;
       int am_vec = -1;
-      Raw am_raw = IO::ninf();  // the vector that raised m_t, kept in registers
+      Raw am_raw = IO::ninf();
       int am_direct = -1;
-      auto vec_update = [&](const float (&v)[N], const Raw& rv, int j) {
-        float vm = v[0];
-#pragma unroll
-        for (int i = 1; i < N; ++i) vm = fmaxf(vm, v[i]);
-        const float m_new = fmaxf(m_t, vm);
-        am_raw = keep_if(vm > m_t, rv, am_raw);
-        am_vec = vm > m_t ? j : am_vec;
-        const float r = exp2_fast((m_t - m_new) * c);
-        h_t = r * (h_t - (m_new - m_t) * s_t);
-        s_t *= r;
-        m_t = m_new;
+      auto rebase = [&](float E_new) {
+        const float D = E_new - E_t;                 // >= 0
+        const int kd = (int)fminf(D, 2048.f);
+        h_t = ldexpf(fmaf(-D, (float)s_t, h_t), -kd);
+        s_t = ldexp(s_t, -kd);
+        E_t = E_new;
       };
-      // exp sum and exp-weighted offset sum of one vector.  A -inf entry
-      // makes its term 0 * -inf = NaN in acch; the stream leaves h_t NaN
-      // then and the thread recomputes it after the stream (see below).
+      // Exp sum (pairwise) and exponent-weighted sum of one vector relative to
+      // E_t: y = z c_hi - E_t + z c_lo (two fma).  A -inf entry makes its
+      // term 0 * -inf = NaN in acch; the stream leaves h_t NaN then and the
+      // thread recomputes it after the stream (see below).
       auto vec_sums = [&](const float (&v)[N], float& acc, float& acch) {
-        acc = 0.f;
+        float e[N];
         acch = 0.f;
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-          const float d = v[i] - m_t;
-          const float e = exp2_fast(d * c);
-          acc += e;
-          acch = fmaf(e, d, acch);
+          const float y = fmaf(v[i], c_lo, fmaf(v[i], c_hi, -E_t));
+          e[i] = exp2_fast(y);
+          acch = fmaf(e[i], y, acch);
         }
+#pragma unroll
+        for (int w = 1; w < N; w <<= 1)
+#pragma unroll
+          for (int i = 0; i + w < N; i += 2 * w) e[i] += e[i + w];
+        acc = e[0];
       };
       // Branch-free: marked vectors are summed too and the sum is dropped
       // (they are resolved element by element after the stream).  The
-      // running max is raised once per group of kG vectors, so one rescale
-      // serves kG vectors.
+      // maxima are raised once per group of kG vectors, so one rebase serves
+      // kG vectors.
       constexpr int kG = kU >= 4 ? 4 : kU;
       auto process = [&](const Raw (&r)[kU], int j0) {
         const uint32_t bits = tile_bits(j0);
 #pragma unroll
         for (int u0 = 0; u0 < kU; u0 += kG) {
           float v[kG][N];
-          float m_run = m_t;
+          float m_run = m_t, r_run = r_t;
 #pragma unroll
           for (int u = 0; u < kG; ++u) {
             IO::unpack(r[u0 + u], v[u]);
@@ -308,17 +352,18 @@ void k_row(RowParams P) {
             am_raw = keep_if(vm > m_run, r[u0 + u], am_raw);
             am_vec = vm > m_run ? j0 + u0 + u : am_vec;   // strictly: first of equal maxima
             m_run = fmaxf(m_run, vm);
+            const bool marked = (bits >> (u0 + u)) & 1u;
+            r_run = fmaxf(r_run, marked ? -FLT_MAX : vm);
           }
-          const float rs = exp2_fast((m_t - m_run) * c);
-          h_t = rs * (h_t - (m_run - m_t) * s_t);
-          s_t *= rs;
           m_t = m_run;
+          r_t = r_run;
+          rebase(ref_exp(r_t, c_hi));
 #pragma unroll
           for (int u = 0; u < kG; ++u) {
             float acc, acch;
             vec_sums(v[u], acc, acch);
             const bool marked = (bits >> (u0 + u)) & 1u;
-            s_t += marked ? 0.f : acc;
+            s_t += (double)(marked ? 0.f : acc);
             h_t += marked ? 0.f : acch;
           }
         }
@@ -334,55 +379,52 @@ void k_row(RowParams P) {
           float v[N];
           const Raw rv = load_one(j, nt);
           IO::unpack(rv, v);
-          vec_update(v, rv, j);
+          float vm = v[0];
+#pragma unroll
+          for (int i = 1; i < N; ++i) vm = fmaxf(vm, v[i]);
+          am_raw = keep_if(vm > m_t, rv, am_raw);
+          am_vec = vm > m_t ? j : am_vec;
+          m_t = fmaxf(m_t, vm);
+          const bool marked = is_marked(j);
+          r_t = fmaxf(r_t, marked ? -FLT_MAX : vm);
+          rebase(ref_exp(r_t, c_hi));
           float acc, acch;
           vec_sums(v, acc, acch);
-          const bool marked = (bitmap[(j >> 5) * B + t] >> (j & 31)) & 1u;
-          s_t += marked ? 0.f : acc;
+          s_t += (double)(marked ? 0.f : acc);
           h_t += marked ? 0.f : acch;
         }
       }
       // A -inf logit among this thread's unmarked vectors left h_t NaN (its
-      // term 0 * -inf): recompute the entropy sum against the final m_t with
+      // term 0 * -inf): recompute the entropy sum against the final E_t with
       // the term clamped to 0, reading the thread's vectors again.  A NaN
       // logit leaves s_t NaN as well (the row is flagged) and is left alone.
+      // Such a row takes the careful pass-2 value (sh_ninf).
       if (h_t != h_t && s_t == s_t) {
+        sh_ninf = 1;
         float hh = 0.f;
         for (int j = 0; j < J; ++j) {
-          if ((bitmap[(j >> 5) * B + t] >> (j & 31)) & 1u) continue;
+          if (is_marked(j)) continue;
           float v[N];
           IO::unpack(load_one(j, std::false_type{}), v);
 #pragma unroll
           for (int i = 0; i < N; ++i) {
-            const float d = v[i] - m_t;
-            hh = fmaf(exp2_fast(d * c), fmaxf(d, -FLT_MAX), hh);
+            const float y = fmaf(v[i], c_lo, fmaf(v[i], c_hi, -E_t));
+            hh = fmaf(exp2_fast(y), fmaxf(y, -FLT_MAX), hh);
           }
         }
         h_t = hh;
       }
-      list_marked();
-      // The partial last vector (vocab not a multiple of N) always goes to the
-      // LDS list; its owner is the thread of vector index n_full.
+      // The partial last vector (vocab not a multiple of N) counts for the
+      // maximum here; its sums are taken with the marked vectors.
       if (rem > 0 && t == (int)(n_full % B)) {
-        float v[N];
-        float tm = -INFINITY;
-        int idx = -1;
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-          v[i] = i < rem ? load_elem(zrow, n_full * N + i) : -INFINITY;
-          if (v[i] > tm) { tm = v[i]; idx = (int)(n_full * N + i); }
+        for (int i = 0; i < rem; ++i) {
+          const float z = load_elem(zrow, (int64_t)n_full * N + i);
+          if (z > m_t) { m_t = z; am_direct = n_full * N + i; }
         }
-        if (tm > m_t) {
-          const float r = exp2_fast((m_t - tm) * c);
-          h_t = r * (h_t - (tm - m_t) * s_t);
-          s_t *= r;
-          m_t = tm;
-          am_direct = idx;
-        }
-        append(n_full, v);
       }
       // Element index of my maximum: the first element equal to m_t in the
-      // vector that raised it (kept in registers during the stream).
+      // vector that raised it (kept in registers during the stream), unless
+      // the partial vector raised it last.
       int am_t = 0x7fffffff;
       if (am_direct >= 0) {
         am_t = am_direct;
@@ -398,51 +440,56 @@ void k_row(RowParams P) {
       block_argmax<B>(mv, mi, redf, redi);
       m = mv;
       argmax = mi;
-      const float r_t = exp2_fast((m_t - m) * c);
-      float tail_part = s_t * r_t;
-      float h_part = r_t * (h_t - (m - m_t) * s_t);
-      // Resolve the listed vectors: each recorded id (and the sampled id)
-      // finds its vector's list entry through the vector map; every other
-      // listed element is a tail term.  Tail terms are summed as 64-bit
-      // fixed point (2^-52 units; each term is <= 1 since z <= m): integer
-      // sums are exact, so the total does not depend on the listing order.
-      const int n_ent = min(sh_ent, P.ke);
-      resolve_slots(n_ent);
-      // The entropy sum D = sum_v 2^((z - m) c) (z - m) takes every listed
-      // element (recorded ids included) in signed 2^-32 fixed point, added
-      // modulo 2^64 (terms are >= -0.37 T each).
-      unsigned long long tail_fx = 0ull, h_fx = 0ull;
-      for (int i = t; i < n_ent * N; i += B) {
-        const int vid = ent_vec[i / N] * N + (i % N);
-        if (vid >= V) continue;
-        const float d = ent_val[i] - m;
-        const float e = exp2_fast(d * c);
-        if (ent_slot[i] < 0) tail_fx += (unsigned long long)(e * 0x1p52f);
-        h_fx += (unsigned long long)(long long)(e * fmaxf(d, -FLT_MAX) * 0x1p32f);
-      }
-      unsigned long long fx[2] = {tail_fx, h_fx};
-      block_sum<B, 2>(fx, redu);
-      tail_part += t == 0 ? (float)((double)fx[0] * 0x1p-52) : 0.f;
-      h_part += t == 0 ? (float)((double)(long long)fx[1] * 0x1p-32) : 0.f;
-      float head_part = 0.f;
-      for (int k = t; k < K; k += B) head_part += exp2_fast((headz[k] - m) * c);
-      float sums[3] = {tail_part, head_part, h_part};
-      block_sum<B, 3>(sums, redf);
-      const float s = sums[0] + sums[1];
-      log2s = log2f(s);
-      // entropy = ln s - D / (T s), with 1 / T = c ln 2
-      entropy = (log2s - sums[2] * c / s) * kLn2;
-      lse = (m * c + log2s) * kLn2;
-      tau = sums[0] / s;
-      const float za = sh_za;
-      logp_a = ((za - m) * c - log2s) * kLn2;
+      E_row = ref_exp(m, c_hi);
+      // This thread's unmarked sums, moved to the row's reference (powers of
+      // two: exact).  Then its marked vectors: recorded logits to headz, the
+      // sampled logit to sh_za, every other element a tail term in float64.
+      const double Dd = (double)(E_row - E_t);
+      const int kd = (int)fmin(Dd, 2048.0);
+      double s_tail = ldexp(s_t, -kd);
+      double h_sum = ldexp((double)h_t - Dd * s_t, -kd);
+      for_marked([&](int n, const float (&v)[N], int cnt) {
+        for (int i = 0; i < cnt; ++i) {
+          const int id = n * N + i;
+          const int slot = idset_find(hkey, hval, hmask, hshift, id);
+          if (slot >= 0) {
+            headz[slot] = v[i];
+          } else {
+            const double y = (double)v[i] * c64 - (double)E_row;
+            const double e = exp2(y);
+            s_tail += e;
+            h_sum += e > 0.0 ? e * y : 0.0;
+          }
+          if (id == a) sh_za = v[i];
+        }
+      });
+      __syncthreads();
+      // Recorded ids: 2^(z c - E_row) and its exponent-weighted term.
+      double s_head = 0.0;
       uint32_t fl = 0;
       for (int k = t; k < K; k += B) {
         const float hz = headz[k];
         if (hz == -INFINITY) fl |= F_NONFINITE;
-        const float l2 = (hz - m) * c - log2s;
-        headp[k] = exp2_fast(l2 + 32.f) * 0x1p-32f;  // subnormal-exact
-        hout[k] = l2 * kLn2;                          // log p at H
+        const double y = (double)hz * c64 - (double)E_row;
+        const double e = exp2(y);
+        headp[k] = e;
+        s_head += e;
+        h_sum += e > 0.0 ? e * y : 0.0;
+      }
+      double sums[3] = {s_tail, s_head, h_sum};
+      block_sum<B, 3>(sums, redd);
+      const double s = sums[0] + sums[1];
+      l2s = log2(s);
+      lse = ((double)E_row + l2s) * kLn2d;
+      tau = sums[0] / s;
+      P_H = sums[1] / s;
+      entropy = kLn2d * (l2s - sums[2] / s);
+      const float za = sh_za;
+      logp_a = ((double)za * c64 - (double)E_row - l2s) * kLn2d;
+      for (int k = t; k < K; k += B) {
+        const double y = (double)headz[k] * c64 - (double)E_row;
+        headp[k] = headp[k] / s;
+        headlp[k] = (y - l2s) * kLn2d;
       }
       if (!(s < INFINITY) || !(m > -FLT_MAX) || !(m < INFINITY) || za == -INFINITY)
         fl |= F_NONFINITE;
@@ -450,64 +497,67 @@ void k_row(RowParams P) {
       a_slot = a_ok ? idset_find(hkey, hval, hmask, hshift, a) : -1;
       __syncthreads();
     } else {
-      // sc_center: pass-1 results come from memory
-      lse = stats[C_LSE];
+      // sc_center: pass-1 results come from memory (the log-sum-exp as its
+      // fp32 value plus the fp32 remainder in column C_LSE_LO); the row max
+      // is read back at the recorded argmax when the row is streamed again.
+      lse = (double)stats[C_LSE] + (double)stats[C_LSE_LO];
       logp_a = stats[C_LOGP_A];
       tau = stats[C_TAIL];
       a_slot = ridx[1];
       argmax = ridx[0];
+      double ph = 0.0;
       for (int k = t; k < K; k += B) {
-        const float lp = P.head_logp[row * K + k];
-        hout[k] = lp;
-        headp[k] = expf(lp);
+        const double lp = (double)P.head_logp[row * K + k];
+        headlp[k] = lp;
+        headp[k] = exp(lp);
+        ph += headp[k];
       }
+      double sums[1] = {ph};
+      block_sum<B, 1>(sums, redd);
+      P_H = sums[0];
+      if (has_out) m = (argmax >= 0 && argmax < V) ? load_elem(zrow, argmax) : qnan;
+      if (t == 0) sh_ninf = 1;   // the row's -inf entries are not known here
       __syncthreads();
     }
 
     const uint32_t flags = sh_flags;
 
     if (KIND == KIND_LOGPROBS) {
-      float ph = 0.f;
-      for (int k = t; k < K; k += B) ph += headp[k];
-      float sums[1] = {ph};
-      block_sum<B, 1>(sums, redf);
       if (t == 0) {
         const bool bad = flags != 0;
-        stats[C_LSE] = bad ? qnan : lse;
-        stats[C_LOGP_A] = bad ? qnan : logp_a;
-        stats[C_TAIL] = bad ? qnan : tau;
-        stats[C_P_H] = bad ? qnan : sums[0];
-        stats[C_ENT] = bad ? qnan : entropy;
+        const float lse32 = (float)lse;
+        stats[C_LSE] = bad ? qnan : lse32;
+        stats[C_LSE_LO] = bad ? qnan : (float)(lse - (double)lse32);
+        stats[C_LOGP_A] = bad ? qnan : (float)logp_a;
+        stats[C_TAIL] = bad ? qnan : (float)tau;
+        stats[C_P_H] = bad ? qnan : (float)P_H;
+        stats[C_ENT] = bad ? qnan : (float)entropy;
         ridx[0] = bad ? -1 : argmax;
         ridx[1] = bad ? -1 : a_slot;
         if (flags) sh_status |= flags;
       }
       if (P.head_logp)
-        for (int k = t; k < K; k += B) P.head_logp[row * K + k] = flags ? qnan : hout[k];
+        for (int k = t; k < K; k += B) P.head_logp[row * K + k] = flags ? qnan : (float)headlp[k];
       continue;
     }
 
     // -------------------------------------------------------------- center
-    double d1[2] = {0.0, 0.0};
-    for (int k = t; k < K; k += B) {
-      d1[0] += (double)P.head_probs[row * K + k];
-      d1[1] += (double)headp[k];
-    }
-    block_sum<B, 2>(d1, redd);
-    const double Q_H = d1[0], P_H = d1[1];
-    const double taud = (double)tau;
-    const double rho = fmax(1.0 - Q_H, kClamp) / fmax(taud, kClamp);
-    const double S = Q_H + rho * taud;
+    double d1[1] = {0.0};
+    for (int k = t; k < K; k += B) d1[0] += (double)P.head_probs[row * K + k];
+    block_sum<B, 1>(d1, redd);
+    const double Q_H = d1[0];
+    const double rho = fmax(1.0 - Q_H, kClamp) / fmax(tau, kClamp);
+    const double S = Q_H + rho * tau;
     double d2[4] = {0.0, 0.0, 0.0, 0.0};
     for (int k = t; k < K; k += B) {
       const double q = (double)P.head_probs[row * K + k];
-      const double p = (double)headp[k];
-      const double lp = (double)hout[k];
+      const double p = headp[k];
+      const double lp = headlp[k];
       const double ck = q - rho * p;
       if (P.coef) P.coef[row * K + k] = flags ? qnan : (float)ck;
       d2[0] += ck * lp;
       d2[1] += fabs(q - p);
-      const double lq = (double)logf((float)q);
+      const double lq = log(q);
       if (q > 0.0) d2[2] += q * (lq - lp);
       if (p > 0.0) d2[3] += p * (lp - lq);   // reverse KL, head part
     }
@@ -515,31 +565,34 @@ void k_row(RowParams P) {
 
     uint32_t rflags = flags;
     if (resp >= P.n_responses) rflags |= F_BAD_RESP;
+    if (KIND == KIND_CENTER && has_out && !(m > -FLT_MAX && m < INFINITY)) rflags |= F_NONFINITE;
     const double A = (resp < P.n_responses) ? (double)P.advantages[resp] : (double)qnan;
     // importance ratio of the sampled token and its stop-gradient weight
     double w = (double)qnan, wt = 1.0;
     double k3 = (double)qnan;
     if (P.rollout_logp) {
-      const double d = (double)logp_a - (double)P.rollout_logp[row];
-      k3 = (double)expm1f((float)d) - d;
-      w = (double)expf((float)d);
+      const double d = logp_a - (double)P.rollout_logp[row];
+      k3 = expm1(d) - d;
+      w = exp(d);
       if (P.is_mode == IS_TIS) wt = fmin(w, (double)P.is_hi);
       else if (P.is_mode == IS_MIS) wt = (w >= (double)P.is_lo && w <= (double)P.is_hi) ? w : 0.0;
     }
-    const double loss = -A * wt * ((double)logp_a - (P.centering ? d2[0] : 0.0));
-    const double tv = 0.5 * (d2[1] + fabs(rho - 1.0) * taud);
-    const double lrho = (double)logf((float)rho);
+    const double loss = -A * wt * (logp_a - (P.centering ? d2[0] : 0.0));
+    const double tv = 0.5 * (d2[1] + fabs(rho - 1.0) * tau);
+    const double lrho = log(rho);
     double kl = d2[2];
-    if (rho * taud > 0.0) kl += rho * taud * lrho;
-    const double rkl = d2[3] - (taud > 0.0 ? taud * lrho : 0.0);
+    if (rho * tau > 0.0) kl += rho * tau * lrho;
+    const double rkl = d2[3] - (tau > 0.0 ? tau * lrho : 0.0);
 
     if (t == 0) {
       const bool bad = rflags != 0;
       if (KIND == KIND_CORRECT) {
-        stats[C_LSE] = bad ? qnan : lse;
-        stats[C_LOGP_A] = bad ? qnan : logp_a;
-        stats[C_TAIL] = bad ? qnan : tau;
-        stats[C_ENT] = bad ? qnan : entropy;
+        const float lse32 = (float)lse;
+        stats[C_LSE] = bad ? qnan : lse32;
+        stats[C_LSE_LO] = bad ? qnan : (float)(lse - (double)lse32);
+        stats[C_LOGP_A] = bad ? qnan : (float)logp_a;
+        stats[C_TAIL] = bad ? qnan : (float)tau;
+        stats[C_ENT] = bad ? qnan : (float)entropy;
         ridx[0] = bad ? -1 : argmax;
         ridx[1] = bad ? -1 : a_slot;
       }
@@ -554,11 +607,10 @@ void k_row(RowParams P) {
       stats[C_W] = bad ? qnan : (float)w;
       stats[C_WT] = bad ? qnan : (float)wt;
       stats[C_RKL] = bad ? qnan : (float)rkl;
-      stats[C_RES] = 0.f;
       if (rflags) sh_status |= rflags;
     }
     if (KIND == KIND_CORRECT && P.head_logp)
-      for (int k = t; k < K; k += B) P.head_logp[row * K + k] = rflags ? qnan : hout[k];
+      for (int k = t; k < K; k += B) P.head_logp[row * K + k] = rflags ? qnan : (float)headlp[k];
 
     if (!has_out) continue;
 
@@ -577,9 +629,8 @@ void k_row(RowParams P) {
       alpha = P.centering ? -scale * (rho + 1.0 - S) : -scale;
     }
     if (rflags) { alpha = (double)qnan; scale = (double)qnan; }
-    __syncthreads();  // all reads of hout as log p are done
     for (int k = t; k < K; k += B) {
-      const double p = (double)headp[k];
+      const double p = headp[k];
       double val;
       if (P.row_mode == M_CORRECTION) {
         val = (double)P.head_probs[row * K + k] - p;
@@ -592,29 +643,48 @@ void k_row(RowParams P) {
     }
     __syncthreads();
 
-    const bool neg = alpha < 0.0;
-    // p_v = 2^((z_v - mref) c - lref); value = sign(alpha) 2^((z_v - mref) c + off)
-    // computed as 2^(y + 32) 2^-32 so that results below 2^-126 stay exact
-    // subnormals (the exp2 instruction flushes them).
-    const float mref = (KIND == KIND_CORRECT) ? m : 0.f;
-    const double lref = (KIND == KIND_CORRECT) ? (double)log2s
-                                               : (double)lse * 1.4426950408889634;
-    const float off = log2f(fabsf((float)alpha)) - (float)lref + 32.f;
-    const float add_a = (float)scale;
+    // log2 normaliser F of p_v = 2^(z c - F); value_v = sign(alpha) 2^((z - m) c - G)
+    // with G = F - m c - log2 |alpha|.
+    const double F = (KIND == KIND_CENTER) ? lse * kLog2ed : (double)E_row + l2s;
+    Pass2 Q;
+    Q.m = m;
+    Q.c_hi = c_hi;
+    Q.c_lo = c_lo;
+    Q.gq = 0.f;
+    Q.nglo = 0.f;
+    Q.scl = qnan;
+    Q.scl_lo = qnan;
+    bool careful = !kBf16In || sh_ninf != 0;
+    {
+      const double G = fmax(F - (double)m * c64 - log2(fabs(alpha)), -1.0e4);
+      const float sgn = alpha < 0.0 ? -1.f : 1.f;
+      if (G == G && rflags == 0) {
+        if (G > 1.0e4) {                       // every value underflows (alpha = 0 too)
+          Q.scl = 0.f * sgn;
+          Q.scl_lo = Q.scl;
+        } else {
+          double gi = ceil(G);
+          double gq = ceil((G - gi) * 16384.0) / 16384.0;   // (-1, 0]
+          const double glo = (G - gi) - gq;                 // (-2^-14, 0]
+          if (gi < -126.0) { gq += gi + 126.0; gi = -126.0; }   // |alpha| beyond 2^126
+          const int g = (int)gi;
+          Q.gq = (float)gq;
+          Q.nglo = (float)(-glo * kLn2d);
+          Q.scl = g > 160 ? 0.f * sgn : ldexpf(sgn, -g);
+          Q.scl_lo = g + 64 > 160 ? 0.f * sgn : ldexpf(sgn, -g - 64);
+          // Results below 2^-126 need the careful value: only when the row's
+          // scale leaves room for them (with bf16 output, values below
+          // 2^-134 round to zero anyway).
+          if (g < (std::is_same<TO, uint16_t>::value ? 8 : 24)) careful = true;
+        }
+      }
+    }
     TO* orow = reinterpret_cast<TO*>(P.row_out) + row * P.out_stride;
 
-    // Stream the row; marked vectors are not stored here (the sc_center kind
-    // lists them now, the fused kind listed them in pass 1).
-    // One output vector; the sign is a compile-time choice so that the
-    // negation folds into the bf16 conversion.
-    auto out_vec = [&](const Raw& r, float (&o)[N], auto negc) {
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const float e = exp2_fast(fmaf(IO::elem(r, i) - mref, c, off)) * 0x1p-32f;
-        o[i] = decltype(negc)::value ? -e : e;
-      }
-    };
-    auto stream2 = [&](auto negc) {
+    // Stream the row; marked vectors are not stored here (their owners write
+    // them below).
+    auto stream2 = [&](auto carefulc) {
+      constexpr bool CF = decltype(carefulc)::value;
       std::integral_constant<bool, true> nt;
       for (int j0 = 0; j0 < Jt; j0 += kU) {
         Raw r[kU];
@@ -623,45 +693,47 @@ void k_row(RowParams P) {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
           float o[N];
-          out_vec(r[u], o, negc);
+#pragma unroll
+          for (int i = 0; i < N; ++i) o[i] = p2_value<CF>(IO::elem(r[u], i), Q);
           if (!((bits >> u) & 1u)) RowOut<TO, N>::store(orow, (j0 + u) * B + t, o);
         }
       }
       for (int j = Jt; j < J; ++j) {
-        if ((bitmap[(j >> 5) * B + t] >> (j & 31)) & 1u) continue;
+        if (is_marked(j)) continue;
+        const Raw r = load_one(j, nt);
         float o[N];
-        out_vec(load_one(j, nt), o, negc);
+#pragma unroll
+        for (int i = 0; i < N; ++i) o[i] = p2_value<CF>(IO::elem(r, i), Q);
         RowOut<TO, N>::store(orow, j * B + t, o);
       }
     };
-    if (neg) stream2(std::true_type{});
+    if (careful) stream2(std::true_type{});
     else stream2(std::false_type{});
-    if (KIND == KIND_CENTER) list_marked();
-    if (KIND == KIND_CENTER && rem > 0 && t == (int)(n_full % B)) {
-      float v[N];
+    // Marked vectors and the partial last one: exact values, in float64.
+    for_marked([&](int n, const float (&v)[N], int cnt) {
+      float o[N];
 #pragma unroll
-      for (int i = 0; i < N; ++i) v[i] = i < rem ? load_elem(zrow, n_full * N + i) : 0.f;
-      append(n_full, v);
-    }
-    __syncthreads();
-    // Marked vectors: exact values, one element per thread.
-    const int n_ent = min(sh_ent, P.ke);
-    if (KIND == KIND_CENTER) resolve_slots(n_ent);
-    for (int i = t; i < n_ent * N; i += B) {
-      const int e = i / N, l = i - e * N;
-      const int vid = ent_vec[e] * N + l;
-      if (vid >= V) continue;
-      const int slot = ent_slot[i];
-      float val;
-      if (slot >= 0) {
-        val = hout[slot];
-      } else {
-        val = exp2_fast(fmaf(ent_val[i] - mref, c, off)) * 0x1p-32f;
-        val = neg ? -val : val;
-        if (vid == a) val += add_a;
+      for (int i = 0; i < N; ++i) {
+        const int id = n * N + i;
+        float val = 0.f;
+        if (i < cnt) {
+          const int slot = idset_find(hkey, hval, hmask, hshift, id);
+          if (slot >= 0) {
+            val = hout[slot];
+          } else {
+            double x = alpha * exp2((double)v[i] * c64 - F);
+            if (id == a) x += scale;
+            val = (float)x;
+          }
+        }
+        o[i] = val;
       }
-      store_elem(orow, vid, val);
-    }
+      if (cnt == N) {
+        RowOut<TO, N>::store(orow, n, o);
+      } else {
+        for (int i = 0; i < cnt; ++i) store_elem(orow, (int64_t)n * N + i, o[i]);
+      }
+    });
   }
 
   __syncthreads();

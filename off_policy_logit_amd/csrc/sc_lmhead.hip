@@ -608,7 +608,7 @@ __global__ __launch_bounds__(256) void k_lm_finalize(LmParams P) {
     if (resp < 0) {
       if (l == 0) {
         stats[SC_STAT_LSE] = 0.f; stats[SC_STAT_LOGP_A] = 0.f; stats[SC_STAT_TAIL] = 0.f;
-        stats[SC_STAT_P_H] = 0.f; stats[SC_STAT_ENTROPY] = 0.f;
+        stats[SC_STAT_P_H] = 0.f; stats[SC_STAT_ENTROPY] = 0.f; stats[SC_STAT_LSE_LO] = 0.f;
         ridx[0] = -1; ridx[1] = -1;
       }
       if (P.head_logp)
@@ -663,7 +663,9 @@ __global__ __launch_bounds__(256) void k_lm_finalize(LmParams P) {
       }
       ph = wave_sum(ph);
       if (l == 0) {
-        stats[SC_STAT_LSE] = bad ? qnan : (m * c + log2s) * kLn2;
+        const double lse64 = ((double)m * (double)c + (double)log2s) * 0.6931471805599453;
+        stats[SC_STAT_LSE] = bad ? qnan : (float)lse64;
+        stats[SC_STAT_LSE_LO] = bad ? qnan : (float)(lse64 - (double)(float)lse64);
         stats[SC_STAT_LOGP_A] = bad ? qnan : ((za - m) * c - log2s) * kLn2;
         stats[SC_STAT_TAIL] = bad ? qnan : s / stot;
         stats[SC_STAT_P_H] = bad ? qnan : ph;

@@ -23,7 +23,7 @@ DEV_BAD_ID, DEV_DUP_ID, DEV_BAD_SAMPLED, DEV_NONFINITE, DEV_BAD_RESP = 1, 2, 4, 
 ROW_DLOGITS, ROW_SCORE, ROW_CORRECTION = 0, 1, 2
 IS_NONE, IS_TIS, IS_MIS = 0, 1, 2
 STATS = ("lse", "logp_a", "tail", "P_H", "Q_H", "rho", "S", "loss", "tv", "kl",
-         "k3", "entropy", "w", "weight", "rev_kl", "reserved")
+         "k3", "entropy", "w", "weight", "rev_kl", "lse_lo")
 NSTATS = len(STATS)
 STAT = {name: i for i, name in enumerate(STATS)}
 BATCH = ("sum_loss", "sum_k3", "sum_tv", "sum_kl", "sum_Q_H", "sum_P_H",

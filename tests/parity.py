@@ -1,35 +1,40 @@
 """Element-by-element comparison of the HIP path with the CPU oracle.
 
-Tolerances (derived from the kernels' fp32 arithmetic; the oracle is exact
-float64):
+The bar is the one stated for this path (GPU result against the float64
+oracle, per row):
 
-* log-probabilities (lse, log p(a), log p at H): abs 1e-5.  The kernel's
-  exponent (z - m) log2(e) / T is rounded once in fp32, the sum of exps is an
-  fp32 sum, and the log is taken in fp32.
-* masses P_H, tau, Q_H, S and TV: abs 1e-6.
-* rho: rel 1e-5 (tau carries the fp32 sum's relative error; the clamp
-  max(tau, 1e-6) does not increase it).
-* c_k = q_k - rho p_k: abs 1e-6 + 1e-5 |rho p_k| (rho's relative error scales
-  the product, which reaches ~1e2 on clamp-active rows).
-* loss: the propagated bound |A| (1e-5 + sum_k tol(c_k) |log p_k| + |c_k| 1e-5).
-* KL: abs 1e-6 + rel 1e-5; K3: abs 1e-6 + 1e-5 |exp(d) - 1| (d has abs 1e-5).
-* entropy ln s + (-D) / (T s): both parts are >= 0 and each carries the
-  fp32 sums' relative error, so abs 1e-5 + rel 1e-5.
-* importance ratio w = exp(d): rel 2e-5 (d has abs 1e-5, expf adds ulps);
-  the weight takes w's tolerance, except that a masked-IS decision within
-  that tolerance of a boundary may go either way (both outcomes checked
-  valid).  The loss and the rows of a weighted token add the weight's
-  relative error to their own.
-* reverse KL sum_H p (log p - log q) - tau log rho: abs 1e-5 + 1e-6 |log rho|
-  + 1e-5 sum_H p |log p - log q|; +inf (p > 0 where q = 0) exactly.
-* full-vocabulary rows in fp32: abs 1e-6 |scale| + 4e-6 |value|.  Each entry
-  is a single exp2 of an fp32 fused multiply-add of size |y| <= ~90, whose
-  rounding gives a relative error <= (|y| 2^-24 + 4 2^-24) ln 2 < 4e-6.
-* full-vocabulary rows in bf16: every entry within one bf16 step of the
-  round-to-nearest-even of the float64 value, and at least 99.8% of them
-  bit-equal (a relative error eps flips a rounding with probability at most
-  2^9 eps <= 1.4e-3).
 * argmax, a_slot and device flags: exact.
+* log-probabilities (lse, log p(a), log p at H): abs 1e-5.
+* masses tau, P_H, Q_H, S and TV: abs 1e-6.
+* rho: rel 1e-5.
+* c_k = q_k - rho p_k: abs 1e-6.
+* K3: abs 1e-6.
+* KL(mu_hat || p): abs 1e-6 + rel 1e-5.
+* loss per row: abs 1e-4.
+* full-vocabulary rows in fp32 (the score g, the correction mu_hat - p, or
+  dLogits = -A wt / (T N_valid) g): abs 1e-6 per entry, scaled by the factor
+  in front of g (|A wt| / (T N_valid) for dLogits, |wt| for the score).
+* full-vocabulary rows in bf16: every entry within one bf16 step of the
+  round-to-nearest-even of the float64 value, and at least 99.99% of the
+  entries a test checks bit-equal.  An entry whose value is within
+  |scale| 2^-45 of the float64 one counts as agreeing: the recorded entries
+  are [k = a] - q_k - (1 - S) p_k (or q_k - p_k), and where q_k equals p_k to
+  within 1e-15 that difference cancels to the size of the float64 rounding
+  of S, a 128-term sum, in the oracle as in the kernel (~1e-16), so no
+  implementation fixes its bits.
+
+Every output is an fp32 number, whose own spacing exceeds an absolute bound
+once the value is large (2^-23 |x| > 1e-6 for |x| >= 16): an absolute
+tolerance is therefore read as "abs tol, or one fp32 spacing of the exact
+value where that is larger" (``f32_tol``); below |x| = 8 this is the
+absolute tolerance itself.
+
+Extra signals, beyond the stated bar: entropy abs 1e-5 + rel 1e-6; the
+importance ratio w and the weight rel 1e-6 (w = exp(log p(a) - log mu(a)) is
+formed in float64 from log p(a), whose own error is far below 1e-6); reverse
+KL abs 1e-6 + rel 1e-5.  A masked-IS decision within w's tolerance of a bound
+may go either way (the test then checks the GPU's side against the oracle
+row at that weight).
 """
 from __future__ import annotations
 
@@ -41,7 +46,19 @@ from oracle import sc_oracle as O
 
 STAT_COLS = dict(lse=0, logp_a=1, tau=2, P_H=3, Q_H=4, rho=5, S=6, loss=7,
                  tv=8, kl=9, k3=10, entropy=11, w=12, weight=13, rev_kl=14)
-REL_W = 2e-5
+REL_W = 1e-6
+MIN_BF16_EQUAL = 0.9999
+
+# Largest error seen per quantity, in units of its tolerance (printed by the
+# tests that check many rows, for the record of how close the bar is).
+WORST = {}
+
+
+def f32_tol(want, atol):
+    """abs tol, or one fp32 spacing of the value where that is larger."""
+    w = np.abs(np.asarray(want, np.float64))
+    sp = np.spacing(np.minimum(w, 3e38).astype(np.float32)).astype(np.float64)
+    return np.maximum(atol, sp)
 
 
 def bf16_bits_to_f64(bits):
@@ -56,15 +73,35 @@ def _ordered(x64):
     return np.where(b & 0x8000, -(b & 0x7FFF), b)
 
 
-def compare_bf16(gpu_bits, oracle_vals):
-    """(max step distance, bit-equal fraction) of bf16 output vs RNE(oracle)."""
+def compare_bf16(gpu_bits, oracle_vals, floor=0.0):
+    """(max step distance, agreeing fraction) of bf16 output vs RNE(oracle).
+
+    An entry agrees when its bits equal RNE(oracle), or when it lies within
+    `floor` of the float64 value (see the module docstring)."""
     ref = O.bf16_rne(oracle_vals)
     got = bf16_bits_to_f64(gpu_bits)
     both_nan = np.isnan(ref) & np.isnan(got)
+    near = np.abs(got - np.asarray(oracle_vals, np.float64)) <= floor
     d = np.abs(_ordered(got) - _ordered(ref))
-    d = np.where(both_nan, 0, d)
-    eq = (got == ref) | both_nan
+    d = np.where(both_nan | near, 0, d)
+    eq = (got == ref) | both_nan | near
     return int(d.max()) if d.size else 0, float(eq.mean()) if eq.size else 1.0
+
+
+def bf16_bar(stats, tag):
+    """Assert the bit-equal fraction over a test's bf16 entries.
+
+    stats: list of (max_dist, equal_fraction, entries).  Returns the
+    fraction.  The bar is MIN_BF16_EQUAL over all the entries the test
+    checked."""
+    total = sum(s[2] for s in stats)
+    if not total:
+        return 1.0
+    eq = sum(s[1] * s[2] for s in stats) / total
+    print(f"[case] {tag}: bf16 bit-equal fraction {eq:.7f} over {total} entries "
+          f"({round((1 - eq) * total)} unequal)", flush=True)
+    assert eq >= MIN_BF16_EQUAL, (tag, eq, total)
+    return eq
 
 
 def oracle_row(z, T, ids, q, a, rlp, A, n_valid, mode, **weighting):
@@ -92,8 +129,8 @@ def check_row(tag, g, o, A=1.0, T=1.0, n_valid=1, mode=O.MODE_DLOGITS,
 
     g: dict with numpy arrays: stats [16], idx [2], head_logp [K] and, unless
     stats_only, coef [K] and (when row_dtype) row [V] (fp32 values or bf16
-    bits).  bf16_stats: list collecting (max_dist, equal_fraction).  The
-    weighting arguments are the ones the oracle row was computed with;
+    bits).  bf16_stats: list collecting (max_dist, equal_fraction, entries).
+    The weighting arguments are the ones the oracle row was computed with;
     rerun(**overrides) recomputes the oracle row with other weighting
     arguments (needed only for a masked-IS decision at a boundary).
     """
@@ -106,50 +143,42 @@ def check_row(tag, g, o, A=1.0, T=1.0, n_valid=1, mode=O.MODE_DLOGITS,
     assert g["idx"][1] == o["a_slot"], (tag, g["idx"][1], o["a_slot"])
 
     def close(name, got, want, tol):
-        err = np.max(np.abs(np.asarray(got, np.float64) - want) - tol)
-        assert err <= 0, (tag, name, np.max(np.abs(np.asarray(got, np.float64) - want)))
+        err = np.abs(np.asarray(got, np.float64) - want)
+        tol = np.broadcast_to(np.asarray(tol, np.float64), err.shape)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            ratio = float(np.max(np.where(err == 0, 0.0, err / tol), initial=0.0))
+        if ratio == ratio:
+            WORST[name] = max(WORST.get(name, 0.0), ratio)
+        assert np.all(err <= tol), (tag, name, float(np.max(err)), ratio)
 
     close("lse", st[0], o["lse"], 1e-5)
     close("logp_a", st[1], o["logp_a"], 1e-5)
     close("tau", st[2], o["tau"], 1e-6)
     close("P_H", st[3], o["P_H"], 1e-6)
     close("head_logp", g["head_logp"], o["head_logp"], 1e-5)
-    close("entropy", st[11], o["entropy"], 1e-5 + 1e-5 * abs(o["entropy"]))
+    close("entropy", st[11], o["entropy"], 1e-5 + 1e-6 * abs(o["entropy"]))
     if stats_only:
         return
     close("Q_H", st[4], o["Q_H"], 1e-6)
     close("rho", st[5], o["rho"], 1e-5 * abs(o["rho"]))
     close("S", st[6], o["S"], 1e-6)
-    p_h = np.exp(o["head_logp"])
-    tol_c = 1e-6 + 1e-5 * np.abs(o["rho"] * p_h)
-    close("coef", g["coef"], o["coef"], tol_c)
+    close("coef", g["coef"], o["coef"], f32_tol(o["coef"], 1e-6))
     if rlp is not None:
         close("w", st[12], o["w"], REL_W * abs(o["w"]))
     wt, boundary = _gpu_weight(o, st[12], is_mode, is_lo, is_hi)
     rel_wt = REL_W if (is_mode != O.IS_NONE and wt != 0) else 0.0
     close("weight", st[13], wt, rel_wt * abs(wt))
-    if centering:
-        bracket = o["logp_a"] - float(np.sum(o["coef"] * o["head_logp"]))
-        tol_b = (1e-5 + np.sum(tol_c * np.abs(o["head_logp"]))
-                 + np.sum(np.abs(o["coef"])) * 1e-5)
-    else:
-        bracket, tol_b = o["logp_a"], 1e-5
+    bracket = o["logp_a"] - (float(np.sum(o["coef"] * o["head_logp"])) if centering else 0.0)
     loss = -A * wt * bracket
-    tol_loss = abs(A) * (abs(wt) * tol_b + rel_wt * abs(wt * bracket))
-    close("loss", st[7], loss, tol_loss)
+    close("loss", st[7], loss, f32_tol(loss, 1e-4))
     close("tv", st[8], o["tv"], 1e-6)
     close("kl", st[9], o["kl"], 1e-6 + 1e-5 * abs(o["kl"]))
     if math.isinf(o["rev_kl"]):
         assert st[14] == o["rev_kl"], (tag, "rev_kl", st[14])
     else:
-        lq = np.log(np.where(o["coef"] + o["rho"] * p_h > 0,
-                             o["coef"] + o["rho"] * p_h, 1.0))
-        spread = float(np.sum(p_h * np.abs(o["head_logp"] - lq)))
-        close("rev_kl", st[14], o["rev_kl"],
-              1e-5 + 1e-6 * abs(math.log(o["rho"])) + 1e-5 * spread)
+        close("rev_kl", st[14], o["rev_kl"], 1e-6 + 1e-5 * abs(o["rev_kl"]))
     if rlp is not None:
-        d = o["logp_a"] - float(rlp)
-        close("k3", st[10], o["k3"], 1e-6 + 1e-5 * abs(math.expm1(d)))
+        close("k3", st[10], o["k3"], f32_tol(o["k3"], 1e-6))
     if row_dtype is None:
         return
     ref_row = o["row"]
@@ -165,13 +194,10 @@ def check_row(tag, g, o, A=1.0, T=1.0, n_valid=1, mode=O.MODE_DLOGITS,
         scale = 1.0
     if mode != O.MODE_CORRECTION:
         scale *= abs(wt)
-    rel_row = 4e-6 + (rel_wt if mode != O.MODE_CORRECTION else 0.0)
     if row_dtype == "f32":
-        tol = 1e-6 * scale + rel_row * np.abs(ref_row)
-        close("row", g["row"], ref_row, tol)
+        close("row", g["row"], ref_row, f32_tol(ref_row, 1e-6 * scale))
     else:
-        dist, eq = compare_bf16(g["row"], ref_row)
+        dist, eq = compare_bf16(g["row"], ref_row, floor=2.0 ** -45 * scale)
         assert dist <= 1, (tag, "bf16 row step distance", dist)
         if bf16_stats is not None:
             bf16_stats.append((dist, eq, ref_row.size))
-

@@ -88,7 +88,7 @@ def test_lmhead_stats_match_oracle_on_own_logits(T, w_sd):
             assert np.all(st[r, [0, 1, 2, 3, 11]] == 0) and list(ix[r]) == [-1, -1]
             assert np.all(hl[r] == 0)
             continue
-        o = O.sc_row(zh[r], T, idh[r], qh[r], ah[r])
+        o = O.sc_row(zh[r], float(np.float32(T)), idh[r], qh[r], ah[r])
         g = dict(stats=st[r], idx=ix[r], head_logp=hl[r])
         check_row(f"lmhead row {r}", g, o, T=T, stats_only=True)
 
@@ -122,7 +122,7 @@ def test_lmhead_then_center_completes_the_correction():
     for r in range(0, n, 5):
         A = float(adv_h[r // 96])
         rlp = float(host(c["rollout_logp"])[r])
-        o = O.sc_row(zh[r], T, host(c["head_ids"])[r], host(c["head_probs"])[r],
+        o = O.sc_row(zh[r], float(np.float32(T)), host(c["head_ids"])[r], host(c["head_probs"])[r],
                      int(host(c["sampled"])[r]), rollout_logp=rlp, advantage=A, n_valid=n)
         g = dict(stats=g_all["row_stats"][r], idx=g_all["row_idx"][r],
                  head_logp=g_all["head_logp"][r], coef=g_all["coef"][r])
@@ -198,7 +198,7 @@ def test_lmhead_more_rows_than_vocabulary():
     zh, idh, qh, ah = host(z), host(c["head_ids"]), host(c["head_probs"]), host(c["sampled"])
     st, ix, hl = host(out["row_stats"]), host(out["row_idx"]), host(out["head_logp"])
     for r in range(0, n, 37):
-        o = O.sc_row(zh[r], T, idh[r], qh[r], ah[r])
+        o = O.sc_row(zh[r], float(np.float32(T)), idh[r], qh[r], ah[r])
         check_row(f"rows>ids row {r}", dict(stats=st[r], idx=ix[r], head_logp=hl[r]), o,
                   stats_only=True)
 

@@ -60,7 +60,7 @@ def oracle_dlogits(z, T, c, resp, adv, n_valid, rows, is_mode, centering):
         if rh[r] < 0:
             G.append(np.zeros(zh.shape[1]))
             continue
-        o = O.sc_row(zh[r], T, ids[r], q[r], a[r], rollout_logp=rlp[r],
+        o = O.sc_row(zh[r], float(np.float32(T)), ids[r], q[r], a[r], rollout_logp=rlp[r],
                      advantage=float(ah[rh[r]]), n_valid=n_valid, row_mode=O.MODE_DLOGITS,
                      is_mode=is_mode, is_lo=0.9, is_hi=1.1, centering=centering)
         G.append(o["row"])
