@@ -73,6 +73,11 @@ int layout(sc::RowParams& P, int kind) {
   P.off_headp = take((size_t)P.k * 8);
   P.off_headlp = take((size_t)P.k * 8);
   P.off_hout = take((size_t)P.k * 4);
+  // marked-vector list: at most k vectors holding recorded ids, the sampled
+  // id's vector and the partial last vector
+  P.ke = P.k + 2;
+  P.off_lval = take((size_t)P.ke * N * 4);
+  P.off_lvec = take((size_t)P.ke * 4);
   P.lds_bytes = off;
   return off <= kMaxLds ? SC_OK : SC_ERR_UNSUPPORTED;
 }

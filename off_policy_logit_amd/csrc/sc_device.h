@@ -97,6 +97,32 @@ SC_DEV void block_sum(F (&v)[N], F* red) {
   }
 }
 
+// Exclusive prefix sum of one int per thread over the workgroup (thread
+// order); `total` gets the sum of all.  Every thread must call it.
+template <int B>
+SC_DEV int block_excl_scan(int v, int* red, int& total) {
+  constexpr int NW = B / kWave;
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    x += l >= o ? y : 0;
+  }
+  __syncthreads();
+  if (l == kWave - 1) red[w] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int r = red[i];
+    base += i < w ? r : 0;
+    tot += r;
+  }
+  total = tot;
+  return base + x - v;
+}
+
 // ---------------------------------------------------------------------------
 // Row element access.  A row is read as "vectors" of N consecutive elements:
 // 16 bytes (N = 8 bf16 or 4 fp32) on the vector path, N = 1 on the scalar

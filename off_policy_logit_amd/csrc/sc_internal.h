@@ -15,28 +15,28 @@ namespace sc {
 #define SC_STATS_BLOCK 256
 #endif
 #ifndef SC_STATS_TILE
-#define SC_STATS_TILE 8
+#define SC_STATS_TILE 4
 #endif
 #ifndef SC_STATS_WAVES
 #define SC_STATS_WAVES 4
 #endif
 #ifndef SC_CENTER_BLOCK
-#define SC_CENTER_BLOCK 512
+#define SC_CENTER_BLOCK 256
 #endif
 #ifndef SC_CENTER_TILE
 #define SC_CENTER_TILE 8
 #endif
 #ifndef SC_CENTER_WAVES
-#define SC_CENTER_WAVES 4
+#define SC_CENTER_WAVES 3
 #endif
 #ifndef SC_FUSED_BLOCK
-#define SC_FUSED_BLOCK 512
+#define SC_FUSED_BLOCK 256
 #endif
 #ifndef SC_FUSED_TILE
 #define SC_FUSED_TILE 8
 #endif
 #ifndef SC_FUSED_WAVES
-#define SC_FUSED_WAVES 4
+#define SC_FUSED_WAVES 3
 #endif
 constexpr int kKindBlock[3] = {SC_STATS_BLOCK, SC_CENTER_BLOCK, SC_FUSED_BLOCK};
 
@@ -71,8 +71,9 @@ struct RowParams {
   int centering;         // 0: centering term dropped
   uint32_t* dev_status;
   // LDS layout (bytes into dynamic shared memory)
-  int hs, hshift, bm_wpt;
+  int hs, hshift, bm_wpt, ke;
   int off_bitmap, off_hkey, off_hval, off_headz, off_headp, off_headlp, off_hout;
+  int off_lval, off_lvec;
   size_t lds_bytes;
 };
 

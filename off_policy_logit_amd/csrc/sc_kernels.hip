@@ -18,15 +18,17 @@
 //             integer exponent E_t that follows the thread's largest unmarked
 //             logit, so that the terms that dominate the tail are computed
 //             from small exponents.
-//   finalize  workgroup max / argmax; each thread resolves its own marked
-//             vectors element by element (recorded logits, the sampled logit,
+//             Marked vectors are copied, as the stream meets them, to an LDS
+//             list whose entry order is fixed by a prefix sum over threads.
+//   finalize  workgroup max / argmax; the listed vectors resolved element by
+//             element over all threads (recorded logits, the sampled logit,
 //             the tail members among them, in float64); the head terms in
 //             float64; lse, log p at H and at a, P_H, tau, entropy; then Q_H,
 //             rho, c, S, loss, TV, KL(mu_hat || p), K3 in float64.
 //   pass 2    (optional) the row streamed again to write one output element
 //             per vocabulary id: off-head ids get alpha * p_v from one exp2 of
-//             an exactly formed exponent, marked vectors take their values
-//             from float64.
+//             an exactly formed exponent; the listed vectors are written from
+//             the list, one 16-byte store each.
 #include "sc_device.h"
 #include "sc_internal.h"
 
@@ -146,6 +148,8 @@ void k_row(RowParams P) {
   double* headp = reinterpret_cast<double*>(lds + P.off_headp);   // p at H
   double* headlp = reinterpret_cast<double*>(lds + P.off_headlp); // log p at H
   float* hout = reinterpret_cast<float*>(lds + P.off_hout);       // output value at H
+  float* lval = reinterpret_cast<float*>(lds + P.off_lval);       // listed vectors' values
+  int* lvec = reinterpret_cast<int*>(lds + P.off_lvec);           // listed vectors' indices
 
   __shared__ float redf[NW];
   __shared__ int redi[NW];
@@ -226,28 +230,26 @@ void k_row(RowParams P) {
     auto is_marked = [&](int j) -> bool {
       return (bitmap[(j >> 5) * B + t] >> (j & 31)) & 1u;
     };
-    // Calls f(n, v, cnt) for each marked vector n of this thread (v: its
-    // values widened to fp32, cnt: its elements) and, for the thread that
-    // owns it, the partial last vector (never in the bitmap).  The vectors
-    // are read again: a marked vector's elements are resolved one by one.
-    auto for_marked = [&](auto&& f) {
-      for (int w = 0; w < P.bm_wpt; ++w) {
-        uint32_t word = bitmap[w * B + t];
-        while (word) {
-          const int j = w * 32 + __builtin_ctz(word);
-          word &= word - 1u;
-          float v[N];
-          IO::unpack(load_one(j, std::false_type{}), v);
-          f(j * B + t, v, N);
-        }
-      }
-      if (rem > 0 && t == (int)(n_full % B)) {
-        float v[N];
+    // Marked-vector list: each thread's marked vectors (and, for its owner,
+    // the partial last vector, which the bitmap never holds) take
+    // consecutive entries from lpos on; lpos comes from a prefix sum over
+    // threads, so the list order, and every sum taken over it, is the same on
+    // every run.  capture() appends one vector as the stream meets it.
+    int lpos = 0, n_ent = 0;
+    auto capture = [&](int n, const float (&v)[N]) {
+      lvec[lpos] = n;
 #pragma unroll
-        for (int i = 0; i < N; ++i)
-          v[i] = i < rem ? load_elem(zrow, (int64_t)n_full * N + i) : -INFINITY;
-        f(n_full, v, rem);
-      }
+      for (int i = 0; i < N; ++i) lval[lpos * N + i] = v[i];
+      ++lpos;
+    };
+    const bool rem_owner = rem > 0 && t == (int)(n_full % B);
+    auto capture_partial = [&]() {
+      float v[N];
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        v[i] = i < rem ? load_elem(zrow, (int64_t)n_full * N + i) : -INFINITY;
+      capture(n_full, v);
+      return v[0];
     };
 
     // ------------------------------------------------------------ stage
@@ -282,6 +284,9 @@ void k_row(RowParams P) {
       }
       if (fl) atomicOr(&sh_flags, fl);
       __syncthreads();
+      int cnt = rem_owner ? 1 : 0;
+      for (int w = 0; w < P.bm_wpt; ++w) cnt += __builtin_popcount(bitmap[w * B + t]);
+      lpos = block_excl_scan<B>(cnt, redi, n_ent);
     }
 
     float m = 0.f;          // row max of raw logits
@@ -354,6 +359,7 @@ void k_row(RowParams P) {
             m_run = fmaxf(m_run, vm);
             const bool marked = (bits >> (u0 + u)) & 1u;
             r_run = fmaxf(r_run, marked ? -FLT_MAX : vm);
+            if (marked) capture((j0 + u0 + u) * B + t, v[u]);
           }
           m_t = m_run;
           r_t = r_run;
@@ -387,6 +393,7 @@ void k_row(RowParams P) {
           m_t = fmaxf(m_t, vm);
           const bool marked = is_marked(j);
           r_t = fmaxf(r_t, marked ? -FLT_MAX : vm);
+          if (marked) capture(j * B + t, v);
           rebase(ref_exp(r_t, c_hi));
           float acc, acch;
           vec_sums(v, acc, acch);
@@ -415,10 +422,11 @@ void k_row(RowParams P) {
         h_t = hh;
       }
       // The partial last vector (vocab not a multiple of N) counts for the
-      // maximum here; its sums are taken with the marked vectors.
-      if (rem > 0 && t == (int)(n_full % B)) {
+      // maximum here and goes to the list; its sums are taken with the list.
+      if (rem_owner) {
+        capture_partial();
         for (int i = 0; i < rem; ++i) {
-          const float z = load_elem(zrow, (int64_t)n_full * N + i);
+          const float z = lval[(lpos - 1) * N + i];
           if (z > m_t) { m_t = z; am_direct = n_full * N + i; }
         }
       }
@@ -448,21 +456,35 @@ void k_row(RowParams P) {
       const int kd = (int)fmin(Dd, 2048.0);
       double s_tail = ldexp(s_t, -kd);
       double h_sum = ldexp((double)h_t - Dd * s_t, -kd);
-      for_marked([&](int n, const float (&v)[N], int cnt) {
-        for (int i = 0; i < cnt; ++i) {
-          const int id = n * N + i;
-          const int slot = idset_find(hkey, hval, hmask, hshift, id);
-          if (slot >= 0) {
-            headz[slot] = v[i];
-          } else {
-            const double y = (double)v[i] * c64 - (double)E_row;
-            const double e = exp2(y);
-            s_tail += e;
-            h_sum += e > 0.0 ? e * y : 0.0;
-          }
-          if (id == a) sh_za = v[i];
+      // Tail members of the list: 2^((z - m) c - G1), G1 = E_row - m c, by the
+      // exact fp32 exponent of pass 2 (relative error ~1e-7 per term).
+      Pass2 Q1;
+      {
+        const double G1 = fmin(fmax((double)E_row - (double)m * c64, -2.0), 2.0);
+        const double gi = ceil(G1);
+        const double gq = ceil((G1 - gi) * 16384.0) / 16384.0;
+        Q1.m = m; Q1.c_hi = c_hi; Q1.c_lo = c_lo;
+        Q1.gq = (float)gq;
+        Q1.nglo = (float)(-((G1 - gi) - gq) * kLn2d);
+        Q1.scl = ldexpf(1.f, -(int)gi);
+        Q1.scl_lo = ldexpf(1.f, -(int)gi - 64);
+      }
+      for (int i = t; i < n_ent * N; i += B) {
+        const int e = i / N;
+        const int id = lvec[e] * N + (i - e * N);
+        if (id >= V) continue;
+        const float z = lval[i];
+        const int slot = idset_find(hkey, hval, hmask, hshift, id);
+        if (slot >= 0) {
+          headz[slot] = z;
+        } else {
+          const float ez = p2_value<true>(z, Q1);
+          const float y = fmaf(z, c_lo, fmaf(z, c_hi, -E_row));
+          s_tail += (double)ez;
+          h_sum += ez > 0.f ? (double)(ez * y) : 0.0;
         }
-      });
+        if (id == a) sh_za = z;
+      }
       __syncthreads();
       // Recorded ids: 2^(z c - E_row) and its exponent-weighted term.
       double s_head = 0.0;
@@ -479,16 +501,17 @@ void k_row(RowParams P) {
       double sums[3] = {s_tail, s_head, h_sum};
       block_sum<B, 3>(sums, redd);
       const double s = sums[0] + sums[1];
+      const double rs = 1.0 / s;
       l2s = log2(s);
       lse = ((double)E_row + l2s) * kLn2d;
-      tau = sums[0] / s;
-      P_H = sums[1] / s;
-      entropy = kLn2d * (l2s - sums[2] / s);
+      tau = sums[0] * rs;
+      P_H = sums[1] * rs;
+      entropy = kLn2d * (l2s - sums[2] * rs);
       const float za = sh_za;
       logp_a = ((double)za * c64 - (double)E_row - l2s) * kLn2d;
       for (int k = t; k < K; k += B) {
         const double y = (double)headz[k] * c64 - (double)E_row;
-        headp[k] = headp[k] / s;
+        headp[k] *= rs;
         headlp[k] = (y - l2s) * kLn2d;
       }
       if (!(s < INFINITY) || !(m > -FLT_MAX) || !(m < INFINITY) || za == -INFINITY)
@@ -507,9 +530,9 @@ void k_row(RowParams P) {
       argmax = ridx[0];
       double ph = 0.0;
       for (int k = t; k < K; k += B) {
-        const double lp = (double)P.head_logp[row * K + k];
+        const float lp = P.head_logp[row * K + k];
         headlp[k] = lp;
-        headp[k] = exp(lp);
+        headp[k] = expf(lp);   // p_k from its stored fp32 log
         ph += headp[k];
       }
       double sums[1] = {ph};
@@ -557,7 +580,7 @@ void k_row(RowParams P) {
       if (P.coef) P.coef[row * K + k] = flags ? qnan : (float)ck;
       d2[0] += ck * lp;
       d2[1] += fabs(q - p);
-      const double lq = log(q);
+      const double lq = logf((float)q);     // fp32 ln q: KL's bar is abs 1e-6
       if (q > 0.0) d2[2] += q * (lq - lp);
       if (p > 0.0) d2[3] += p * (lp - lq);   // reverse KL, head part
     }
@@ -571,15 +594,17 @@ void k_row(RowParams P) {
     double w = (double)qnan, wt = 1.0;
     double k3 = (double)qnan;
     if (P.rollout_logp) {
+      // one float64 exponential: w = e^d and K3 = (w - 1) - d (for small |d|
+      // the subtraction leaves an absolute error near 1e-16, far below K3's bar)
       const double d = logp_a - (double)P.rollout_logp[row];
-      k3 = expm1(d) - d;
       w = exp(d);
+      k3 = (w - 1.0) - d;
       if (P.is_mode == IS_TIS) wt = fmin(w, (double)P.is_hi);
       else if (P.is_mode == IS_MIS) wt = (w >= (double)P.is_lo && w <= (double)P.is_hi) ? w : 0.0;
     }
     const double loss = -A * wt * (logp_a - (P.centering ? d2[0] : 0.0));
     const double tv = 0.5 * (d2[1] + fabs(rho - 1.0) * tau);
-    const double lrho = log(rho);
+    const double lrho = (double)logf((float)rho);
     double kl = d2[2];
     if (rho * tau > 0.0) kl += rho * tau * lrho;
     const double rkl = d2[3] - (tau > 0.0 ? tau * lrho : 0.0);
@@ -681,8 +706,9 @@ void k_row(RowParams P) {
     }
     TO* orow = reinterpret_cast<TO*>(P.row_out) + row * P.out_stride;
 
-    // Stream the row; marked vectors are not stored here (their owners write
-    // them below).
+    // Stream the row; marked vectors are not stored here but from the list
+    // below (the sc_center kind lists them now, as the stream meets them; the
+    // fused kind listed them in pass 1).
     auto stream2 = [&](auto carefulc) {
       constexpr bool CF = decltype(carefulc)::value;
       std::integral_constant<bool, true> nt;
@@ -695,12 +721,25 @@ void k_row(RowParams P) {
           float o[N];
 #pragma unroll
           for (int i = 0; i < N; ++i) o[i] = p2_value<CF>(IO::elem(r[u], i), Q);
-          if (!((bits >> u) & 1u)) RowOut<TO, N>::store(orow, (j0 + u) * B + t, o);
+          const bool marked = (bits >> u) & 1u;
+          if (!marked) RowOut<TO, N>::store(orow, (j0 + u) * B + t, o);
+          if (KIND == KIND_CENTER && marked) {
+            float v[N];
+            IO::unpack(r[u], v);
+            capture((j0 + u) * B + t, v);
+          }
         }
       }
       for (int j = Jt; j < J; ++j) {
-        if (is_marked(j)) continue;
+        const bool marked = is_marked(j);
+        if (KIND != KIND_CENTER && marked) continue;
         const Raw r = load_one(j, nt);
+        if (marked) {
+          float v[N];
+          IO::unpack(r, v);
+          capture(j * B + t, v);
+          continue;
+        }
         float o[N];
 #pragma unroll
         for (int i = 0; i < N; ++i) o[i] = p2_value<CF>(IO::elem(r, i), Q);
@@ -709,31 +748,35 @@ void k_row(RowParams P) {
     };
     if (careful) stream2(std::true_type{});
     else stream2(std::false_type{});
-    // Marked vectors and the partial last one: exact values, in float64.
-    for_marked([&](int n, const float (&v)[N], int cnt) {
+    if (KIND == KIND_CENTER) {
+      if (rem_owner) capture_partial();
+      __syncthreads();
+    }
+    // Listed vectors: recorded ids take hout, the sampled id outside H the
+    // float64 value alpha p_a + scale, every other element the streamed
+    // value; one thread per listed vector, one store per vector.
+    for (int e = t; e < n_ent; e += B) {
+      const int n = lvec[e];
       float o[N];
 #pragma unroll
       for (int i = 0; i < N; ++i) {
         const int id = n * N + i;
+        const float z = lval[e * N + i];
         float val = 0.f;
-        if (i < cnt) {
+        if (id < V) {
           const int slot = idset_find(hkey, hval, hmask, hshift, id);
-          if (slot >= 0) {
-            val = hout[slot];
-          } else {
-            double x = alpha * exp2((double)v[i] * c64 - F);
-            if (id == a) x += scale;
-            val = (float)x;
-          }
+          if (slot >= 0) val = hout[slot];
+          else if (id == a) val = (float)(alpha * exp2((double)z * c64 - F) + scale);
+          else val = p2_value<true>(z, Q);
         }
         o[i] = val;
       }
-      if (cnt == N) {
+      if (n < n_full) {
         RowOut<TO, N>::store(orow, n, o);
       } else {
-        for (int i = 0; i < cnt; ++i) store_elem(orow, (int64_t)n * N + i, o[i]);
+        for (int i = 0; i < rem; ++i) store_elem(orow, (int64_t)n * N + i, o[i]);
       }
-    });
+    }
   }
 
   __syncthreads();
