@@ -53,8 +53,9 @@ enum sc_status {
   SC_OK = 0,
   SC_ERR_ARG = -1,          /* invalid argument (checked before any HIP call) */
   SC_ERR_UNSUPPORTED = -2,  /* valid but outside what the library supports    */
-  SC_ERR_HIP = -3           /* a HIP runtime call or kernel launch failed       */
-};
+  SC_ERR_HIP = -3,          /* a HIP runtime call or kernel launch failed       */
+  SC_ERR_TOO_LARGE = -4     /* beyond the static workspace of an entry point    */
+};                          /* that allocates nothing (see below)              */
 
 /* Element types of logits and of the full-vocabulary output row. */
 enum sc_dtype { SC_F32 = 0, SC_BF16 = 1 };
@@ -294,6 +295,29 @@ int sc_logprobs_lmhead(const void* hidden, int64_t n_rows, int32_t d,
                        float temperature, float* row_stats, int32_t* row_idx,
                        float* head_logp, void* workspace, int64_t workspace_bytes,
                        uint32_t* dev_status, void* stream);
+
+/*
+ * sc_logprobs_lmhead_static -- sc_logprobs_lmhead for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same arguments without the workspace, the same
+ * kernels and bit-identical outputs.  Its workspace is a static device array
+ * of SC_STATIC_SCRATCH_BYTES per GPU, held until the process ends; the call
+ * allocates nothing.  Requests whose sc_lmhead_workspace_size exceeds it
+ * return SC_ERR_TOO_LARGE before any HIP call (at vocab = 248,320 and
+ * k = 128 that is more than 11,881 rows: call it on chunks of rows).  Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (concurrent streams or threads) race and must be serialised by the caller.
+ */
+#define SC_STATIC_SCRATCH_BYTES ((int64_t)64 << 20)
+
+int sc_logprobs_lmhead_static(const void* hidden, int64_t n_rows, int32_t d,
+                              int64_t hidden_stride, const void* weight,
+                              int64_t vocab, int64_t weight_stride,
+                              const int32_t* head_ids, int32_t k,
+                              const int32_t* sampled, const int32_t* resp_idx,
+                              float temperature, float* row_stats,
+                              int32_t* row_idx, float* head_logp,
+                              uint32_t* dev_status, void* stream);
 
 /*
  * sc_lmhead_logits -- the logits X W^T of the fused kernel's GEMM, written as

@@ -13,6 +13,8 @@ namespace {
 
 constexpr int64_t kMaxI32 = 2147483647;
 constexpr int kMaxK = 1024;
+static_assert(sc::kStaticScratchBytes == (size_t)SC_STATIC_SCRATCH_BYTES,
+              "the static workspace size is declared twice");
 constexpr size_t kMaxLds = 160 * 1024;  // gfx950 LDS per compute unit
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -336,26 +338,24 @@ int64_t sc_lmhead_workspace_size(int64_t n_rows, int64_t vocab, int32_t k) {
   return (int64_t)lm_workspace(n_rows, vocab, k, nullptr, nullptr);
 }
 
-int sc_logprobs_lmhead(const void* hidden, int64_t n_rows, int32_t d, int64_t hidden_stride,
-                       const void* weight, int64_t vocab, int64_t weight_stride,
-                       const int32_t* head_ids, int32_t k, const int32_t* sampled,
-                       const int32_t* resp_idx, float temperature, float* row_stats,
-                       int32_t* row_idx, float* head_logp, void* workspace,
-                       int64_t workspace_bytes, uint32_t* dev_status, void* stream) {
-  sc::LmParams P{};
+namespace {
+
+// Argument checks of the LM-head statistics entry points (no HIP call).
+int check_lmhead_stats(sc::LmParams& P, const void* hidden, int64_t n_rows, int32_t d,
+                       int64_t hidden_stride, const void* weight, int64_t vocab,
+                       int64_t weight_stride, const int32_t* head_ids, int32_t k,
+                       const int32_t* sampled, const int32_t* resp_idx, float temperature,
+                       float* row_stats, int32_t* row_idx, float* head_logp,
+                       uint32_t* dev_status) {
   int st = check_lm(P, hidden, n_rows, d, hidden_stride, weight, vocab, weight_stride);
   if (st != SC_OK) return st;
   if (k < 1 || k > kMaxK || (int64_t)k > vocab) return SC_ERR_ARG;
   if (!(std::isfinite(temperature) && temperature > 0.f)) return SC_ERR_ARG;
-  if (!head_ids || !sampled || !row_stats || !row_idx || !workspace) return SC_ERR_ARG;
+  if (!head_ids || !sampled || !row_stats || !row_idx) return SC_ERR_ARG;
   if (!aligned(head_ids, 4) || !aligned(sampled, 4) || !aligned(row_stats, 4) ||
-      !aligned(row_idx, 4) || !aligned(workspace, 256) ||
-      (head_logp && !aligned(head_logp, 4)) || (resp_idx && !aligned(resp_idx, 4)) ||
-      (dev_status && !aligned(dev_status, 4)))
+      !aligned(row_idx, 4) || (head_logp && !aligned(head_logp, 4)) ||
+      (resp_idx && !aligned(resp_idx, 4)) || (dev_status && !aligned(dev_status, 4)))
     return SC_ERR_ARG;
-  const size_t need = lm_workspace(n_rows, vocab, k, nullptr, nullptr);
-  if (workspace_bytes < 0 || (size_t)workspace_bytes < need) return SC_ERR_ARG;
-  lm_workspace(n_rows, vocab, k, &P, static_cast<char*>(workspace));
   P.c = (float)(1.4426950408889634 / (double)temperature);
   P.head_ids = head_ids;
   P.k = k;
@@ -365,7 +365,48 @@ int sc_logprobs_lmhead(const void* hidden, int64_t n_rows, int32_t d, int64_t hi
   P.row_idx = row_idx;
   P.head_logp = head_logp;
   P.dev_status = dev_status;
+  return SC_OK;
+}
+
+}  // namespace
+
+int sc_logprobs_lmhead(const void* hidden, int64_t n_rows, int32_t d, int64_t hidden_stride,
+                       const void* weight, int64_t vocab, int64_t weight_stride,
+                       const int32_t* head_ids, int32_t k, const int32_t* sampled,
+                       const int32_t* resp_idx, float temperature, float* row_stats,
+                       int32_t* row_idx, float* head_logp, void* workspace,
+                       int64_t workspace_bytes, uint32_t* dev_status, void* stream) {
+  sc::LmParams P{};
+  int st = check_lmhead_stats(P, hidden, n_rows, d, hidden_stride, weight, vocab, weight_stride,
+                              head_ids, k, sampled, resp_idx, temperature, row_stats, row_idx,
+                              head_logp, dev_status);
+  if (st != SC_OK) return st;
+  if (!workspace || !aligned(workspace, 256)) return SC_ERR_ARG;
+  const size_t need = lm_workspace(n_rows, vocab, k, nullptr, nullptr);
+  if (workspace_bytes < 0 || (size_t)workspace_bytes < need) return SC_ERR_ARG;
+  lm_workspace(n_rows, vocab, k, &P, static_cast<char*>(workspace));
   if (n_rows == 0) return SC_OK;
+  hipError_t e = sc::launch_lmhead(P, 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SC_OK : SC_ERR_HIP;
+}
+
+int sc_logprobs_lmhead_static(const void* hidden, int64_t n_rows, int32_t d,
+                              int64_t hidden_stride, const void* weight, int64_t vocab,
+                              int64_t weight_stride, const int32_t* head_ids, int32_t k,
+                              const int32_t* sampled, const int32_t* resp_idx,
+                              float temperature, float* row_stats, int32_t* row_idx,
+                              float* head_logp, uint32_t* dev_status, void* stream) {
+  sc::LmParams P{};
+  int st = check_lmhead_stats(P, hidden, n_rows, d, hidden_stride, weight, vocab, weight_stride,
+                              head_ids, k, sampled, resp_idx, temperature, row_stats, row_idx,
+                              head_logp, dev_status);
+  if (st != SC_OK) return st;
+  if (lm_workspace(n_rows, vocab, k, nullptr, nullptr) > sc::kStaticScratchBytes)
+    return SC_ERR_TOO_LARGE;
+  if (n_rows == 0) return SC_OK;
+  void* ws = nullptr;
+  if (sc::static_scratch(&ws) != hipSuccess) return SC_ERR_HIP;
+  lm_workspace(n_rows, vocab, k, &P, static_cast<char*>(ws));
   hipError_t e = sc::launch_lmhead(P, 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SC_OK : SC_ERR_HIP;
 }
@@ -626,6 +667,9 @@ const char* sc_status_string(int status) {
     case SC_ERR_ARG: return "SC_ERR_ARG: invalid argument";
     case SC_ERR_UNSUPPORTED: return "SC_ERR_UNSUPPORTED: outside what the library supports";
     case SC_ERR_HIP: return "SC_ERR_HIP: HIP runtime call or kernel launch failed";
+    case SC_ERR_TOO_LARGE:
+      return "SC_ERR_TOO_LARGE: the request needs more than the static workspace of "
+             "sc_logprobs_lmhead_static (SC_STATIC_SCRATCH_BYTES per GPU)";
     default: return "unknown sc_status";
   }
 }

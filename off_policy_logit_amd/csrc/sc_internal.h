@@ -137,6 +137,11 @@ struct LmParams {
   uint32_t* dev_status;
 };
 
+// Static workspace of sc_logprobs_lmhead_static (bytes per GPU).
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+// Its device address on the current device (looked up once per device).
+hipError_t static_scratch(void** ptr);
+
 // mode 0: statistics (stage, main, finalize); 1: fp32 logits; 2: bf16 dLogits
 // (main, then the recorded / sampled ids).
 hipError_t launch_lmhead(const LmParams& P, int mode, hipStream_t s);

@@ -34,6 +34,8 @@
 #include "sc_device.h"
 #include "sc_internal.h"
 
+#include <mutex>
+
 namespace sc {
 namespace {
 
@@ -795,6 +797,36 @@ hipError_t launch_transpose_bf16(const uint16_t* src, int64_t rows, int64_t cols
   hipLaunchKernelGGL(k_transpose_bf16, grid, dim3(256), 0, s, src, rows, cols, ss, dst, rpad, ds,
                      vec);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Workspace of sc_logprobs_lmhead_static, the entry point for callers that
+// cannot allocate: one static device array per GPU, shared by every call on
+// that GPU (calls that overlap on one GPU race; nothing in it needs clearing,
+// since each kernel writes every workspace entry it later reads).
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; host code uses this address,
+// never the array's name (which stands for the symbol, not device memory).
+hipError_t static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_lmhead(const LmParams& P, int mode, hipStream_t s) {

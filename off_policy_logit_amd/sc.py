@@ -17,7 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsc.so")
 
 # Mirrors of the enums in include/sc.h
-SC_OK, SC_ERR_ARG, SC_ERR_UNSUPPORTED, SC_ERR_HIP = 0, -1, -2, -3
+SC_OK, SC_ERR_ARG, SC_ERR_UNSUPPORTED, SC_ERR_HIP, SC_ERR_TOO_LARGE = 0, -1, -2, -3, -4
+STATIC_SCRATCH_BYTES = 64 << 20
 SC_F32, SC_BF16 = 0, 1
 DEV_BAD_ID, DEV_DUP_ID, DEV_BAD_SAMPLED, DEV_NONFINITE, DEV_BAD_RESP = 1, 2, 4, 8, 16
 ROW_DLOGITS, ROW_SCORE, ROW_CORRECTION = 0, 1, 2
@@ -50,6 +51,8 @@ _SIGS = {
     "sc_lmhead_workspace_size": [_i64, _i64, _i32],
     "sc_logprobs_lmhead": [_vp, _i64, _i32, _i64, _vp, _i64, _i64, _vp, _i32, _vp,
                            _vp, _f32, _vp, _vp, _vp, _vp, _i64, _vp, _vp],
+    "sc_logprobs_lmhead_static": [_vp, _i64, _i32, _i64, _vp, _i64, _i64, _vp, _i32, _vp,
+                                  _vp, _f32, _vp, _vp, _vp, _vp, _vp],
     "sc_lmhead_logits": [_vp, _i64, _i32, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
     "sc_record": [_vp, ctypes.c_int, _i64, _i64, _i64, _f32, _i32, _vp, _vp, _vp, _vp,
                   _vp, _vp],
@@ -312,6 +315,29 @@ def logprobs_lmhead(hidden, weight, head_ids, sampled, resp_idx=None,
         _ptr(sampled), _ptr(resp_idx), float(temperature), _ptr(out["row_stats"]),
         _ptr(out["row_idx"]), _ptr(out.get("head_logp")), _ptr(workspace),
         workspace.numel(), _ptr(dev_status), _stream(stream)))
+    return out
+
+
+def logprobs_lmhead_static(hidden, weight, head_ids, sampled, resp_idx=None,
+                           temperature=1.0, out=None, dev_status=None, stream=None):
+    """sc_logprobs_lmhead_static: logprobs_lmhead() on the library's static
+    per-GPU workspace; allocates nothing when `out` is given.  Calls that
+    overlap on one GPU race."""
+    n, d, hs = _bf16_matrix(hidden, "hidden")
+    V, dw, ws = _bf16_matrix(weight, "weight")
+    if dw != d:
+        raise ValueError("hidden and weight disagree on d")
+    _need(head_ids, torch.int32, "head_ids")
+    _need(sampled, torch.int32, "sampled")
+    if resp_idx is not None:
+        _need(resp_idx, torch.int32, "resp_idx")
+    k = head_ids.shape[1]
+    out = out or _alloc_stats(n, k, hidden.device)
+    _check(lib().sc_logprobs_lmhead_static(
+        _ptr(hidden), n, d, hs, _ptr(weight), V, ws, _ptr(head_ids), k,
+        _ptr(sampled), _ptr(resp_idx), float(temperature), _ptr(out["row_stats"]),
+        _ptr(out["row_idx"]), _ptr(out.get("head_logp")), _ptr(dev_status),
+        _stream(stream)))
     return out
 
 

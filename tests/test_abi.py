@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = sc.lib()
-    for code in (OK, ARG, UNSUP, sc.SC_ERR_HIP):
+    for code in (OK, ARG, UNSUP, sc.SC_ERR_HIP, sc.SC_ERR_TOO_LARGE):
         assert L.sc_status_string(code).startswith(b"SC_")
     assert L.sc_version() >= 100
 
@@ -191,6 +191,41 @@ def lmhead(**kw):
 ])
 def test_lmhead_rejects_bad_arguments(kw):
     assert lmhead(**kw) == ARG
+
+
+def lmhead_static(**kw):
+    a = dict(x=FAKE, n=300, d=256, xs=256, w=FAKE, V=1000, ws=256, ids=FAKE, k=16,
+             sampled=FAKE, resp=NULL, T=1.0, stats=FAKE, idx=FAKE, hlp=NULL,
+             dev=NULL, stream=NULL)
+    a.update(kw)
+    return sc.lib().sc_logprobs_lmhead_static(
+        a["x"], a["n"], a["d"], a["xs"], a["w"], a["V"], a["ws"], a["ids"], a["k"],
+        a["sampled"], a["resp"], a["T"], a["stats"], a["idx"], a["hlp"], a["dev"],
+        a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=NULL), dict(w=NULL), dict(ids=NULL), dict(sampled=NULL), dict(stats=NULL),
+    dict(idx=NULL), dict(n=-1), dict(V=0), dict(d=0), dict(xs=255), dict(x=FAKE2),
+    dict(k=0), dict(k=1001), dict(T=0.0), dict(T=float("nan")),
+])
+def test_lmhead_static_rejects_bad_arguments(kw):
+    assert lmhead_static(**kw) == ARG
+
+
+def test_lmhead_static_limit_is_checked_before_any_hip_call():
+    L = sc.lib()
+    V, k = 248_320, 128
+    lim = sc.STATIC_SCRATCH_BYTES
+    assert L.sc_lmhead_workspace_size(11_881, V, k) <= lim
+    assert L.sc_lmhead_workspace_size(11_882, V, k) > lim
+    # Rejected on the host: no device is touched (there is none here).
+    big = dict(n=11_882, d=4096, xs=4096, ws=4096, V=V, k=k)
+    assert lmhead_static(**big) == sc.SC_ERR_TOO_LARGE
+    assert lmhead_static(**dict(big, n=(1 << 31) - 1)) == sc.SC_ERR_TOO_LARGE
+    assert b"static workspace" in L.sc_status_string(sc.SC_ERR_TOO_LARGE)
+    assert lmhead_static(n=0) == OK
+    assert lmhead_static(n=0, d=200, xs=200, ws=200) == UNSUP
 
 
 def test_lmhead_d_must_be_a_multiple_of_64():
