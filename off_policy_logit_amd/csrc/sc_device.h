@@ -135,13 +135,32 @@ SC_DEV float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16)
 SC_DEV uint32_t f32_to_bf16(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
 }
+// Two values in one v_cvt_pk_bf16_f32 (the pair converted as a vector).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 SC_DEV uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+
+// Buffer resource over the `bytes` bytes at p (raw addressing, gfx9 format
+// word).  A buffer access whose offset lies at or beyond `bytes` reads zeros
+// and drops a store, so the row streams read 16-byte vectors through one
+// resource per row, and a store is skipped on purpose by giving it an offset
+// of kSkip or more (bytes stays below 2^31).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kSkip = 0x80000000u;
+SC_DEV rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+// Cache policy of a buffer access: 0 default, 2 nontemporal (last use).
+constexpr int kNT = 2;
 
 // RowIO<T, VECTOR>: `raw` is one vector as loaded (16 bytes, or one element
 // on the scalar path); load() fetches vector n of a row, unpack() widens it to
-// fp32 and ninf() is a vector of -inf (padding of a partial tile).
+// fp32 and ninf() is a vector of -inf (padding of a partial tile).  On the
+// vector path bload() fetches the vector at byte offset `off` of a row
+// resource.
 template <typename T, bool VECTOR> struct RowIO;
 
 template <> struct RowIO<uint16_t, true> {   // bf16, 16-byte vectors
@@ -151,6 +170,10 @@ template <> struct RowIO<uint16_t, true> {   // bf16, 16-byte vectors
   static SC_DEV raw load(const uint16_t* row, int64_t n) {
     const u32x4* p = reinterpret_cast<const u32x4*>(row) + n;
     return NT ? __builtin_nontemporal_load(p) : *p;
+  }
+  template <int AUX>
+  static SC_DEV raw bload(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
   }
   static SC_DEV void unpack(const raw& w, float (&v)[N]) {
 #pragma unroll
@@ -171,6 +194,10 @@ template <> struct RowIO<float, true> {      // fp32, 16-byte vectors
   static SC_DEV raw load(const float* row, int64_t n) {
     const f32x4* p = reinterpret_cast<const f32x4*>(row) + n;
     return NT ? __builtin_nontemporal_load(p) : *p;
+  }
+  template <int AUX>
+  static SC_DEV raw bload(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
   }
   static SC_DEV void unpack(const raw& w, float (&v)[N]) {
 #pragma unroll
@@ -202,43 +229,72 @@ SC_DEV float load_elem(const uint16_t* row, int64_t i) { return bf16_to_f32(row[
 SC_DEV float load_elem(const float* row, int64_t i) { return row[i]; }
 
 // Store N output values of one vector (bf16 bits or fp32), nontemporal.
+// bstore() writes them at byte offset `off` of an output-row resource
+// (BYTES = N x the element size); off >= kSkip drops the store.
 template <typename O, int N> struct RowOut;
 template <> struct RowOut<uint16_t, 8> {
-  static SC_DEV void store(uint16_t* row, int64_t n, const float (&v)[8]) {
+  static constexpr uint32_t BYTES = 16;
+  static SC_DEV u32x4 pack(const float (&v)[8]) {
     u32x4 w;
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(row) + n);
+    return w;
+  }
+  static SC_DEV void store(uint16_t* row, int64_t n, const float (&v)[8]) {
+    __builtin_nontemporal_store(pack(v), reinterpret_cast<u32x4*>(row) + n);
+  }
+  static SC_DEV void bstore(rsrc_t r, uint32_t off, const float (&v)[8]) {
+    __builtin_amdgcn_raw_buffer_store_b128(pack(v), r, off, 0, kNT);
   }
 };
 template <> struct RowOut<uint16_t, 4> {
-  static SC_DEV void store(uint16_t* row, int64_t n, const float (&v)[4]) {
+  static constexpr uint32_t BYTES = 8;
+  static SC_DEV u32x2 pack(const float (&v)[4]) {
     u32x2 w;
     w[0] = pack_bf16x2(v[0], v[1]);
     w[1] = pack_bf16x2(v[2], v[3]);
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(row) + n);
+    return w;
+  }
+  static SC_DEV void store(uint16_t* row, int64_t n, const float (&v)[4]) {
+    __builtin_nontemporal_store(pack(v), reinterpret_cast<u32x2*>(row) + n);
+  }
+  static SC_DEV void bstore(rsrc_t r, uint32_t off, const float (&v)[4]) {
+    __builtin_amdgcn_raw_buffer_store_b64(pack(v), r, off, 0, kNT);
   }
 };
 template <> struct RowOut<float, 8> {
+  static constexpr uint32_t BYTES = 32;
   static SC_DEV void store(float* row, int64_t n, const float (&v)[8]) {
     f32x4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
     f32x4* p = reinterpret_cast<f32x4*>(row) + 2 * n;
     __builtin_nontemporal_store(a, p);
     __builtin_nontemporal_store(b, p + 1);
   }
+  static SC_DEV void bstore(rsrc_t r, uint32_t off, const float (&v)[8]) {
+    const f32x4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, a), r, off, 0, kNT);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, b), r, off + 16u, 0, kNT);
+  }
 };
 template <> struct RowOut<float, 4> {
+  static constexpr uint32_t BYTES = 16;
   static SC_DEV void store(float* row, int64_t n, const float (&v)[4]) {
     f32x4 a = {v[0], v[1], v[2], v[3]};
     __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(row) + n);
   }
+  static SC_DEV void bstore(rsrc_t r, uint32_t off, const float (&v)[4]) {
+    const f32x4 a = {v[0], v[1], v[2], v[3]};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, a), r, off, 0, kNT);
+  }
 };
 template <> struct RowOut<uint16_t, 1> {
+  static constexpr uint32_t BYTES = 2;
   static SC_DEV void store(uint16_t* row, int64_t n, const float (&v)[1]) {
     row[n] = (uint16_t)f32_to_bf16(v[0]);
   }
 };
 template <> struct RowOut<float, 1> {
+  static constexpr uint32_t BYTES = 4;
   static SC_DEV void store(float* row, int64_t n, const float (&v)[1]) { row[n] = v[0]; }
 };
 

@@ -212,17 +212,44 @@ void k_row(RowParams P) {
     // Vector j of this thread is row vector j * B + t.  Every thread owns at
     // least Jmin vectors, so tiles of kU vectors below Jt are loaded with the
     // same unconditional code by the whole workgroup; the remaining J - Jt
-    // vectors of a thread (fewer than kU + 1) are handled one at a time.
+    // vectors of a thread (fewer than kU + 1) are handled one at a time.  On
+    // the vector path the row's full vectors are read through a buffer
+    // resource over exactly those bytes.
     const int Jmin = n_full / B;
     const int Jt = (Jmin / kU) * kU;
-    auto load_tile = [&](Raw (&r)[kU], int j0, auto nt) {
-      const int64_t n0 = (int64_t)j0 * B + t;
-#pragma unroll
-      for (int u = 0; u < kU; ++u)
-        r[u] = IO::template load<decltype(nt)::value>(zrow, n0 + u * B);
+    const rsrc_t zr = make_rsrc(zrow, VECTOR ? (uint32_t)n_full * 16u : 0u);
+    auto ld = [&](int j, auto ntc) -> Raw {
+      constexpr bool NT = decltype(ntc)::value;
+      if constexpr (VECTOR)
+        return IO::template bload<NT ? kNT : 0>(zr, (uint32_t)(j * B + t) * 16u);
+      else
+        return IO::template load<NT>(zrow, (int64_t)j * B + t);
     };
-    auto load_one = [&](int j, auto nt) -> Raw {
-      return IO::template load<decltype(nt)::value>(zrow, (int64_t)j * B + t);
+    // A tile's loads.  The stream below also fetches the tile after the
+    // thread's last full one, never consumed: on the vector path its
+    // vectors beyond the row read zeros without a memory access, on the
+    // scalar path the index is held at the thread's last vector.
+    auto load_tile = [&](Raw (&r)[kU], int j0, auto ntc) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) r[u] = ld(VECTOR ? j0 + u : min(j0 + u, J - 1), ntc);
+    };
+    // The thread's full tiles in order, software pipelined: the loads of the
+    // next tile are issued before the current one is consumed, so that every
+    // wave keeps a tile of loads in flight while it computes.  The loads
+    // are unconditional: a load under a branch would leave the compiler's
+    // wait counts at the join unable to tell the tiles apart, and it would
+    // wait for the prefetch as well.
+    auto stream_tiles = [&](auto ntc, auto&& consume) {
+      if (Jt == 0) return;
+      Raw cur[kU];
+      load_tile(cur, 0, ntc);
+      for (int j0 = 0; j0 < Jt; j0 += kU) {
+        Raw nxt[kU];
+        load_tile(nxt, j0 + kU, ntc);
+        consume(cur, j0);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) cur[u] = nxt[u];
+      }
     };
     auto tile_bits = [&](int j0) -> uint32_t {
       return (bitmap[(j0 >> 5) * B + t] >> (j0 & 31)) & ((1u << kU) - 1u);
@@ -298,18 +325,16 @@ void k_row(RowParams P) {
     if (KIND != KIND_CENTER) {
       // ---------------------------------------------------------- pass 1
       // m_t: running max of every vector (argmax; starts at -FLT_MAX so that
-      // all -inf vectors never count); am_raw / am_vec: the vector that last
-      // raised it (strictly, so the first of equal maxima is kept).  r_t:
-      // running max of the unmarked vectors, E_t = ref_exp(r_t): the exponent
-      // reference of s_t = sum 2^(z c - E_t) (float64) and of
-      // h_t = sum 2^(z c - E_t) (z c - E_t) over unmarked vectors.  When E_t
-      // rises by D, s_t scales by 2^-D and h_t by 2^-D after subtracting
-      // D s_t, both exactly.
-      float m_t = -FLT_MAX, r_t = -FLT_MAX, E_t = ref_exp(-FLT_MAX, c_hi);
+      // all -inf vectors never count); am_vec: the thread's vector that last
+      // raised it (strictly, so the first of equal maxima is kept).
+      // E_t = ref_exp(m_t): the exponent reference of s_t = sum 2^(z c - E_t)
+      // (float64) and of h_t = sum 2^(z c - E_t) (z c - E_t) over unmarked
+      // vectors.  When E_t rises by D, s_t scales by 2^-D and h_t by 2^-D
+      // after subtracting D s_t, both exactly.
+      float m_t = -FLT_MAX, E_t = ref_exp(-FLT_MAX, c_hi);
       double s_t = 0.0;
       float h_t = 0.f;
       int am_vec = -1;
-      Raw am_raw = IO::ninf();
       int am_direct = -1;
       auto rebase = [&](float E_new) {
         const float D = E_new - E_t;                 // >= 0
@@ -337,70 +362,68 @@ void k_row(RowParams P) {
           for (int i = 0; i + w < N; i += 2 * w) e[i] += e[i + w];
         acc = e[0];
       };
-      // Branch-free: marked vectors are summed too and the sum is dropped
-      // (they are resolved element by element after the stream).  The
-      // maxima are raised once per group of kG vectors, so one rebase serves
-      // kG vectors.
+      // One vector's maximum, its argmax bookkeeping and, when marked, its
+      // capture to the list.
+      auto scan_vec = [&](const float (&v)[N], int j, bool marked, float& m_run) {
+        float vm = v[0];
+#pragma unroll
+        for (int i = 1; i < N; ++i) vm = fmaxf(vm, v[i]);
+        am_vec = vm > m_run ? j : am_vec;          // strictly: first of equal maxima
+        m_run = fmaxf(m_run, vm);
+        if (marked) capture(j * B + t, v);
+      };
+      // Branch-free sums: marked vectors are summed too and the sum is
+      // dropped (they are resolved element by element after the stream).
+      // The maximum is raised once per group of kG vectors, so one rebase
+      // serves kG vectors, and each group's sums are added in fp32 first.
       constexpr int kG = kU >= 4 ? 4 : kU;
       auto process = [&](const Raw (&r)[kU], int j0) {
         const uint32_t bits = tile_bits(j0);
 #pragma unroll
         for (int u0 = 0; u0 < kU; u0 += kG) {
           float v[kG][N];
-          float m_run = m_t, r_run = r_t;
+          float m_run = m_t;
 #pragma unroll
           for (int u = 0; u < kG; ++u) {
             IO::unpack(r[u0 + u], v[u]);
-            float vm = v[u][0];
-#pragma unroll
-            for (int i = 1; i < N; ++i) vm = fmaxf(vm, v[u][i]);
-            am_raw = keep_if(vm > m_run, r[u0 + u], am_raw);
-            am_vec = vm > m_run ? j0 + u0 + u : am_vec;   // strictly: first of equal maxima
-            m_run = fmaxf(m_run, vm);
-            const bool marked = (bits >> (u0 + u)) & 1u;
-            r_run = fmaxf(r_run, marked ? -FLT_MAX : vm);
-            if (marked) capture((j0 + u0 + u) * B + t, v[u]);
+            scan_vec(v[u], j0 + u0 + u, (bits >> (u0 + u)) & 1u, m_run);
           }
           m_t = m_run;
-          r_t = r_run;
-          rebase(ref_exp(r_t, c_hi));
+          rebase(ref_exp(m_t, c_hi));
+          float sg = 0.f, hg = 0.f;
 #pragma unroll
           for (int u = 0; u < kG; ++u) {
             float acc, acch;
             vec_sums(v[u], acc, acch);
             const bool marked = (bits >> (u0 + u)) & 1u;
-            s_t += (double)(marked ? 0.f : acc);
-            h_t += marked ? 0.f : acch;
+            sg += marked ? 0.f : acc;
+            hg += marked ? 0.f : acch;
           }
+          s_t += (double)sg;
+          h_t += hg;
         }
       };
       {
         std::integral_constant<bool, KIND == KIND_LOGPROBS> nt;
-        for (int j0 = 0; j0 < Jt; j0 += kU) {
-          Raw r[kU];
-          load_tile(r, j0, nt);
-          process(r, j0);
-        }
+        stream_tiles(nt, process);
         for (int j = Jt; j < J; ++j) {
           float v[N];
-          const Raw rv = load_one(j, nt);
-          IO::unpack(rv, v);
-          float vm = v[0];
-#pragma unroll
-          for (int i = 1; i < N; ++i) vm = fmaxf(vm, v[i]);
-          am_raw = keep_if(vm > m_t, rv, am_raw);
-          am_vec = vm > m_t ? j : am_vec;
-          m_t = fmaxf(m_t, vm);
+          IO::unpack(ld(j, nt), v);
           const bool marked = is_marked(j);
-          r_t = fmaxf(r_t, marked ? -FLT_MAX : vm);
-          if (marked) capture(j * B + t, v);
-          rebase(ref_exp(r_t, c_hi));
+          float m_run = m_t;
+          scan_vec(v, j, marked, m_run);
+          m_t = m_run;
+          rebase(ref_exp(m_t, c_hi));
           float acc, acch;
           vec_sums(v, acc, acch);
           s_t += (double)(marked ? 0.f : acc);
           h_t += marked ? 0.f : acch;
         }
       }
+      // The element index of the thread's maximum: the first element equal
+      // to m_t in the vector that raised it, read again (one load).
+      Raw am_raw = IO::ninf();
+      if (am_vec >= 0) am_raw = ld(am_vec, std::false_type{});
       // A -inf logit among this thread's unmarked vectors left h_t NaN (its
       // term 0 * -inf): recompute the entropy sum against the final E_t with
       // the term clamped to 0, reading the thread's vectors again.  A NaN
@@ -412,7 +435,7 @@ void k_row(RowParams P) {
         for (int j = 0; j < J; ++j) {
           if (is_marked(j)) continue;
           float v[N];
-          IO::unpack(load_one(j, std::false_type{}), v);
+          IO::unpack(ld(j, std::false_type{}), v);
 #pragma unroll
           for (int i = 0; i < N; ++i) {
             const float y = fmaf(v[i], c_lo, fmaf(v[i], c_hi, -E_t));
@@ -430,9 +453,6 @@ void k_row(RowParams P) {
           if (z > m_t) { m_t = z; am_direct = n_full * N + i; }
         }
       }
-      // Element index of my maximum: the first element equal to m_t in the
-      // vector that raised it (kept in registers during the stream), unless
-      // the partial vector raised it last.
       int am_t = 0x7fffffff;
       if (am_direct >= 0) {
         am_t = am_direct;
@@ -708,13 +728,20 @@ void k_row(RowParams P) {
 
     // Stream the row; marked vectors are not stored here but from the list
     // below (the sc_center kind lists them now, as the stream meets them; the
-    // fused kind listed them in pass 1).
+    // fused kind listed them in pass 1).  On the vector path a marked
+    // vector's store is dropped by its offset, so the loop has no branch.
+    using RO = RowOut<TO, N>;
+    const rsrc_t orr = make_rsrc(orow, VECTOR ? (uint32_t)n_full * RO::BYTES : 0u);
+    auto put = [&](int j, bool skip, const float (&o)[N]) {
+      if constexpr (VECTOR)
+        RO::bstore(orr, skip ? kSkip : (uint32_t)(j * B + t) * RO::BYTES, o);
+      else if (!skip)
+        RO::store(orow, (int64_t)j * B + t, o);
+    };
     auto stream2 = [&](auto carefulc) {
       constexpr bool CF = decltype(carefulc)::value;
       std::integral_constant<bool, true> nt;
-      for (int j0 = 0; j0 < Jt; j0 += kU) {
-        Raw r[kU];
-        load_tile(r, j0, nt);
+      auto emit = [&](const Raw (&r)[kU], int j0) {
         const uint32_t bits = tile_bits(j0);
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
@@ -722,18 +749,19 @@ void k_row(RowParams P) {
 #pragma unroll
           for (int i = 0; i < N; ++i) o[i] = p2_value<CF>(IO::elem(r[u], i), Q);
           const bool marked = (bits >> u) & 1u;
-          if (!marked) RowOut<TO, N>::store(orow, (j0 + u) * B + t, o);
+          put(j0 + u, marked, o);
           if (KIND == KIND_CENTER && marked) {
             float v[N];
             IO::unpack(r[u], v);
             capture((j0 + u) * B + t, v);
           }
         }
-      }
+      };
+      stream_tiles(nt, emit);
       for (int j = Jt; j < J; ++j) {
         const bool marked = is_marked(j);
         if (KIND != KIND_CENTER && marked) continue;
-        const Raw r = load_one(j, nt);
+        const Raw r = ld(j, nt);
         if (marked) {
           float v[N];
           IO::unpack(r, v);
@@ -743,7 +771,7 @@ void k_row(RowParams P) {
         float o[N];
 #pragma unroll
         for (int i = 0; i < N; ++i) o[i] = p2_value<CF>(IO::elem(r, i), Q);
-        RowOut<TO, N>::store(orow, j * B + t, o);
+        put(j, false, o);
       }
     };
     if (careful) stream2(std::true_type{});
