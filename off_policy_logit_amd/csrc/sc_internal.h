@@ -36,7 +36,7 @@ namespace sc {
 #define SC_FUSED_TILE 8
 #endif
 #ifndef SC_FUSED_WAVES
-#define SC_FUSED_WAVES 3
+#define SC_FUSED_WAVES 2
 #endif
 constexpr int kKindBlock[3] = {SC_STATS_BLOCK, SC_CENTER_BLOCK, SC_FUSED_BLOCK};
 
