@@ -21,6 +21,14 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 size_t esize(int dtype) { return dtype == SC_BF16 ? 2 : 4; }
 bool dtype_ok(int d) { return d == SC_F32 || d == SC_BF16; }
 
+// log2(e) / T as fp32, as float64 and as an fp32 pair (hi + lo).
+void set_lm_temperature(sc::LmParams& P, float temperature) {
+  P.c64 = 1.4426950408889634 / (double)temperature;
+  P.c = (float)P.c64;
+  P.c_hi = P.c;
+  P.c_lo = (float)(P.c64 - (double)P.c_hi);
+}
+
 // Shared row-kernel argument checks; fills the geometry part of RowParams.
 int check_rows(sc::RowParams& P, const void* logits, bool logits_needed, int logits_dtype,
                int64_t n_rows, int64_t vocab, int64_t row_stride,
@@ -356,7 +364,7 @@ int check_lmhead_stats(sc::LmParams& P, const void* hidden, int64_t n_rows, int3
       !aligned(row_idx, 4) || (head_logp && !aligned(head_logp, 4)) ||
       (resp_idx && !aligned(resp_idx, 4)) || (dev_status && !aligned(dev_status, 4)))
     return SC_ERR_ARG;
-  P.c = (float)(1.4426950408889634 / (double)temperature);
+  set_lm_temperature(P, temperature);
   P.head_ids = head_ids;
   P.k = k;
   P.sampled = sampled;
@@ -421,7 +429,7 @@ int sc_lmhead_logits(const void* hidden, int64_t n_rows, int32_t d, int64_t hidd
   P.out = logits;
   P.os = logits_stride;
   P.out_vec = (logits_stride % 4 == 0) && aligned(logits, 16);
-  P.c = 1.f;
+  set_lm_temperature(P, 1.f);
   if (n_rows == 0) return SC_OK;
   hipError_t e = sc::launch_lmhead(P, 1, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SC_OK : SC_ERR_HIP;
@@ -495,7 +503,7 @@ int check_lm_dz(sc::LmParams& P, const int32_t* head_ids, const float* head_prob
       !aligned(advantages, 4) || !aligned(n_valid, 8) || !aligned(row_stats, 4) ||
       !aligned(row_idx, 4) || !aligned(head_logp, 4) || (resp_idx && !aligned(resp_idx, 4)))
     return SC_ERR_ARG;
-  P.c = (float)(1.4426950408889634 / (double)temperature);
+  set_lm_temperature(P, temperature);
   P.temperature = temperature;
   P.head_ids = head_ids;
   P.head_probs = head_probs;
@@ -648,7 +656,8 @@ int sc_record(const void* logits, int logits_dtype, int64_t n_rows, int64_t voca
   P.n_rows = n_rows;
   P.vocab = vocab;
   P.row_stride = row_stride;
-  P.c = (float)(1.4426950408889634 / (double)temperature);
+  P.c64 = 1.4426950408889634 / (double)temperature;
+  P.c = (float)P.c64;
   P.k = k;
   P.sampled = sampled;
   P.head_ids = head_ids;

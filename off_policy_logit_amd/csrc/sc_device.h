@@ -301,6 +301,97 @@ template <> struct RowOut<float, 1> {
 SC_DEV void store_elem(uint16_t* row, int64_t i, float v) { row[i] = (uint16_t)f32_to_bf16(v); }
 SC_DEV void store_elem(float* row, int64_t i, float v) { row[i] = v; }
 
+// Reference exponent of a running maximum x: ceil(x c_hi), an integer held in
+// a float, clamped to +-2^60 so that it stays finite while nothing finite has
+// been seen (x = -FLT_MAX) or when x is +inf (such a row is flagged).
+SC_DEV float ref_exp(float x, float c_hi) {
+  return fminf(fmaxf(ceilf(x * c_hi), -0x1p60f), 0x1p60f);
+}
+
+// Per-row constants of the pass-2 value sign(alpha) 2^((z - m) c - G):
+// G = Gint + gq + glo with Gint an integer, gq on the 2^-14 grid in (-1, 0]
+// and |glo| < 2^-14.
+struct Pass2 {
+  float m, c_hi, c_lo;
+  float gq;      // gq (as above)
+  float nglo;    // -glo ln 2
+  float scl;     // sign(alpha) 2^-Gint (NaN for a flagged row, +-0 when all values underflow)
+  float scl_lo;  // scl 2^-64, for exponents moved up by 64 (subnormal results)
+};
+
+// Pass-2 value of one logit z.  d = z - m is exact for bf16 z and m (else its
+// rounding error de comes from a two-sum).  P = RN(d c_hi) and its exact
+// residual Pe = d c_hi - P (one fma); yh = P - gq is exact because gq lies on
+// a grid no finer than P's (|P| < 2^10) and shrinks |P|.  The small remainder
+// k = ln 2 (Pe + d c_lo - glo) (|k| < 2^-14) is applied as 2^yh (1 + k), and
+// the power of two comes last, in one multiply (a single rounding when the
+// result is subnormal).  CAREFUL adds what rare rows need: -inf logits give 0
+// (not NaN), fp32 logits take the two-sum, and exponents below -96 are moved
+// up by 64 (back in the final multiply) so that the exp2 instruction, which
+// flushes results below 2^-126, keeps them.
+template <bool CAREFUL>
+SC_DEV float p2_value(float z, const Pass2& Q) {
+#pragma clang fp contract(off)
+  float d = z - Q.m;
+  float de = 0.f;
+  if (CAREFUL) {
+    const float zz = d + Q.m;          // two-sum of z and -m
+    const float mm = d - zz;
+    de = (z - zz) - (Q.m + mm);
+    de = d >= -0x1p20f ? de : 0.f;     // -inf (or a NaN row): no residual
+    d = fmaxf(d, -0x1p20f);
+  }
+  const float P = d * Q.c_hi;
+  const float Pe = fmaf(d, Q.c_hi, -P);
+  float yh = P - Q.gq;
+  float scl = Q.scl;
+  if (CAREFUL) {
+    const bool low = yh < -96.f;
+    yh = low ? yh + 64.f : yh;         // exact: the magnitude shrinks
+    scl = low ? Q.scl_lo : scl;
+  }
+  const float r = CAREFUL ? fmaf(de, Q.c_hi, Pe) : Pe;
+  const float k = fmaf(fmaf(d, Q.c_lo, r), kLn2, Q.nglo);
+  const float e = exp2_fast(yh);
+  return fmaf(e, k, e) * scl;
+}
+
+// Per-row constants for the value sign 2^((z - m) c - G), c = c_hi + c_lo:
+// G = Gint + gq + glo split as above (Gint clamped at -126 for a factor
+// beyond 2^126; G above 10^4, alpha = 0 included, makes every value a signed
+// zero; a NaN G makes every value NaN).  g returns Gint (2^20 for a row of
+// zeros, 0 for a NaN row).
+SC_DEV Pass2 pass2_setup(float m, float c_hi, float c_lo, double G, bool neg, int& g) {
+  Pass2 Q;
+  Q.m = m;
+  Q.c_hi = c_hi;
+  Q.c_lo = c_lo;
+  Q.gq = 0.f;
+  Q.nglo = 0.f;
+  Q.scl = __builtin_nanf("");
+  Q.scl_lo = Q.scl;
+  g = 0;
+  const float sgn = neg ? -1.f : 1.f;
+  if (!(G == G)) return Q;
+  G = fmax(G, -1.0e4);
+  if (G > 1.0e4) {
+    Q.scl = 0.f * sgn;
+    Q.scl_lo = Q.scl;
+    g = 1 << 20;
+    return Q;
+  }
+  double gi = ceil(G);
+  double gq = ceil((G - gi) * 16384.0) / 16384.0;   // (-1, 0]
+  const double glo = (G - gi) - gq;                 // (-2^-14, 0]
+  if (gi < -126.0) { gq += gi + 126.0; gi = -126.0; }
+  g = (int)gi;
+  Q.gq = (float)gq;
+  Q.nglo = (float)(-glo * 0.6931471805599453);
+  Q.scl = g > 160 ? 0.f * sgn : ldexpf(sgn, -g);
+  Q.scl_lo = g + 64 > 160 ? 0.f * sgn : ldexpf(sgn, -g - 64);
+  return Q;
+}
+
 // ---------------------------------------------------------------------------
 // Recorded-id set in LDS: open addressing with linear probing, id -> slot.
 // Capacity is a power of two >= 2K, so probes always reach an empty key.

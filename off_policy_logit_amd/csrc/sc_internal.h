@@ -93,7 +93,9 @@ struct LmParams {
   int64_t ws;
   int64_t n_rows, vocab;
   int d;
-  float c;               // log2(e) / T
+  float c;               // log2(e) / T (fp32)
+  double c64;            // log2(e) / T
+  float c_hi, c_lo;      // c64 = c_hi + c_lo (c_hi = c64 rounded to fp32)
   int splits, n_chunks, n_ptiles;
   int order;             // 0: row tiles vary fastest over the grid, 1: XCD groups
   int lm_pt, lm_sp;      // order 1: row tiles x splits per XCD group (lm_sp divides splits)
@@ -157,7 +159,8 @@ struct RecParams {
   int in_dtype;          // 0 fp32, 1 bf16
   int vector;            // 1: 16-byte vector path
   int64_t n_rows, vocab, row_stride;
-  float c;               // log2(e) / T
+  float c;               // log2(e) / T (fp32)
+  double c64;            // log2(e) / T
   int32_t k;
   const int32_t* sampled;
   int32_t* head_ids;

@@ -66,61 +66,6 @@ SC_DEV f32x4 keep_if(bool c, const f32x4& a, const f32x4& b) {
 SC_DEV uint32_t keep_if(bool c, uint32_t a, uint32_t b) { return c ? a : b; }
 SC_DEV float keep_if(bool c, float a, float b) { return c ? a : b; }
 
-// Reference exponent of a running maximum x: ceil(x c_hi), an integer held in
-// a float, clamped to +-2^60 so that it stays finite while nothing finite has
-// been seen (x = -FLT_MAX) or when x is +inf (such a row is flagged).
-SC_DEV float ref_exp(float x, float c_hi) {
-  return fminf(fmaxf(ceilf(x * c_hi), -0x1p60f), 0x1p60f);
-}
-
-// Per-row constants of the pass-2 value sign(alpha) 2^((z - m) c - G):
-// G = Gint + gq + glo with Gint an integer, gq on the 2^-14 grid in (-1, 0]
-// and |glo| < 2^-14.
-struct Pass2 {
-  float m, c_hi, c_lo;
-  float gq;      // gq (as above)
-  float nglo;    // -glo ln 2
-  float scl;     // sign(alpha) 2^-Gint (NaN for a flagged row, +-0 when all values underflow)
-  float scl_lo;  // scl 2^-64, for exponents moved up by 64 (subnormal results)
-};
-
-// Pass-2 value of one logit z.  d = z - m is exact for bf16 z and m (else its
-// rounding error de comes from a two-sum).  P = RN(d c_hi) and its exact
-// residual Pe = d c_hi - P (one fma); yh = P - gq is exact because gq lies on
-// a grid no finer than P's (|P| < 2^10) and shrinks |P|.  The small remainder
-// k = ln 2 (Pe + d c_lo - glo) (|k| < 2^-14) is applied as 2^yh (1 + k), and
-// the power of two comes last, in one multiply (a single rounding when the
-// result is subnormal).  CAREFUL adds what rare rows need: -inf logits give 0
-// (not NaN), fp32 logits take the two-sum, and exponents below -96 are moved
-// up by 64 (back in the final multiply) so that the exp2 instruction, which
-// flushes results below 2^-126, keeps them.
-template <bool CAREFUL>
-SC_DEV float p2_value(float z, const Pass2& Q) {
-#pragma clang fp contract(off)
-  float d = z - Q.m;
-  float de = 0.f;
-  if (CAREFUL) {
-    const float zz = d + Q.m;          // two-sum of z and -m
-    const float mm = d - zz;
-    de = (z - zz) - (Q.m + mm);
-    de = d >= -0x1p20f ? de : 0.f;     // -inf (or a NaN row): no residual
-    d = fmaxf(d, -0x1p20f);
-  }
-  const float P = d * Q.c_hi;
-  const float Pe = fmaf(d, Q.c_hi, -P);
-  float yh = P - Q.gq;
-  float scl = Q.scl;
-  if (CAREFUL) {
-    const bool low = yh < -96.f;
-    yh = low ? yh + 64.f : yh;         // exact: the magnitude shrinks
-    scl = low ? Q.scl_lo : scl;
-  }
-  const float r = CAREFUL ? fmaf(de, Q.c_hi, Pe) : Pe;
-  const float k = fmaf(fmaf(d, Q.c_lo, r), kLn2, Q.nglo);
-  const float e = exp2_fast(yh);
-  return fmaf(e, k, e) * scl;
-}
-
 template <typename TI, typename TO, bool VECTOR, int B, int KIND, int kU, int WAVES>
 __global__ __launch_bounds__(B) __attribute__((amdgpu_waves_per_eu(WAVES)))
 void k_row(RowParams P) {
@@ -691,39 +636,13 @@ void k_row(RowParams P) {
     // log2 normaliser F of p_v = 2^(z c - F); value_v = sign(alpha) 2^((z - m) c - G)
     // with G = F - m c - log2 |alpha|.
     const double F = (KIND == KIND_CENTER) ? lse * kLog2ed : (double)E_row + l2s;
-    Pass2 Q;
-    Q.m = m;
-    Q.c_hi = c_hi;
-    Q.c_lo = c_lo;
-    Q.gq = 0.f;
-    Q.nglo = 0.f;
-    Q.scl = qnan;
-    Q.scl_lo = qnan;
-    bool careful = !kBf16In || sh_ninf != 0;
-    {
-      const double G = fmax(F - (double)m * c64 - log2(fabs(alpha)), -1.0e4);
-      const float sgn = alpha < 0.0 ? -1.f : 1.f;
-      if (G == G && rflags == 0) {
-        if (G > 1.0e4) {                       // every value underflows (alpha = 0 too)
-          Q.scl = 0.f * sgn;
-          Q.scl_lo = Q.scl;
-        } else {
-          double gi = ceil(G);
-          double gq = ceil((G - gi) * 16384.0) / 16384.0;   // (-1, 0]
-          const double glo = (G - gi) - gq;                 // (-2^-14, 0]
-          if (gi < -126.0) { gq += gi + 126.0; gi = -126.0; }   // |alpha| beyond 2^126
-          const int g = (int)gi;
-          Q.gq = (float)gq;
-          Q.nglo = (float)(-glo * kLn2d);
-          Q.scl = g > 160 ? 0.f * sgn : ldexpf(sgn, -g);
-          Q.scl_lo = g + 64 > 160 ? 0.f * sgn : ldexpf(sgn, -g - 64);
-          // Results below 2^-126 need the careful value: only when the row's
-          // scale leaves room for them (with bf16 output, values below
-          // 2^-134 round to zero anyway).
-          if (g < (std::is_same<TO, uint16_t>::value ? 8 : 24)) careful = true;
-        }
-      }
-    }
+    const double G = rflags ? (double)qnan : F - (double)m * c64 - log2(fabs(alpha));
+    int g = 0;
+    const Pass2 Q = pass2_setup(m, c_hi, c_lo, G, alpha < 0.0, g);
+    // Results below 2^-126 need the careful value: only when the row's scale
+    // leaves room for them (with bf16 output, values below 2^-134 round to
+    // zero anyway).
+    const bool careful = !kBf16In || sh_ninf != 0 || g < (std::is_same<TO, uint16_t>::value ? 8 : 24);
     TO* orow = reinterpret_cast<TO*>(P.row_out) + row * P.out_stride;
 
     // Stream the row; marked vectors are not stored here but from the list

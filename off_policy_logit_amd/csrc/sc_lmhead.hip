@@ -59,19 +59,28 @@ static_assert(kTV == 256 && kTP == 256 && kKB == 64, "tile shape is fixed");
 static_assert(kLds <= 160 * 1024, "LDS budget");
 
 constexpr int kNoIdx = 0x7fffffff;
+constexpr double kLn2d = 0.6931471805599453;
 
 SC_DEV int lm_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 
+SC_DEV float scale2(float x, int k) { return ldexpf(x, k); }
+SC_DEV double scale2(double x, int k) { return ldexp(x, k); }
+
 // Merge running state (m, s, hy, am) with (m2, s2, h2, am2).  s is a sum of
-// 2^((z - m) c), hy the sum of 2^((z - m) c) (z - m) c over the same ids.
-SC_DEV void lm_merge(float& m, float& s, float& hy, int& am, float m2, float s2,
-                     float h2, int am2, float c) {
+// 2^(z c - E(m)) over ids whose logits are at most m, with the integer
+// reference E(m) = ref_exp(m), and hy the sum of those terms times their
+// exponents z c - E(m); moving a state to a larger reference multiplies s by
+// a power of two (and subtracts the shift times s from hy first): exact.
+template <typename F>
+SC_DEV void lm_merge(float& m, F& s, F& hy, int& am, float m2, F s2, F h2, int am2,
+                     float c_hi) {
   const float M = fmaxf(m, m2);
-  const float r1 = exp2_fast((m - M) * c), r2 = exp2_fast((m2 - M) * c);
-  const float t1 = s > 0.f ? r1 * (hy - (M - m) * c * s) : 0.f;
-  const float t2 = s2 > 0.f ? r2 * (h2 - (M - m2) * c * s2) : 0.f;
+  const float EM = ref_exp(M, c_hi);
+  const float D1 = EM - ref_exp(m, c_hi), D2 = EM - ref_exp(m2, c_hi);
+  const int k1 = (int)fminf(D1, 2048.f), k2 = (int)fminf(D2, 2048.f);
+  const F t1 = scale2(hy - (F)D1 * s, -k1), t2 = scale2(h2 - (F)D2 * s2, -k2);
   am = (m2 > m || (m2 == m && am2 < am)) ? am2 : am;
-  s = r1 * s + r2 * s2;
+  s = scale2(s, -k1) + scale2(s2, -k2);
   hy = t1 + t2;
   m = M;
 }
@@ -143,17 +152,15 @@ __global__ __launch_bounds__(256) void k_lm_stage(LmParams P) {
 // mean): scale = -A wt / (T N_valid) and the off-head factor alpha =
 // -scale (rho + 1 - S) (centering) or -scale; zero for padding rows, NaN for
 // rows whose statistics are NaN or whose response index is out of range.
-SC_DEV void lm_row_factors(const LmParams& P, int64_t p, float& scale, float& alpha) {
+SC_DEV void lm_row_factors(const LmParams& P, int64_t p, double& scale, double& alpha) {
   const int resp = P.resp_idx ? P.resp_idx[p] : 0;
-  if (resp < 0) { scale = 0.f; alpha = 0.f; return; }
-  if (resp >= P.n_responses) { scale = alpha = __builtin_nanf(""); return; }
+  if (resp < 0) { scale = 0.0; alpha = 0.0; return; }
+  if (resp >= P.n_responses) { scale = alpha = (double)__builtin_nanf(""); return; }
   const float* st = P.stats_in + p * SC_NSTATS;
-  const double sc = -(double)P.advantages[resp] * (double)st[SC_STAT_WEIGHT] /
-                    ((double)P.temperature * (double)P.n_valid[0]);
-  const double al = P.centering ? -sc * ((double)st[SC_STAT_RHO] + 1.0 - (double)st[SC_STAT_S])
-                                : -sc;
-  scale = (float)sc;
-  alpha = (float)al;
+  scale = -(double)P.advantages[resp] * (double)st[SC_STAT_WEIGHT] /
+          ((double)P.temperature * (double)P.n_valid[0]);
+  alpha = P.centering ? -scale * ((double)st[SC_STAT_RHO] + 1.0 - (double)st[SC_STAT_S])
+                      : -scale;
 }
 
 template <int MODE>
@@ -197,7 +204,7 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
   if (n_ck <= 0) return;  // the host keeps splits <= chunks
   const int ST = P.d / kKB;
   const int total = n_ck * ST;
-  const float c = P.c;
+  const float c_hi = P.c_hi, c_lo = P.c_lo;
   const int V = (int)P.vocab;
 
   // Loader: thread t moves 16 bytes of rows (t >> 3) + 64 j, j < 4, of each
@@ -296,20 +303,26 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
   int cur = 0, cnt = 0, nid = kNoIdx;
   float sm[NJ], ss[NJ], sh[NJ];
   int sam[NJ], sa_l[NJ];
-  // dLogits mode: value = sign(alpha) 2^(z c + off) 2^-32 with
-  // off = log2|alpha| - lse log2(e) + 32 (subnormal results stay exact)
-  float dz_off[NJ];
-  bool dz_neg[NJ];
+  // dLogits mode: value alpha p_v = sign(alpha) 2^((z - R) c - G) by the
+  // exact exponent of the row kernels' pass 2 (p2_value), with the reference
+  // R = lse T rounded to fp32 (R >= every logit of the row, so that the
+  // exponent is small where the values are large), G = lse log2(e) - R c -
+  // log2|alpha|, and lse = the fp32 statistic plus its remainder column.
+  Pass2 dzq[NJ];
   if (MODE == 2) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int64_t p = p0 + wp * kWR + j * 32 + lc;
-      float sc = 0.f, al = 0.f;
-      if (p < P.n_rows) lm_row_factors(P, p, sc, al);
-      const float lse = p < P.n_rows ? P.stats_in[p * SC_NSTATS + SC_STAT_LSE] : 0.f;
-      dz_off[j] = log2f(fabsf(al)) - lse * kLog2e + 32.f;
-      dz_off[j] = (al != al) ? al : dz_off[j];
-      dz_neg[j] = al < 0.f;
+      double sc = 0.0, al = 0.0, lse = 0.0;
+      if (p < P.n_rows) {
+        lm_row_factors(P, p, sc, al);
+        const float* st = P.stats_in + p * SC_NSTATS;
+        lse = (double)st[SC_STAT_LSE] + (double)st[SC_STAT_LSE_LO];
+      }
+      const float R = (float)(lse * (double)P.temperature);
+      const double G = lse * 1.4426950408889634 - (double)R * P.c64 - log2(fabs(al));
+      int g = 0;
+      dzq[j] = pass2_setup(R, P.c_hi, P.c_lo, G, al < 0.0, g);
     }
   }
   if (!STORE) {
@@ -363,8 +376,7 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
             for (int i = 0; i < 16; ++i) {
               const int v = v0 + wv * 128 + bi * 32 + lm_row(i, h);
               if (v >= V) continue;
-              float y = exp2_fast(fmaf(acc[bi][j][i], c, dz_off[j])) * 0x1p-32f;
-              y = dz_neg[j] ? -y : y;
+              const float y = p2_value<true>(acc[bi][j][i], dzq[j]);
               P.dzt[(int64_t)v * P.dzts + p] = live ? (uint16_t)f32_to_bf16(y) : (uint16_t)0;
             }
         }
@@ -382,10 +394,7 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
             const int v = v0 + wv * 128 + bi * 32 + 8 * g4 + 4 * h;
             float x[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float y = exp2_fast(fmaf(acc[bi][j][4 * g4 + e], c, dz_off[j])) * 0x1p-32f;
-              x[e] = dz_neg[j] ? -y : y;
-            }
+            for (int e = 0; e < 4; ++e) x[e] = p2_value<true>(acc[bi][j][4 * g4 + e], dzq[j]);
             if (v + 3 < V) {
               u32x2 wv2;
               wv2[0] = pack_bf16x2(x[0], x[1]);
@@ -476,13 +485,15 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
           for (int i = 15; i >= 0; --i) e = acc[bi][j][i] == bmx ? bi * 16 + i : e;
         sam[j] = v0 + wv * 128 + (e >> 4) * 32 + lm_row(e & 15, h);
       }
+      // the row's integer reference E = ref_exp(max): rebase by 2^-(E' - E)
       const float mn = fmaxf(sm[j], bmx);
-      const float r = exp2_fast((sm[j] - mn) * c);
-      sh[j] = ss[j] > 0.f ? r * (sh[j] - (mn - sm[j]) * c * ss[j]) : 0.f;
-      ss[j] *= r;
+      const float E = ref_exp(mn, c_hi);
+      const float D = E - ref_exp(sm[j], c_hi);
+      const int kd = (int)fminf(D, 2048.f);
+      sh[j] = ldexpf(fmaf(-D, ss[j], sh[j]), -kd);
+      ss[j] = ldexpf(ss[j], -kd);
       sm[j] = mn;
-      const float mc = mn * c;
-      float s_acc = 0.f, h_acc = 0.f;
+      float sb[4], h_acc = 0.f;
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) {
         const int vb = v0 + wv * 128 + bi * 32;    // first id of the block
@@ -493,14 +504,21 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
           word |= nv <= 0 ? 0xffffffffu : (nv >= 32 ? 0u : ~((1u << nv) - 1u));
         }
         const uint32_t wh = word >> (4 * h);
+        // 2^(z c - E), z c = z c_hi + z c_lo; summed pairwise
+        float e16[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float y = fmaf(acc[bi][j][i], c, -mc);
+          const float y = fmaf(acc[bi][j][i], c_lo, fmaf(acc[bi][j][i], c_hi, -E));
           const float e = exp2_fast(y);
           const bool ex = (wh >> (8 * (i >> 2) + (i & 3))) & 1u;
-          s_acc += ex ? 0.f : e;
+          e16[i] = ex ? 0.f : e;
           h_acc += ex ? 0.f : e * y;
         }
+#pragma unroll
+        for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+          for (int i = 0; i + w < 16; i += 2 * w) e16[i] += e16[i + w];
+        sb[bi] = e16[0];
         // Captures: logits at recorded ids (rare) and at the sampled id.
         uint32_t bits = hw & (0x0f0f0f0fu << (4 * h));   // this lane's rows
         while (bits) {
@@ -529,7 +547,7 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
           P.za[p0 + ploc] = za;
         }
       }
-      ss[j] += s_acc;
+      ss[j] += (sb[0] + sb[1]) + (sb[2] + sb[3]);
       sh[j] += h_acc;
     }
   };
@@ -568,7 +586,7 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
     const float m2 = __shfl_xor(sm[j], 32), s2 = __shfl_xor(ss[j], 32);
     const float h2 = __shfl_xor(sh[j], 32);
     const int a2 = __shfl_xor(sam[j], 32);
-    lm_merge(sm[j], ss[j], sh[j], sam[j], m2, s2, h2, a2, c);
+    lm_merge(sm[j], ss[j], sh[j], sam[j], m2, s2, h2, a2, c_hi);
   }
   float4* xch = reinterpret_cast<float4*>(lds);  // operand buffers are free now
   if (wv == 1 && h == 0) {
@@ -582,7 +600,7 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
     for (int j = 0; j < NJ; ++j) {
       const int ploc = wp * kWR + j * 32 + lc;
       const float4 o = xch[ploc];
-      lm_merge(sm[j], ss[j], sh[j], sam[j], o.x, o.y, o.z, __float_as_int(o.w), c);
+      lm_merge(sm[j], ss[j], sh[j], sam[j], o.x, o.y, o.z, __float_as_int(o.w), c_hi);
       const int64_t p = p0 + ploc;
       if (p < P.n_rows)
         P.state[(int64_t)split * P.n_rows + p] =
@@ -601,7 +619,8 @@ __global__ __launch_bounds__(256) void k_lm_finalize(LmParams P) {
   if (t == 0) sh_status = 0u;
   __syncthreads();
   const int K = P.k;
-  const float c = P.c;
+  const float c_hi = P.c_hi;
+  const double c64 = P.c64;
   const float qnan = __builtin_nanf("");
   if (p < P.n_rows) {
     float* stats = P.row_stats + p * SC_NSTATS;
@@ -617,61 +636,67 @@ __global__ __launch_bounds__(256) void k_lm_finalize(LmParams P) {
         for (int k = l; k < K; k += kWave) P.head_logp[p * K + k] = 0.f;
     } else {
       uint32_t fl = P.sflags[p];
-      // merge the split states in a fixed butterfly order
-      // (lane l takes splits l, l + 64, ... in order, then the butterfly)
-      float m = -FLT_MAX, s = 0.f, hy = 0.f;
+      // merge the split states in a fixed butterfly order (lane l takes
+      // splits l, l + 64, ... in order, then the butterfly), in float64
+      float m = -FLT_MAX;
+      double s = 0.0, hy = 0.0;
       int am = kNoIdx;
       for (int q = l; q < P.splits; q += kWave) {
         const float4 st = P.state[(int64_t)q * P.n_rows + p];
-        lm_merge(m, s, hy, am, st.x, st.y, st.z, __float_as_int(st.w), c);
+        lm_merge<double>(m, s, hy, am, st.x, (double)st.y, (double)st.z,
+                         __float_as_int(st.w), c_hi);
       }
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
-        const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o), h2 = __shfl_xor(hy, o);
+        const float m2 = __shfl_xor(m, o);
+        const double s2 = __shfl_xor(s, o), h2 = __shfl_xor(hy, o);
         const int a2 = __shfl_xor(am, o);
-        lm_merge(m, s, hy, am, m2, s2, h2, a2, c);
+        lm_merge<double>(m, s, hy, am, m2, s2, h2, a2, c_hi);
       }
-      // recorded ids: their logits were captured by the main kernel
-      float sH = 0.f, hH = 0.f;
+      // s and hy are relative to the integer reference E; the recorded ids'
+      // terms 2^(z c - E) (their logits were captured by the main kernel)
+      // join them in float64
+      const double E = (double)ref_exp(m, c_hi);
+      double sH = 0.0, hH = 0.0;
       bool ninf = false;
       int aslot = kNoIdx;
       const int32_t a = P.sampled[p];
       for (int k = l; k < K; k += kWave) {
         const float z = fl ? 0.f : P.head_raw[p * K + k];
-        const float y = (z - m) * c;
-        const float e = exp2_fast(y);
+        const double y = (double)z * c64 - E;
+        const double e = exp2(y);
         ninf |= !(z > -INFINITY);
         sH += e;
-        hH += e > 0.f ? e * y : 0.f;
+        hH += e > 0.0 ? e * y : 0.0;
         if (P.head_ids[p * K + k] == a) aslot = min(aslot, k);
       }
       sH = wave_sum(sH);
       hH = wave_sum(hH);
 #pragma unroll
       for (int o = kWave / 2; o > 0; o >>= 1) aslot = min(aslot, __shfl_xor(aslot, o));
-      const float stot = s + sH;
-      const float log2s = log2f(stot);
+      const double stot = s + sH;
+      const double log2s = log2(stot);
       const float za = fl ? 0.f : P.za[p];
       if (!(stot < INFINITY) || !(m > -FLT_MAX) || !(m < INFINITY) || !(za > -INFINITY) ||
           !(hy + hH == hy + hH) || wave_or(ninf ? 1u : 0u))
         fl |= SC_DEV_NONFINITE;
       const bool bad = fl != 0;
-      float ph = 0.f;
+      double ph = 0.0;
       for (int k = l; k < K; k += kWave) {
         const float z = bad ? 0.f : P.head_raw[p * K + k];
-        const float l2 = (z - m) * c - log2s;
-        ph += exp2_fast(l2 + 32.f) * 0x1p-32f;
-        if (P.head_logp) P.head_logp[p * K + k] = bad ? qnan : l2 * kLn2;
+        const double l2 = (double)z * c64 - E - log2s;
+        ph += exp2(l2);
+        if (P.head_logp) P.head_logp[p * K + k] = bad ? qnan : (float)(l2 * kLn2d);
       }
       ph = wave_sum(ph);
       if (l == 0) {
-        const double lse64 = ((double)m * (double)c + (double)log2s) * 0.6931471805599453;
+        const double lse64 = (E + log2s) * kLn2d;
         stats[SC_STAT_LSE] = bad ? qnan : (float)lse64;
         stats[SC_STAT_LSE_LO] = bad ? qnan : (float)(lse64 - (double)(float)lse64);
-        stats[SC_STAT_LOGP_A] = bad ? qnan : ((za - m) * c - log2s) * kLn2;
-        stats[SC_STAT_TAIL] = bad ? qnan : s / stot;
-        stats[SC_STAT_P_H] = bad ? qnan : ph;
-        stats[SC_STAT_ENTROPY] = bad ? qnan : (log2s - (hy + hH) / stot) * kLn2;
+        stats[SC_STAT_LOGP_A] = bad ? qnan : (float)(((double)za * c64 - E - log2s) * kLn2d);
+        stats[SC_STAT_TAIL] = bad ? qnan : (float)(s / stot);
+        stats[SC_STAT_P_H] = bad ? qnan : (float)ph;
+        stats[SC_STAT_ENTROPY] = bad ? qnan : (float)((log2s - (hy + hH) / stot) * kLn2d);
         ridx[0] = bad ? -1 : am;
         ridx[1] = bad ? -1 : (aslot == kNoIdx ? -1 : aslot);
         if (fl) atomicOr(&sh_status, fl);
@@ -694,9 +719,8 @@ __global__ __launch_bounds__(256) void k_lm_dz_fix(LmParams P) {
   if (p >= P.n_rows) return;
   const int resp = P.resp_idx ? P.resp_idx[p] : 0;
   if (resp < 0) return;
-  float scf = 0.f, alf = 0.f;
-  lm_row_factors(P, p, scf, alf);
-  const double scale = scf, alpha = alf;
+  double scale = 0.0, alpha = 0.0;
+  lm_row_factors(P, p, scale, alpha);
   const float* st = P.stats_in + p * SC_NSTATS;
   const double oms = 1.0 - (double)st[SC_STAT_S];
   const int K = P.k;

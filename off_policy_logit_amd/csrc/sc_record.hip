@@ -507,8 +507,11 @@ void k_record(RecParams P) {
       P.head_probs[row * K + k] = q;
     }
     if (t == 0) {
-      if (P.sampled_logp)
-        P.sampled_logp[row] = (flags || a < 0) ? qnan : ((za - m) * c - log2s) * kLn2;
+      // log p(a) in float64: the logit difference is exact there, and the
+      // fp32 log-sum-exp of the row enters only through log2 of its sum
+      const double lpa = (((double)za - (double)m) * P.c64 - log2((double)part[0])) *
+                         0.6931471805599453;
+      if (P.sampled_logp) P.sampled_logp[row] = (flags || a < 0) ? qnan : (float)lpa;
       if (flags) sh_u[3] |= flags;
     }
   }

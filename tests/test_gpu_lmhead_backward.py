@@ -4,8 +4,8 @@ kernel (sc_lmhead_dlogits) and the gradients dHidden = dZ W, dW = dZ^T X
 float64 oracle on the kernel's own logits.
 
 Tolerances: dLogits rows as the other bf16 rows (one bf16 step of the RNE of
-the float64 value, >= 99.5% bit-equal; the kernel takes lse from the fp32
-statistics).  Gradients: |err| <= 2^-8 sum_k |G||M| elementwise (bf16
+the float64 value, >= 99.99% bit-equal over a test's entries; the kernel takes
+lse from the fp32 statistic plus its remainder column).  Gradients: |err| <= 2^-8 sum_k |G||M| elementwise (bf16
 rounding of dZ, 2^-9 relative, plus fp32 accumulation over <= 2^14 terms,
 2^-10 relative), plus 2^-9 |value| when d_hidden is bf16.
 """
@@ -15,7 +15,7 @@ import torch
 
 from oracle import sc_oracle as O
 import synthetic
-from tests.parity import compare_bf16
+from tests.parity import MIN_BF16_EQUAL, compare_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -81,7 +81,7 @@ def test_lmhead_dlogits_rows_match_oracle(is_mode, centering, T):
     bits = dz.view(torch.int16).cpu().numpy()
     dist, eq = compare_bf16(bits, G)
     say(f"dlogits bf16: max step distance {dist}, bit-equal {eq:.6f}")
-    assert dist <= 1 and eq >= 0.995, (dist, eq)
+    assert dist <= 1 and eq >= MIN_BF16_EQUAL, (dist, eq)
     pad = host(resp) < 0
     assert np.all(bits[pad] == 0)
 
