@@ -38,11 +38,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix peak
 LM_ROWS, LM_D = 16_384, 4096    # fused LM-head slice (64 x 8,800-token batch, d = 4,096)
 PROFILE = os.path.join(ROOT, "profiles", "sc_correct_quick_check_pmc.md")
-# Sources of the fused row kernel whose counters profiles/ holds (its launch
-# shape is set in sc_kernels.hip's template arguments and sc_internal.h's
-# macros; the latter file also carries unrelated structs, so it is left out).
+# Everything that shapes the fused row kernel whose counters profiles/ holds:
+# its sources, the header with its launch-shape macros, and the build flags.
 KERNEL_SOURCES = [os.path.join(ROOT, "off_policy_logit_amd", "csrc", f)
-                  for f in ("sc_kernels.hip", "sc_device.h")]
+                  for f in ("sc_kernels.hip", "sc_device.h", "sc_internal.h")]
 
 # Algorithmic bytes of one position through the fused kernel (sc_correct with
 # a bf16 dLogits row): logits 2V, head ids 4K, head probs 4K, sampled,
@@ -58,10 +57,12 @@ BYTES_PER_POSITION_RECORD = 2 * VOCAB + 4 + 8 * K + 4
 
 
 def source_digest():
+    from off_policy_logit_amd import build as B
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
         with open(p, "rb") as f:
             h.update(f.read())
+    h.update(" ".join(B.FLAGS).encode())
     return h.hexdigest()[:16]
 
 
@@ -93,11 +94,23 @@ def _oracle_rows(idx):
     return len(idx)
 
 
-def cpu_baseline(rows, min_seconds=10.0, max_passes=200):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(rows, min_seconds=10.0, max_passes=200, single_seconds=4.0):
     """Time the oracle on `rows` positions generated on the host with the
-    quick-check generator, in passes over the sample until `min_seconds` of
-    wall time have elapsed.  Runs before anything touches the GPU, in a fork
-    pool of one process per available core (capped at 16)."""
+    quick-check generator: first on one thread in this process for about
+    `single_seconds`, then in passes over the sample until `min_seconds` of
+    wall time have elapsed in a fork pool of one process per available core
+    (capped at 16).  Runs before anything touches the GPU."""
     global _SAMPLE
     import synthetic
     spec = synthetic.BigSpec(seed=1)
@@ -109,6 +122,10 @@ def cpu_baseline(rows, min_seconds=10.0, max_passes=200):
     a = np.concatenate([p["sampled"].numpy() for p in parts])
     rlp = np.concatenate([p["rollout_logp"].numpy() for p in parts])
     _SAMPLE = (z, ids, q, a, rlp)
+    one, t1 = 0, time.perf_counter()
+    while time.perf_counter() - t1 < single_seconds and one < rows:
+        one += _oracle_rows([one])
+    single = one / (time.perf_counter() - t1)
     cores = min(16, len(os.sched_getaffinity(0)))
     chunks = [list(range(i, rows, cores)) for i in range(cores)]
     ctx = mp.get_context("fork")
@@ -123,61 +140,135 @@ def cpu_baseline(rows, min_seconds=10.0, max_passes=200):
     dt = time.perf_counter() - t0
     _SAMPLE = None
     return dict(value=round(done / dt, 1), unit="positions/s", cores=cores, kind="oracle",
+                cpu_model=cpu_model(), single_thread_value=round(single, 1),
                 sample=f"{rows} positions of the quick-check workload (V={VOCAB}, K={K}, "
                        f"bf16 logits) x {passes} passes = {done} positions, full "
                        f"per-position outputs incl. the dLogits row, float64, "
-                       f"{dt:.1f} s wall on {cores} processes")
+                       f"{dt:.1f} s wall on {cores} processes; single thread: {one} "
+                       f"positions in this process")
 
 
 # ---------------------------------------------------------------------------
 # GPU
 # ---------------------------------------------------------------------------
-def full_step_measure(dev, reps):
-    """One 16,384-position chunk of the full-step workload (4 responses x
-    4,096 tokens, lengths uniform in [256, 4,096], the rest padding): exact
-    count, the fused kernel with bf16 dLogits, step sums, timed together."""
+def _events():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def full_step_measure(dev, reps, chunks=32, chunk_rows=16_384):
+    """The full-step workload: 32 prompts x 4 responses x 4,096 tokens =
+    524,288 positions, response lengths uniform in [256, 4,096] and the rest
+    padding, in 32 chunks of 16,384 positions.  The exact valid count runs
+    once over the step's response indices; then each chunk is generated into
+    HBM (untimed) and its fused kernel (bf16 dLogits) and step sums are timed
+    `reps` times.  The step time is the count plus the sum of the chunk
+    times."""
     import torch
     import synthetic
     from off_policy_logit_amd import sc
     lengths = synthetic.full_step_lengths()
-    c = synthetic.full_step_chunk(dev, 0, lengths)
-    rows = c["logits"].shape[0]
+    rows_all = torch.arange(chunks * chunk_rows)
+    lens = torch.as_tensor(np.asarray(lengths))[rows_all // 4096]
+    resp_all = torch.where(rows_all % 4096 < lens, rows_all // 4096, -1).to(torch.int32).to(dev)
     n_valid = torch.empty(1, dtype=torch.int64, device=dev)
-    sc.count_valid(c["resp_idx"], out=n_valid)
-    valid = int(n_valid.item())
-    g = torch.Generator().manual_seed(12)
-    adv = torch.randn(int(c["resp_idx"].max().item()) + 1, generator=g).to(dev)
-    dz = torch.empty_like(c["logits"])
-    batch = torch.empty(sc.NBATCH, dtype=torch.float64, device=dev)
-    status = torch.zeros(1, dtype=torch.int32, device=dev)
-    out = sc.correct(c["logits"], c["head_ids"], c["head_probs"], c["sampled"], c["resp_idx"],
-                     adv, n_valid=n_valid, rollout_logp=c["rollout_logp"], row_out=dz,
-                     dev_status=status)
-
-    def run():
-        sc.count_valid(c["resp_idx"], out=n_valid)
-        sc.correct(c["logits"], c["head_ids"], c["head_probs"], c["sampled"], c["resp_idx"],
-                   adv, n_valid=n_valid, rollout_logp=c["rollout_logp"], row_out=dz,
-                   out=out, coef=out["coef"], dev_status=status)
-        sc.batch_sums(out["row_stats"], c["resp_idx"], n_valid, out=batch)
-    run()
+    sc.count_valid(resp_all, out=n_valid)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = _events()
     e0.record()
     for _ in range(reps):
-        run()
+        sc.count_valid(resp_all, out=n_valid)
     e1.record()
     torch.cuda.synchronize()
+    count_ms = e0.elapsed_time(e1) / reps
+    valid = int(n_valid.item())
+    g = torch.Generator().manual_seed(12)
+    adv = torch.randn(int(resp_all.max().item()) + 1, generator=g).to(dev)
+    batch = torch.empty(sc.NBATCH, dtype=torch.float64, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    dz = torch.empty(chunk_rows, VOCAB, dtype=torch.bfloat16, device=dev)
+    out = None
+    chunk_ms, byte_total = [], 0
+    for ck in range(chunks):
+        c = synthetic.full_step_chunk(dev, ck, lengths, chunk_rows=chunk_rows)
+        resp = resp_all[ck * chunk_rows:(ck + 1) * chunk_rows]
+        assert torch.equal(resp, c["resp_idx"])
+        kw = dict(n_valid=n_valid, rollout_logp=c["rollout_logp"], row_out=dz,
+                  dev_status=status)
+        if out is None:
+            out = sc.correct(c["logits"], c["head_ids"], c["head_probs"], c["sampled"], resp,
+                             adv, **kw)
+        sc.correct(c["logits"], c["head_ids"], c["head_probs"], c["sampled"], resp, adv,
+                   out=out, coef=out["coef"], **kw)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            sc.correct(c["logits"], c["head_ids"], c["head_probs"], c["sampled"], resp, adv,
+                       out=out, coef=out["coef"], **kw)
+            sc.batch_sums(out["row_stats"], resp, n_valid, out=batch, accumulate=ck > 0)
+        e1.record()
+        torch.cuda.synchronize()
+        chunk_ms.append(e0.elapsed_time(e1) / reps)
+        nv = int((resp >= 0).sum().item())
+        # valid rows move the fused kernel's bytes; padding rows only write a zero row
+        byte_total += nv * BYTES_PER_POSITION + (chunk_rows - nv) * (2 * VOCAB + 8 * K + 72)
+        del c
     if int(status.item()) != 0:
         raise RuntimeError(f"full-step device status {int(status.item())}")
-    ms = e0.elapsed_time(e1) / reps
-    # valid rows move the fused kernel's bytes; padding rows only write a zero row
-    bytes_ = valid * BYTES_PER_POSITION + (rows - valid) * (2 * VOCAB + 8 * K + 72)
-    del c, dz, out
+    del dz, out
     torch.cuda.empty_cache()
-    return {"workload": f"full-step chunk 0: {rows} positions, {valid} valid, V={VOCAB}, K={K}",
-            "ms": round(ms, 4), "valid_positions_per_s": round(valid / (ms * 1e-3), 1),
-            "GBps": round(bytes_ / (ms * 1e-3) / 1e9, 1)}
+    total_ms = count_ms + sum(chunk_ms)
+    return {"workload": f"full step: {chunks} chunks x {chunk_rows} = {chunks * chunk_rows} "
+                        f"positions, {valid} valid, V={VOCAB}, K={K}, bf16 logits and dLogits",
+            "step_ms": round(total_ms, 3), "count_ms": round(count_ms, 4),
+            "chunk_ms_min": round(min(chunk_ms), 4), "chunk_ms_max": round(max(chunk_ms), 4),
+            "valid_positions_per_s": round(valid / (total_ms * 1e-3), 1),
+            "GBps": round(byte_total / (sum(chunk_ms) * 1e-3) / 1e9, 1)}
+
+
+def stress_measure(dev, reps, chunks=8, chunk_rows=16_384):
+    """Distribution stress: 131,072 positions (8 chunks of 16,384: thirds
+    peaked x8, flat x0.1 and mixed; 5% of sampled tokens outside the head)
+    per rollout-noise sigma in {0.01, 0.1, 0.5}; each chunk generated into
+    HBM (untimed), then the fused kernel with bf16 dLogits timed `reps`
+    times."""
+    import torch
+    import synthetic
+    from off_policy_logit_amd import sc
+    res = {}
+    adv = torch.tensor([0.5], device=dev)
+    n_valid = torch.tensor([chunks * chunk_rows], dtype=torch.int64, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    dz = torch.empty(chunk_rows, VOCAB, dtype=torch.bfloat16, device=dev)
+    e0, e1 = _events()
+    for sigma in (0.01, 0.1, 0.5):
+        ms, out = [], None
+        for ck in range(chunks):
+            c = synthetic.stress_chunk(dev, ck, sigma, chunk_rows=chunk_rows)
+            kw = dict(n_valid=n_valid, rollout_logp=c["rollout_logp"], row_out=dz,
+                      dev_status=status)
+            args = (c["logits"], c["head_ids"], c["head_probs"], c["sampled"], c["resp_idx"],
+                    adv)
+            out = sc.correct(*args, out=out, coef=None if out is None else out["coef"], **kw)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                sc.correct(*args, out=out, coef=out["coef"], **kw)
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1) / reps)
+            del c
+        if int(status.item()) != 0:
+            raise RuntimeError(f"stress device status {int(status.item())}")
+        tot = sum(ms)
+        res[f"sigma={sigma}"] = {"kernel_ms_total": round(tot, 3),
+                                 "positions_per_s": round(chunks * chunk_rows / (tot * 1e-3), 1),
+                                 "GBps": round(chunks * chunk_rows * BYTES_PER_POSITION /
+                                               (tot * 1e-3) / 1e9, 1)}
+    del dz
+    torch.cuda.empty_cache()
+    return {"workload": f"distribution stress: {chunks * chunk_rows} positions per sigma, "
+                        f"V={VOCAB}, K={K}, bf16 logits and dLogits", **res}
 
 
 def lmhead_measure(dev, reps):
@@ -263,6 +354,10 @@ def main():
                     help="positions in the CPU-oracle sample (0 skips it)")
     ap.add_argument("--no-lmhead", action="store_true",
                     help="skip the fused LM-head measurement")
+    ap.add_argument("--no-full-step", action="store_true",
+                    help="skip the full-step workload (32 chunks)")
+    ap.add_argument("--no-stress", action="store_true",
+                    help="skip the distribution-stress workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy before the timed region "
                          "(reference kernel for PMC byte counters)")
@@ -355,6 +450,17 @@ def main():
     torch.cuda.synchronize()
     copy_ms = e0.elapsed_time(e1) / reps
     copy_bytes = 2 * d["logits"].numel() * d["logits"].element_size()
+    # the library's reference copy kernel on the same bytes (nontemporal
+    # 16-byte stream, one workgroup per 512 KiB): the measured copy ceiling
+    sc.reference_copy(d["logits"], dlogits)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        sc.reference_copy(d["logits"], dlogits)
+    e1.record()
+    torch.cuda.synchronize()
+    ref_copy_ms = e0.elapsed_time(e1) / reps
+    ref_copy_gbps = copy_bytes / (ref_copy_ms * 1e-3) / 1e9
 
     # two-call path: sc_logprobs, then sc_center streaming the logits again
     # for the dLogits row (the same outputs as the fused kernel)
@@ -391,7 +497,10 @@ def main():
     if int(status.item()) != 0:
         raise RuntimeError(f"record device status {int(status.item())}")
 
-    full = full_step_measure(dev, max(5, args.steps // 5))
+    del d, dlogits, out, coef, st, rec
+    torch.cuda.empty_cache()
+    full = None if args.no_full_step else full_step_measure(dev, 3)
+    stress = None if args.no_stress else stress_measure(dev, 3)
     lm = None if args.no_lmhead else lmhead_measure(dev, max(3, args.steps // 10))
 
     bytes_launch = n * BYTES_PER_POSITION
@@ -420,6 +529,8 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
+                     "copy_reference_GBps": round(ref_copy_gbps, 1),
+                     "frac_of_copy": round(achieved / ref_copy_gbps, 4),
                      "kernel": "sc_correct (k_row bf16->bf16, fused)",
                      "kernel_ms": round(kern_ms, 4),
                      "bytes_per_launch": bytes_launch},
@@ -430,12 +541,16 @@ def main():
             "stats_only_GBps": round(n * BYTES_PER_POSITION_STATS / (stats_ms * 1e-3) / 1e9, 1),
             "copy_same_bytes_ms": round(copy_ms, 4),
             "copy_GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1),
+            "reference_copy_ms": round(ref_copy_ms, 4),
+            "stats_only_frac_of_copy": round(n * BYTES_PER_POSITION_STATS / (stats_ms * 1e-3) /
+                                             1e9 / ref_copy_gbps, 4),
             "two_call_positions_per_s": round(n / (two_ms * 1e-3), 1),
             "two_call_ms": round(two_ms, 4),
             "record_positions_per_s": round(n / (rec_ms * 1e-3), 1),
             "record_kernel_ms": round(rec_ms, 4),
             "record_GBps": round(n * BYTES_PER_POSITION_RECORD / (rec_ms * 1e-3) / 1e9, 1),
-            "full_step_chunk": full,
+            "full_step": full,
+            "stress": stress,
             "lmhead": lm,
         },
     }

@@ -124,9 +124,10 @@ enum sc_batch {
 /*
  * sc_logprobs -- trainer log-probabilities at the recorded and sampled ids.
  *
- * Score Centering section: "scores the current policy over the full model
- * vocabulary at the rollout temperature, then gathers candidate and sampled
- * logprobs".  One HBM pass over each valid row of logits.
+ * Score Centering page, section "Score Centering": the trainer evaluates its
+ * policy on the whole vocabulary at the temperature the rollout used and
+ * reads off the log-probabilities of the recorded candidates and of the
+ * sampled token.  One HBM pass over each valid row of logits.
  *
  *   logits        device, [n_rows, row_stride] of logits_dtype (SC_F32/SC_BF16)
  *   head_ids      device int32 [n_rows, k]: recorded ids H, distinct, in [0,V)
@@ -255,6 +256,18 @@ int sc_count_valid(const int32_t* resp_idx, int64_t n_rows, int64_t* out,
 int sc_batch_sums(const float* row_stats, const int32_t* resp_idx,
                   int64_t n_rows, const int64_t* n_valid, double* batch,
                   int32_t accumulate, void* stream);
+
+/*
+ * sc_reference_copy -- copies `bytes` bytes from src to dst with the plain
+ * streaming kernel that serves as the measured bandwidth reference of the
+ * roofline figures (a read-once / write-once stream with no arithmetic:
+ * 16-byte nontemporal loads and stores, one workgroup per 512 KiB).  Not
+ * part of the SC computation.
+ *   src, dst   device, 16-byte aligned, not overlapping
+ *   bytes      a multiple of 16, at most 2^40; 0 is a no-op
+ * Returns SC_ERR_ARG for a bad argument before any HIP call.
+ */
+int sc_reference_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* sc_status_string(int status);

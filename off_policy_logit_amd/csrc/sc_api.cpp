@@ -253,6 +253,14 @@ int sc_batch_sums(const float* row_stats, const int32_t* resp_idx, int64_t n_row
   return e == hipSuccess ? SC_OK : SC_ERR_HIP;
 }
 
+int sc_reference_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (bytes < 0 || bytes % 16 || bytes > ((int64_t)1 << 40)) return SC_ERR_ARG;
+  if (bytes > 0 && (!src || !dst || !aligned(src, 16) || !aligned(dst, 16))) return SC_ERR_ARG;
+  if (bytes == 0) return SC_OK;
+  hipError_t e = sc::launch_copy(src, dst, bytes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SC_OK : SC_ERR_HIP;
+}
+
 // ---------------------------------------------------------------------------
 // Fused LM-head statistics
 // ---------------------------------------------------------------------------

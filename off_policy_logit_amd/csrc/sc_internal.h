@@ -171,6 +171,7 @@ struct RecParams {
 };
 size_t record_lds_bytes(int k);
 hipError_t launch_record(RecParams P, hipStream_t s);
+hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
 hipError_t launch_group_norm(const float* r, int n_groups, int G, int mode,
                              float eps, float* adv, hipStream_t s);
 hipError_t launch_count_valid(const int32_t* resp, int64_t n, int64_t* out,

@@ -827,6 +827,37 @@ __global__ __launch_bounds__(B) void k_batch_sums(const float* __restrict__ st,
 }
 
 // ---------------------------------------------------------------------------
+// Reference copy: the memory system's rate for a read-once / write-once
+// stream of the same bytes, with no arithmetic.  One workgroup of 512 threads
+// per 512 KiB chunk; each thread keeps 8 16-byte loads in flight, loads and
+// stores nontemporal, through buffer resources over the chunk (the last chunk
+// may be shorter: its out-of-range vectors read zeros and drop their stores).
+// ---------------------------------------------------------------------------
+constexpr int kCopyB = 512;
+constexpr int kCopyU = 8;
+constexpr uint32_t kCopyChunk = 512u << 10;
+
+__global__ __launch_bounds__(kCopyB) void k_copy(const unsigned char* __restrict__ src,
+                                                 unsigned char* __restrict__ dst,
+                                                 int64_t bytes) {
+  const int64_t base = (int64_t)blockIdx.x * kCopyChunk;
+  const int64_t left = bytes - base;
+  const uint32_t n = left < (int64_t)kCopyChunk ? (uint32_t)left : kCopyChunk;
+  const rsrc_t rs = make_rsrc(src + base, n);
+  const rsrc_t rd = make_rsrc(dst + base, n);
+  constexpr uint32_t step = kCopyB * 16u * kCopyU;
+  for (uint32_t o = threadIdx.x * 16u; o < kCopyChunk; o += step) {
+    u32x4 v[kCopyU];
+#pragma unroll
+    for (int u = 0; u < kCopyU; ++u)
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, o + u * kCopyB * 16u, 0, kNT);
+#pragma unroll
+    for (int u = 0; u < kCopyU; ++u)
+      __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, o + u * kCopyB * 16u, 0, kNT);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 template <typename TI, typename TO, bool VECTOR, int B, int KIND>
@@ -867,6 +898,14 @@ hipError_t launch_row(const RowParams& P, int kind, int grid, hipStream_t s) {
     case KIND_CENTER: return launch_row_b<SC_CENTER_BLOCK, KIND_CENTER>(P, grid, s);
     default: return launch_row_b<SC_FUSED_BLOCK, KIND_CORRECT>(P, grid, s);
   }
+}
+
+hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s) {
+  const int64_t grid = (bytes + kCopyChunk - 1) / kCopyChunk;
+  hipLaunchKernelGGL(k_copy, dim3((unsigned)grid), dim3(kCopyB), 0, s,
+                     static_cast<const unsigned char*>(src), static_cast<unsigned char*>(dst),
+                     bytes);
+  return hipGetLastError();
 }
 
 hipError_t launch_group_norm(const float* r, int n_groups, int G, int mode,

@@ -1,9 +1,9 @@
 // Fused LM-head statistics of the SC correction for gfx950.
 //
-// The trainer step of the Score Centering page (section "Score Centering")
-// scores the current policy over the full vocabulary at the rollout
-// temperature and gathers log-probabilities at the recorded ids H and at the
-// sampled id a.  Here the logits z = X W^T (X: final hidden states [n, d],
+// In the trainer step of the Score Centering page (section "Score
+// Centering") the policy is evaluated on every vocabulary id at the rollout's
+// temperature, and log-probabilities are read at the recorded ids H and at
+// the sampled id a.  Here the logits z = X W^T (X: final hidden states [n, d],
 // W: vocabulary projection [V, d], both bf16) are produced tile by tile by
 // bf16 MFMA with fp32 accumulation and consumed in the same kernel by the
 // per-row online softmax statistics, so the [n, V] logits never reach HBM.

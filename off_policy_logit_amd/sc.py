@@ -62,6 +62,7 @@ _SIGS = {
     "sc_lmhead_backward": [_vp, _i64, _i32, _i64, _vp, _i64, _i64, _vp, _vp, _i32, _vp, _vp,
                            _vp, _i32, _f32, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
                            ctypes.c_int, _i64, _vp, _i64, ctypes.c_int, _i64, _vp, _i64, _vp],
+    "sc_reference_copy": [_vp, _vp, _i64, _vp],
     "sc_status_string": [ctypes.c_int],
     "sc_version": [],
 }
@@ -339,6 +340,16 @@ def logprobs_lmhead_static(hidden, weight, head_ids, sampled, resp_idx=None,
         _ptr(out["row_idx"]), _ptr(out.get("head_logp")), _ptr(dev_status),
         _stream(stream)))
     return out
+
+
+def reference_copy(src, dst, stream=None):
+    """sc_reference_copy: the streaming copy kernel used as the bandwidth
+    reference (src and dst: contiguous device tensors of equal byte size)."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n or not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous and of equal byte size")
+    _check(lib().sc_reference_copy(_ptr(src), _ptr(dst), n, _stream(stream)))
+    return dst
 
 
 def lmhead_logits(hidden, weight, out=None, stream=None):

@@ -91,9 +91,9 @@ MODE_CORRECTION = 2   # mu_hat - p
 def trainer_log_softmax(z, temperature):
     """log p over the full vocabulary at the rollout temperature.
 
-    Score Centering section: the trainer scores the current policy over the
-    full model vocabulary at the rollout temperature.  Returns (log p, lse)
-    with lse = logsumexp(z / T) in float64.
+    Score Centering page, section "Score Centering": the trainer evaluates
+    its policy on every vocabulary id, at the temperature the rollout used.
+    Returns (log p, lse) with lse = logsumexp(z / T) in float64.
     """
     u = np.asarray(z, dtype=np.float64) / float(temperature)
     m = np.max(u)

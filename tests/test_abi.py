@@ -292,3 +292,14 @@ def test_lmhead_backward_workspace_and_arguments():
                dict(adv=NULL), dict(nv=NULL), dict(dhd=7), dict(q=NULL)):
         assert bwd(**kw) == ARG, kw
     assert bwd(d=100, xs=104, ws=104) == UNSUP
+
+
+def test_reference_copy_rejects_bad_arguments():
+    L = sc.lib()
+    assert L.sc_reference_copy(FAKE256, FAKE256, 0, NULL) == OK
+    assert L.sc_reference_copy(NULL, FAKE256, 16, NULL) == ARG
+    assert L.sc_reference_copy(FAKE256, NULL, 16, NULL) == ARG
+    assert L.sc_reference_copy(FAKE256, FAKE256, 24, NULL) == ARG     # not a multiple of 16
+    assert L.sc_reference_copy(FAKE256, FAKE256, -16, NULL) == ARG
+    assert L.sc_reference_copy(FAKE2, FAKE256, 16, NULL) == ARG       # misaligned
+    assert L.sc_reference_copy(FAKE256, FAKE256, (1 << 40) + 16, NULL) == ARG
