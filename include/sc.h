@@ -372,6 +372,8 @@ int sc_lmhead_logits(const void* hidden, int64_t n_rows, int32_t d,
  *   d_weight   fp32 [vocab, dw_stride >= d]; written, or added to when
  *              accumulate != 0 (e.g. over several calls of one step)
  * The same argument rules as sc_logprobs_lmhead apply to hidden and weight.
+ * Sizes whose workspace would exceed 2^62 bytes return SC_ERR_UNSUPPORTED
+ * (from the size query and from sc_lmhead_backward alike).
  */
 int sc_lmhead_dlogits(const void* hidden, int64_t n_rows, int32_t d,
                       int64_t hidden_stride, const void* weight, int64_t vocab,

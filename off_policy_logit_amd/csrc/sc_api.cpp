@@ -300,22 +300,22 @@ void lm_order(sc::LmParams& P, int64_t rows, int64_t vocab) {
 size_t lm_workspace(int64_t n, int64_t vocab, int k, sc::LmParams* P, char* base) {
   const int S = lm_splits(vocab);
   size_t off = 0;
-  auto take = [&](size_t bytes) { size_t o = off; off += up256(bytes); return base + o; };
-  char* skey = take((size_t)n * k * 8);
-  char* head_raw = take((size_t)n * k * 4);
-  char* state = take((size_t)S * n * 16);
-  char* za = take((size_t)n * 4);
-  char* scount = take((size_t)n * 4);
-  char* sa = take((size_t)n * 4);
-  char* sflags = take((size_t)n * 4);
-  if (P) {
-    P->skey = reinterpret_cast<long long*>(skey);
-    P->head_raw = reinterpret_cast<float*>(head_raw);
-    P->state = reinterpret_cast<float4*>(state);
-    P->za = reinterpret_cast<float*>(za);
-    P->scount = reinterpret_cast<int32_t*>(scount);
-    P->sa = reinterpret_cast<int32_t*>(sa);
-    P->sflags = reinterpret_cast<uint32_t*>(sflags);
+  auto take = [&](size_t bytes) { size_t o = off; off += up256(bytes); return o; };
+  const size_t skey = take((size_t)n * k * 8);
+  const size_t head_raw = take((size_t)n * k * 4);
+  const size_t state = take((size_t)S * n * 16);
+  const size_t za = take((size_t)n * 4);
+  const size_t scount = take((size_t)n * 4);
+  const size_t sa = take((size_t)n * 4);
+  const size_t sflags = take((size_t)n * 4);
+  if (P && base) {
+    P->skey = reinterpret_cast<long long*>(base + skey);
+    P->head_raw = reinterpret_cast<float*>(base + head_raw);
+    P->state = reinterpret_cast<float4*>(base + state);
+    P->za = reinterpret_cast<float*>(base + za);
+    P->scount = reinterpret_cast<int32_t*>(base + scount);
+    P->sa = reinterpret_cast<int32_t*>(base + sa);
+    P->sflags = reinterpret_cast<uint32_t*>(base + sflags);
   }
   return off;
 }
@@ -458,6 +458,15 @@ struct BwdLayout {
   int64_t vp, cp;
   size_t wt, dz, dzt, xt, total;
 };
+// True when the backward's workspace for these sizes would exceed 2^62 bytes
+// (its size arithmetic stays far from wrapping below that).
+bool bwd_too_large(int64_t chunk, int64_t vocab, int64_t d) {
+  const long double vp = (long double)pad64(vocab), cp = (long double)pad64(chunk);
+  const long double bytes = 2.0L * ((long double)d * vp + (long double)chunk * vp +
+                                    (long double)vocab * cp + (long double)d * cp);
+  return bytes > 4611686018427387904.0L;
+}
+
 BwdLayout bwd_layout(int64_t chunk, int64_t vocab, int64_t d) {
   BwdLayout L{};
   L.vp = pad64(vocab);
@@ -573,6 +582,7 @@ int64_t sc_lmhead_backward_workspace_size(int64_t chunk_rows, int64_t vocab, int
   if (chunk_rows < 1 || chunk_rows > kMaxI32 || vocab < 1 || vocab > kMaxI32 - sc::kLmTileV ||
       d < 1)
     return SC_ERR_ARG;
+  if (bwd_too_large(chunk_rows, vocab, d)) return SC_ERR_UNSUPPORTED;
   return (int64_t)bwd_layout(chunk_rows, vocab, d).total;
 }
 
@@ -596,6 +606,7 @@ int sc_lmhead_backward(const void* hidden, int64_t n_rows, int32_t d, int64_t hi
   if (!d_weight || dw_stride < d || !aligned(d_weight, 4)) return SC_ERR_ARG;
   if (chunk_rows < 1 || chunk_rows > kMaxI32 || !workspace || !aligned(workspace, 256))
     return SC_ERR_ARG;
+  if (bwd_too_large(chunk_rows, vocab, d)) return SC_ERR_UNSUPPORTED;
   const BwdLayout L = bwd_layout(chunk_rows, vocab, d);
   if (L.cp > kLmMaxStride || L.vp > kLmMaxStride) return SC_ERR_UNSUPPORTED;
   if (workspace_bytes < 0 || (size_t)workspace_bytes < L.total) return SC_ERR_ARG;

@@ -150,7 +150,9 @@ void k_row(RowParams P) {
       continue;
     }
 
-    const TI* zrow = reinterpret_cast<const TI*>(P.logits) + row * P.row_stride;
+    // (sc_center without an output row reads no logits: they may be absent)
+    const TI* zrow = P.logits ? reinterpret_cast<const TI*>(P.logits) + row * P.row_stride
+                              : nullptr;
     const bool a_ok = a >= 0 && a < V;
     const bool need_stage = (KIND != KIND_CENTER) || has_out;
 

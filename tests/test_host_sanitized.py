@@ -1,0 +1,128 @@
+"""The library's C ABI and its row and LM-head kernels on the CPU, under
+AddressSanitizer and UndefinedBehaviorSanitizer (tests/host: the kernels are
+compiled for the host against an emulated device environment in which every
+GPU thread is a fiber, wave operations and barriers switch fibers, and
+buffer-resource accesses are bounds checked).
+
+* argument checks and workspace-size arithmetic at the extremes;
+* seeded random shapes through sc_logprobs, sc_correct and sc_center (data
+  errors, -inf / NaN logits, ragged vectors, strided rows);
+* the LM-head entry points on one small ragged problem (two row tiles, two
+  vocabulary tiles, a three-chunk backward), their outputs compared with the
+  oracle: logits with the fp32 summation bound, statistics at the row
+  kernels' tolerances, dLogits at the bf16 bar, dHidden and dW with the
+  backward's tolerance.  This also pins the emulated MFMA's operand layout.
+
+A sanitizer finding, an out-of-range store, a barrier deadlock or a failed
+entry point ends the harness with a non-zero status.
+"""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import sc_oracle as O
+from tests.parity import MIN_BF16_EQUAL, check_row, compare_bf16
+
+HOST = os.path.join(os.path.dirname(os.path.abspath(__file__)), "host")
+ENV = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:detect_stack_use_after_return=0",
+           UBSAN_OPTIONS="print_stacktrace=1")
+
+
+@pytest.fixture(scope="module")
+def harness():
+    sys.path.insert(0, HOST)
+    try:
+        import build as host_build
+        return host_build.build()
+    finally:
+        sys.path.remove(HOST)
+
+
+def run(exe, *args):
+    res = subprocess.run([exe, *map(str, args)], capture_output=True, text=True, env=ENV,
+                         timeout=900)
+    tail = (res.stdout[-2000:] + res.stderr[-4000:])
+    assert res.returncode == 0 and "HARNESS OK" in res.stdout, tail
+    return res.stdout
+
+
+def test_abi_checks_under_sanitizers(harness):
+    out = run(harness, "abi")
+    assert "0 failures" in out
+
+
+def test_row_kernels_random_shapes_under_sanitizers(harness):
+    out = run(harness, "rows", 16, 3)
+    assert out.count("rows case") == 16
+
+
+def read_lmhead(path):
+    b = open(path, "rb").read()
+    o = 0
+
+    def take(dt, n):
+        nonlocal o
+        a = np.frombuffer(b, dt, n, o)
+        o += a.nbytes
+        return a
+    n, V, d, K, chunk, dzs = (int(v) for v in take(np.int32, 6))
+    r = dict(n=n, V=V, d=d, K=K, chunk=chunk)
+    bf = lambda u: (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)  # noqa: E731
+    r["x"] = bf(take(np.uint16, n * d)).reshape(n, d)
+    r["w"] = bf(take(np.uint16, V * d)).reshape(V, d)
+    r["ids"] = take(np.int32, n * K).reshape(n, K)
+    r["q"] = take(np.float32, n * K).reshape(n, K)
+    r["sampled"] = take(np.int32, n)
+    r["resp"] = take(np.int32, n)
+    r["adv"] = take(np.float32, 4)
+    r["n_valid"] = int(take(np.int64, 1)[0])
+    r["z"] = take(np.float32, n * V).reshape(n, V)
+    r["stats"] = take(np.float32, n * 16).reshape(n, 16)
+    r["idx"] = take(np.int32, n * 2).reshape(n, 2)
+    r["hl"] = take(np.float32, n * K).reshape(n, K)
+    r["dz"] = take(np.uint16, n * dzs).reshape(n, dzs)[:, :V]
+    r["dh"] = take(np.float32, n * d).reshape(n, d)
+    r["dw"] = take(np.float32, V * d).reshape(V, d)
+    r["status"] = int(take(np.uint32, 1)[0])
+    return r
+
+
+def test_lmhead_entry_points_match_oracle_under_sanitizers(harness, tmp_path):
+    path = tmp_path / "lmhead.bin"
+    # 260 rows (two row tiles), 300 ids (two vocabulary tiles, ragged),
+    # d = 64, K = 8, backward chunks of 100 rows (three, the last ragged)
+    run(harness, "lmhead", path, 260, 300, 64, 8, 100)
+    r = read_lmhead(path)
+    assert r["status"] == 0
+    x, w, d = r["x"], r["w"], r["d"]
+    # the GEMM's logits against the float64 product
+    err = np.abs(r["z"] - O.lmhead_logits(x, w))
+    bound = (d + 16) * 2.0 ** -24 * (np.abs(x) @ np.abs(w).T)
+    assert np.all(err <= bound), float(err.max())
+    # statistics on the emulated logits, at the row kernels' tolerances;
+    # the sc_center columns need q and the advantages: checked through the
+    # dLogits rows below
+    G = np.zeros((r["n"], r["V"]))
+    for p in range(r["n"]):
+        if r["resp"][p] < 0:
+            assert list(r["idx"][p]) == [-1, -1]
+            continue
+        o = O.sc_row(r["z"][p].astype(np.float64), 1.0, r["ids"][p], r["q"][p],
+                     int(r["sampled"][p]))
+        check_row(f"emulated lmhead row {p}",
+                  dict(stats=r["stats"][p], idx=r["idx"][p], head_logp=r["hl"][p]), o,
+                  stats_only=True)
+        G[p] = O.sc_row(r["z"][p].astype(np.float64), 1.0, r["ids"][p], r["q"][p],
+                        int(r["sampled"][p]), advantage=float(r["adv"][r["resp"][p]]),
+                        n_valid=r["n_valid"], row_mode=O.MODE_DLOGITS)["row"]
+    dist, eq = compare_bf16(r["dz"], G)
+    assert dist <= 1 and eq >= MIN_BF16_EQUAL, (dist, eq)
+    # gradients: the GPU tests' bound (bf16 rounding of dZ plus fp32 sums)
+    rdX, rdW = O.lmhead_backward(x, w, G)
+    tol_x = 2.0 ** -8 * (np.abs(G) @ np.abs(w)) + 1e-30
+    tol_w = 2.0 ** -8 * (np.abs(G).T @ np.abs(x)) + 1e-30
+    assert np.all(np.abs(r["dh"] - rdX) <= tol_x), float(np.abs(r["dh"] - rdX).max())
+    assert np.all(np.abs(r["dw"] - rdW) <= tol_w), float(np.abs(r["dw"] - rdW).max())
