@@ -150,3 +150,46 @@ def test_lmhead_backward_full_vocab_slice():
     bound = 2.0 ** -8 * (l1 @ np.abs(host(c["hidden"])).astype(np.float64)) + 1e-12
     assert np.all(np.abs(colsum) <= bound), float((np.abs(colsum) / bound).max())
     assert bool(torch.isfinite(dW).all()) and bool(torch.isfinite(dh.float()).all())
+
+
+def test_lmhead_backward_1024_row_chunks_full_vocab():
+    """16 chunks of 1,024 rows at V = 248,320, d = 4,096 against the bench's
+    8,192-row chunks on the same inputs: dHidden bit-identical (each row's
+    product runs over the same vocabulary tiles in the same order, and both
+    chunk sizes are whole 256-row tiles), dW within the rounding bound of
+    the two accumulation orders, and sampled dHidden rows against the
+    oracle."""
+    n, V, d, T = 16_384, synthetic.VOCAB, 4096, 1.0
+    say(f"lmhead backward 1024-row chunks n={n} V={V} d={d}: forward")
+    w, c, resp, adv, nv, st, _ = forward(n, V, d, T, 7, w_sd=0.02)
+    args = (c["hidden"], w, st, c["head_ids"], c["head_probs"], c["sampled"], resp, adv, nv)
+    out = {}
+    for chunk in (8192, 1024):
+        say(f"lmhead backward 1024-row chunks: backward with chunk_rows={chunk}")
+        dh = torch.empty(n, d, dtype=torch.float32, device=DEV)
+        dW = torch.empty(V, d, device=DEV)
+        sc.lmhead_backward(*args, temperature=T, d_hidden=dh, d_weight=dW, chunk_rows=chunk)
+        torch.cuda.synchronize()
+        out[chunk] = (dh, dW)
+    assert torch.equal(out[1024][0].view(torch.int32), out[8192][0].view(torch.int32))
+    dW1, dW8 = out[1024][1].double(), out[8192][1].double()
+    # each dW entry is a sum over the 16,384 rows of bf16 dZ x X products in
+    # fp32: both orders lie within 2^-8 sum |dZ||X| of the exact value
+    rng = np.random.default_rng(5)
+    vs = torch.as_tensor(np.unique(rng.choice(V, 64, replace=False)), device=DEV)
+    dzt = sc.lmhead_dlogits(c["hidden"], w, st, c["head_ids"], c["head_probs"], c["sampled"],
+                            resp, adv, nv, temperature=T)
+    g = dzt[:, vs].double()                               # [n, 64]
+    del dzt
+    bound = 2.0 ** -7 * (g.abs().T @ c["hidden"].double().abs())
+    assert bool(((dW1[vs] - dW8[vs]).abs() <= bound).all())
+    rows = np.unique(np.concatenate([rng.choice(n, 3, replace=False), [0, 1023, 1024, n - 1]]))
+    sub = torch.as_tensor(rows, device=DEV)
+    z = sc.lmhead_logits(c["hidden"][sub].contiguous(), w)
+    cs = {k2: v[sub] for k2, v in c.items()}
+    G = oracle_dlogits(z, T, cs, resp[sub], adv, int(nv.item()), range(len(rows)),
+                       O.IS_NONE, True)
+    W = host(w)
+    rdX = G @ W
+    tol = 2.0 ** -8 * (np.abs(G) @ np.abs(W)) + 1e-30
+    assert np.all(np.abs(host(out[1024][0][sub]) - rdX) - tol <= 0)

@@ -853,3 +853,61 @@ def test_argmax_ties_first_index(dtype):
         o = O.sc_row(zh[r], 1.0, ids[r], q[r], a[r])
         assert o["argmax"] == min(patterns[r % len(patterns)]), r
         assert got_s[r] == o["argmax"] and got_c[r] == o["argmax"], (r, got_s[r], got_c[r], o["argmax"])
+
+
+def test_flat_rows_k1024_full_vocabulary():
+    """Rows whose tail terms are all near their largest: exactly uniform
+    logits (every one of the ~8,200 listed elements a tail term of weight
+    one, argmax at index 0), uniform with the 1,024 recorded ids in one
+    contiguous block, near-flat N(0, 0.01^2), and a two-level row (recorded
+    ids one logit above the rest), at V = 248,320, K = 1,024, bf16."""
+    n, V, K = 8, synthetic.VOCAB, 1024
+    say(f"flat rows n={n} V={V} K={K} bf16")
+    d, z = crafted(n, V, K, seed=99, dtype="bf16")
+    ids = d["head_ids"].cpu().numpy()
+    rng = np.random.default_rng(99)
+    z[0:2] = 0.5
+    z[2:4] = 0.5
+    s0 = int(rng.integers(0, V - K))
+    ids[2] = np.arange(s0, s0 + K, dtype=np.int32)
+    ids[3] = np.arange(V - K, V, dtype=np.int32)                 # up to the row's end
+    z[4:6] = torch.from_numpy(rng.normal(0, 0.01, (2, V)).astype(np.float32)).to(
+        torch.bfloat16).float().numpy()
+    z[6:8] = 0.0
+    z[6, ids[6]] = 1.0
+    z[7, ids[7]] = 1.0
+    d["head_ids"] = torch.from_numpy(ids).to(DEV)
+    d["logits"] = torch.from_numpy(z).to(DEV).to(torch.bfloat16)
+    adv = torch.tensor([0.8, -1.2], device=DEV)
+    n_valid = sc.count_valid(d["resp_idx"])
+    for mode in (O.MODE_DLOGITS, O.MODE_CORRECTION):
+        out = run_correct(d, adv, n_valid, 1.0, mode, "bf16")
+        torch.cuda.synchronize()
+        assert int(out["status"].item()) == 0
+        assert out["row_idx"][0, 0].item() == 0 and out["row_idx"][1, 0].item() == 0
+        check_rows(f"flat rows mode={mode}", d, out, np.arange(n), adv.cpu().numpy(), n, 1.0,
+                   mode, "bf16", logits_h=z)
+
+
+# Large vocabularies around the full one (whole 256-thread rounds of
+# vectors, a ragged tail, one vector more) with a -inf-masked row, the row
+# maximum in the last vectors and a flat row; bf16 and fp32 output.
+@pytest.mark.parametrize("V", [180224, 180231, 253952, 253960])
+def test_large_vocabularies_masked_and_flat_rows(V):
+    n, K = 16, 128
+    say(f"large vocabulary n={n} V={V} K={K} bf16")
+    d, z = crafted(n, V, K, seed=V, dtype="bf16")
+    ids = d["head_ids"].cpu().numpy()
+    z[3, ::3] = -np.inf                  # masked vocabulary (careful pass-2 values)
+    z[3, ids[3]] = 0.25
+    z[5, V - 2] = 30.0                   # the row maximum in the last vectors
+    z[6, :] = 1.5                        # flat row: argmax 0, equal tail terms
+    d["logits"] = torch.from_numpy(z).to(DEV).to(torch.bfloat16)
+    adv = torch.tensor([0.8, -1.2, 0.3, 1.1], device=DEV)
+    n_valid = sc.count_valid(d["resp_idx"])
+    for out_dtype in ("bf16", "f32"):
+        out = run_correct(d, adv, n_valid, 1.0, O.MODE_DLOGITS, out_dtype)
+        torch.cuda.synchronize()
+        assert int(out["status"].item()) == 0
+        check_rows(f"large vocabulary V={V} ->{out_dtype}", d, out, np.arange(n),
+                   adv.cpu().numpy(), n, 1.0, O.MODE_DLOGITS, out_dtype, logits_h=z)
