@@ -103,6 +103,7 @@ void k_row(RowParams P) {
   __shared__ float sh_za;
   __shared__ uint32_t sh_status;
   __shared__ int sh_ninf;
+  __shared__ int sh_am;
 
   const uint32_t hmask = (uint32_t)P.hs - 1;
   const int hshift = P.hshift;
@@ -367,10 +368,6 @@ void k_row(RowParams P) {
           h_t += marked ? 0.f : acch;
         }
       }
-      // The element index of the thread's maximum: the first element equal
-      // to m_t in the vector that raised it, read again (one load).
-      Raw am_raw = IO::ninf();
-      if (am_vec >= 0) am_raw = ld(am_vec, std::false_type{});
       // A -inf logit among this thread's unmarked vectors left h_t NaN (its
       // term 0 * -inf): recompute the entropy sum against the final E_t with
       // the term clamped to 0, reading the thread's vectors again.  A NaN
@@ -400,21 +397,25 @@ void k_row(RowParams P) {
           if (z > m_t) { m_t = z; am_direct = n_full * N + i; }
         }
       }
-      int am_t = 0x7fffffff;
-      if (am_direct >= 0) {
-        am_t = am_direct;
-      } else if (am_vec >= 0) {
-#pragma unroll
-        for (int i = N - 1; i >= 0; --i)
-          if (IO::elem(am_raw, i) == m_t) am_t = (int)((am_vec * B + t) * N + i);
-      }
+      // Argmax key: the first element index of the vector that holds the
+      // thread's maximum (for the partial vector, the element itself).
+      // Vectors do not overlap, so among the threads holding the row maximum
+      // the lowest key is the vector of the row's first maximum.
+      int am_key = 0x7fffffff;
+      if (am_direct >= 0) am_key = am_direct;
+      else if (am_vec >= 0) am_key = (am_vec * B + t) * N;
 
       // ---------------------------------------------------------- finalize
       float mv = m_t;
-      int mi = am_t;
+      int mi = am_key;
       block_argmax<B>(mv, mi, redf, redi);
       m = mv;
       argmax = mi;
+      // Only the thread owning that vector reads it again, to find the
+      // element (one load per workgroup, awaited after the list below).
+      const bool am_owner = mi < n_full * N && am_key == mi;
+      Raw am_raw = IO::ninf();
+      if (am_owner) am_raw = ld(am_vec, std::false_type{});
       E_row = ref_exp(m, c_hi);
       // This thread's unmarked sums, moved to the row's reference (powers of
       // two: exact).  Then its marked vectors: recorded logits to headz, the
@@ -452,7 +453,15 @@ void k_row(RowParams P) {
         }
         if (id == a) sh_za = z;
       }
+      if (am_owner) {   // the first element equal to the row maximum
+        int i0 = 0;
+#pragma unroll
+        for (int i = N - 1; i >= 0; --i)
+          if (IO::elem(am_raw, i) == m) i0 = i;
+        sh_am = mi + i0;
+      }
       __syncthreads();
+      if (mi < n_full * N) argmax = sh_am;
       // Recorded ids: 2^(z c - E_row) and its exponent-weighted term.
       double s_head = 0.0;
       uint32_t fl = 0;
