@@ -3,8 +3,9 @@
 // AddressSanitizer and UndefinedBehaviorSanitizer.
 //
 //   harness abi                      argument checks and workspace arithmetic
-//   harness rows CASES SEED          seeded random shapes through sc_logprobs,
-//                                    sc_correct and sc_center
+//   harness rows CASES SEED [OUT]    seeded random shapes through sc_logprobs,
+//                                    sc_correct and sc_center; with OUT, each
+//                                    case's sc_correct inputs and outputs
 //   harness lmhead OUT N V D K CHUNK the LM-head entry points on one seeded
 //                                    problem; inputs and outputs written to OUT
 //                                    for a comparison with the oracle
@@ -138,7 +139,11 @@ static void abi_checks() {
 // ---------------------------------------------------------------------------
 // Row kernels: seeded random shapes (bounds, barriers, sanitizers).
 // ---------------------------------------------------------------------------
-static void rows(int cases, uint64_t seed0) {
+// With `out`, each case's sc_correct inputs and outputs are appended to that
+// file (before sc_center writes its own) for a comparison with the oracle.
+static void rows(int cases, uint64_t seed0, const char* out = nullptr) {
+  FILE* rec = out ? fopen(out, "wb") : nullptr;
+  if (out && !rec) { ++failures; return; }
   for (int c = 0; c < cases; ++c) {
     std::mt19937_64 g(seed0 * 1000003 + c);
     auto U = [&](int lo, int hi) { return lo + (int)(g() % (uint64_t)(hi - lo + 1)); };
@@ -202,6 +207,25 @@ static void rows(int cases, uint64_t seed0) {
                       rlp.data(), resp.data(), adv.data(), n, T, &nv, stats.data(), idx.data(),
                       hl.data(), coef.data(), outp, out_dtype, stride, mode, SC_IS_NONE, 0.5f,
                       2.f, 1, &status, nullptr), SC_OK);
+    if (rec) {
+      const int32_t hdr[7] = {n, V, K, (int32_t)stride, dtype, out_dtype, mode};
+      fwrite(hdr, 4, 7, rec);
+      fwrite(&T, 4, 1, rec);
+      fwrite(zf.data(), 4, zf.size(), rec);           // the fp32 logits (bf16 input: rounded below)
+      fwrite(ids.data(), 4, ids.size(), rec);
+      fwrite(q.data(), 4, q.size(), rec);
+      fwrite(sampled.data(), 4, n, rec);
+      fwrite(resp.data(), 4, n, rec);
+      fwrite(rlp.data(), 4, n, rec);
+      fwrite(adv.data(), 4, n, rec);
+      fwrite(&nv, 8, 1, rec);
+      fwrite(stats.data(), 4, stats.size(), rec);
+      fwrite(idx.data(), 4, idx.size(), rec);
+      fwrite(hl.data(), 4, hl.size(), rec);
+      fwrite(coef.data(), 4, coef.size(), rec);
+      if (out_dtype == SC_BF16) fwrite(out16.data(), 2, out16.size(), rec);
+      else fwrite(out32.data(), 4, out32.size(), rec);
+    }
     EXPECT(sc_center(logits, dtype, n, V, stride, ids.data(), q.data(), K, sampled.data(),
                      rlp.data(), resp.data(), adv.data(), n, T, &nv, stats.data(), idx.data(),
                      hl.data(), coef.data(), outp, out_dtype, stride, mode, SC_IS_NONE, 0.5f, 2.f,
@@ -209,6 +233,7 @@ static void rows(int cases, uint64_t seed0) {
     printf("rows case %d: n=%d V=%d K=%d in=%d out=%d mode=%d pad=%d T=%g status %u\n", c, n, V,
            K, dtype, out_dtype, mode, pad, T, status);
   }
+  if (rec) fclose(rec);
 }
 
 // ---------------------------------------------------------------------------
@@ -330,7 +355,7 @@ int main(int argc, char** argv) {
   if (mode == "abi") {
     abi_checks();
   } else if (mode == "rows" && argc > 3) {
-    rows(atoi(argv[2]), (uint64_t)atoll(argv[3]));
+    rows(atoi(argv[2]), (uint64_t)atoll(argv[3]), argc > 4 ? argv[4] : nullptr);
   } else if (mode == "lmhead" && argc > 7) {
     lmhead(argv[2], atoi(argv[3]), atoi(argv[4]), atoi(argv[5]), atoi(argv[6]), atoi(argv[7]));
   } else if (mode == "replay" && argc > 5) {

@@ -30,8 +30,10 @@ value where that is larger" (``f32_tol``); below |x| = 8 this is the
 absolute tolerance itself.
 
 Extra signals, beyond the stated bar: entropy abs 1e-5 + rel 1e-6; the
-importance ratio w and the weight rel 1e-6 (w = exp(log p(a) - log mu(a)) is
-formed in float64 from log p(a), whose own error is far below 1e-6); reverse
+importance ratio w and the weight rel 1e-6, or one fp32 spacing of the value
+where that is larger (w = exp(log p(a) - log mu(a)) is formed in float64 from
+log p(a), whose own error is far below 1e-6, and stored as fp32: a ratio below
+the fp32 subnormal range stores as 0); reverse
 KL abs 1e-6 + rel 1e-5.  A masked-IS decision within w's tolerance of a bound
 may go either way (the test then checks the GPU's side against the oracle
 row at that weight).
@@ -59,6 +61,15 @@ def f32_tol(want, atol):
     w = np.abs(np.asarray(want, np.float64))
     sp = np.spacing(np.minimum(w, 3e38).astype(np.float32)).astype(np.float64)
     return np.maximum(atol, sp)
+
+
+def f32_rel(want, rel):
+    """rel |value|, or one fp32 spacing of the value where that is larger
+    (a value below the fp32 subnormal range stores as 0 or the smallest
+    subnormal, which no relative bound can ask more of)."""
+    w = np.abs(np.asarray(want, np.float64))
+    sp = np.spacing(np.minimum(w, 3e38).astype(np.float32)).astype(np.float64)
+    return np.maximum(rel * w, sp)
 
 
 def bf16_bits_to_f64(bits):
@@ -164,10 +175,10 @@ def check_row(tag, g, o, A=1.0, T=1.0, n_valid=1, mode=O.MODE_DLOGITS,
     close("S", st[6], o["S"], 1e-6)
     close("coef", g["coef"], o["coef"], f32_tol(o["coef"], 1e-6))
     if rlp is not None:
-        close("w", st[12], o["w"], REL_W * abs(o["w"]))
+        close("w", st[12], o["w"], f32_rel(o["w"], REL_W))
     wt, boundary = _gpu_weight(o, st[12], is_mode, is_lo, is_hi)
     rel_wt = REL_W if (is_mode != O.IS_NONE and wt != 0) else 0.0
-    close("weight", st[13], wt, rel_wt * abs(wt))
+    close("weight", st[13], wt, f32_rel(wt, rel_wt) if rel_wt else 0.0)
     bracket = o["logp_a"] - (float(np.sum(o["coef"] * o["head_logp"])) if centering else 0.0)
     loss = -A * wt * bracket
     close("loss", st[7], loss, f32_tol(loss, 1e-4))

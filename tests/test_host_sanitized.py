@@ -6,7 +6,8 @@ buffer-resource accesses are bounds checked).
 
 * argument checks and workspace-size arithmetic at the extremes;
 * seeded random shapes through sc_logprobs, sc_correct and sc_center (data
-  errors, -inf / NaN logits, ragged vectors, strided rows);
+  errors, -inf / NaN logits, ragged vectors, strided rows), sc_correct's
+  outputs on every row compared with the oracle at the GPU tests' bar;
 * the LM-head entry points on one small ragged problem (two row tiles, two
   vocabulary tiles, a three-chunk backward), their outputs compared with the
   oracle: logits with the fp32 summation bound, statistics at the row
@@ -24,7 +25,10 @@ import numpy as np
 import pytest
 
 from oracle import sc_oracle as O
-from tests.parity import MIN_BF16_EQUAL, check_row, compare_bf16
+import torch
+
+from off_policy_logit_amd.sc import SC_BF16
+from tests.parity import MIN_BF16_EQUAL, bf16_bar, check_row, compare_bf16
 
 HOST = os.path.join(os.path.dirname(os.path.abspath(__file__)), "host")
 ENV = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:detect_stack_use_after_return=0",
@@ -54,9 +58,75 @@ def test_abi_checks_under_sanitizers(harness):
     assert "0 failures" in out
 
 
-def test_row_kernels_random_shapes_under_sanitizers(harness):
-    out = run(harness, "rows", 16, 3)
-    assert out.count("rows case") == 16
+def read_rows(path):
+    """The cases `harness rows ... OUT` recorded: sc_correct's inputs and
+    outputs per case."""
+    b = open(path, "rb").read()
+    o = 0
+
+    def take(dt, n):
+        nonlocal o
+        a = np.frombuffer(b, dt, n, o)
+        o += a.nbytes
+        return a
+    cases = []
+    while o < len(b):
+        n, V, K, stride, dtype, out_dtype, mode = (int(v) for v in take(np.int32, 7))
+        c = dict(n=n, V=V, K=K, dtype=dtype, out_dtype=out_dtype, mode=mode,
+                 T=float(take(np.float32, 1)[0]))
+        z = take(np.float32, n * stride).reshape(n, stride)[:, :V]
+        if dtype == SC_BF16:   # the kernel read the logits rounded to bf16 (RNE)
+            z = torch.from_numpy(z.copy()).to(torch.bfloat16).float().numpy()
+        c["z"] = z.astype(np.float64)
+        c["ids"] = take(np.int32, n * K).reshape(n, K)
+        c["q"] = take(np.float32, n * K).reshape(n, K)
+        c["sampled"] = take(np.int32, n)
+        c["resp"] = take(np.int32, n)
+        c["rlp"] = take(np.float32, n)
+        c["adv"] = take(np.float32, n)
+        c["n_valid"] = int(take(np.int64, 1)[0])
+        c["stats"] = take(np.float32, n * 16).reshape(n, 16)
+        c["idx"] = take(np.int32, n * 2).reshape(n, 2)
+        c["hl"] = take(np.float32, n * K).reshape(n, K)
+        c["coef"] = take(np.float32, n * K).reshape(n, K)
+        if out_dtype == SC_BF16:
+            c["row"] = take(np.uint16, n * stride).reshape(n, stride)[:, :V]
+        else:
+            c["row"] = take(np.float32, n * stride).reshape(n, stride)[:, :V]
+        cases.append(c)
+    return cases
+
+
+def test_row_kernels_random_shapes_under_sanitizers(harness, tmp_path):
+    """Bounds and sanitizers on every entry point, and sc_correct's outputs
+    (statistics, coefficients, the row in every mode and output type) on
+    every row against the oracle at the GPU tests' bar."""
+    path = tmp_path / "rows.bin"
+    out = run(harness, "rows", 32, 3, path)
+    assert out.count("rows case") == 32
+    cases = read_rows(path)
+    assert len(cases) == 32
+    modes = {0: O.MODE_DLOGITS, 1: O.MODE_SCORE, 2: O.MODE_CORRECTION}
+    bf, checked = [], 0
+    for ci, c in enumerate(cases):
+        row_dtype = "bf16" if c["out_dtype"] == SC_BF16 else "f32"
+        for p in range(c["n"]):
+            g = dict(stats=c["stats"][p], idx=c["idx"][p], head_logp=c["hl"][p],
+                     coef=c["coef"][p], row=c["row"][p])
+            if c["resp"][p] < 0:
+                assert np.all(g["stats"][:15] == 0) and list(g["idx"]) == [-1, -1]
+                assert np.all(g["row"] == 0)
+                continue
+            A = float(c["adv"][c["resp"][p]])
+            o = O.sc_row(c["z"][p], c["T"], c["ids"][p], c["q"][p], int(c["sampled"][p]),
+                         rollout_logp=float(c["rlp"][p]), advantage=A,
+                         n_valid=c["n_valid"], row_mode=modes[c["mode"]])
+            check_row(f"emulated rows case {ci} row {p}", g, o, A=A, T=c["T"],
+                      n_valid=c["n_valid"], mode=modes[c["mode"]], row_dtype=row_dtype,
+                      bf16_stats=bf, rlp=float(c["rlp"][p]))
+            checked += 1
+    assert checked >= 60, checked
+    bf16_bar(bf, "emulated random rows")
 
 
 def read_lmhead(path):
