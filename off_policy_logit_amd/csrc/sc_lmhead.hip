@@ -52,8 +52,11 @@ constexpr int kWR = SC_LM_WAVE_ROWS;    // rows per wave (kWR / 32 MFMA column b
 constexpr int kB = 2 * (kLmTileP / kWR) * 64;   // threads: 2 (vocab halves) x kTP / kWR waves
 constexpr int kPitch = kKB * 2 + 16;    // LDS bytes per tile row (bank rotation)
 constexpr int kBuf = kTV * kPitch;      // one operand buffer
-constexpr int kOffBm = 4 * kBuf;        // [kTP][8] hit words of the chunk
-constexpr int kOffBeg = kOffBm + kTP * 8 * 4;
+// Hit words of the chunk, 8 per row at a row stride of 9 words: the 32 rows
+// a wave's lanes read at once fall in 32 different banks.
+constexpr int kBmS = 9;
+constexpr int kOffBm = 4 * kBuf;        // [kTP][kBmS] hit words of the chunk
+constexpr int kOffBeg = kOffBm + kTP * kBmS * 4;
 constexpr int kLds = kOffBeg + kTP * 4;
 static_assert(kTV == 256 && kTP == 256 && kKB == 64, "tile shape is fixed");
 static_assert(kLds <= 160 * 1024, "LDS budget");
@@ -348,11 +351,11 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
     if (t >= kTP) return;
     const int v0 = ck * kTV, v1 = v0 + kTV;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) bm[t * 8 + q] = 0u;
+    for (int q = 0; q < 8; ++q) bm[t * kBmS + q] = 0u;
     beg[t] = cur;
     while (nid < v1) {
       const int o = nid - v0;
-      bm[t * 8 + (o >> 5)] |= 1u << (o & 31);
+      bm[t * kBmS + (o >> 5)] |= 1u << (o & 31);
       ++cur;
       nid = cur < cnt ? (int)(P.skey[my_p * P.k + cur] >> 32) : kNoIdx;
     }
@@ -497,7 +500,7 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) {
         const int vb = v0 + wv * 128 + bi * 32;    // first id of the block
-        const uint32_t hw = bm[ploc * 8 + wv * 4 + bi];
+        const uint32_t hw = bm[ploc * kBmS + wv * 4 + bi];
         uint32_t word = hw;
         if (ragged) {
           const int nv = V - vb;                    // valid ids in the block
