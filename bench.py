@@ -62,7 +62,10 @@ def source_digest():
     for p in KERNEL_SOURCES:
         with open(p, "rb") as f:
             h.update(f.read())
-    h.update(" ".join(B.FLAGS).encode())
+    # include paths relative to the repository: the same tree can sit at
+    # another absolute path (where the bench runs)
+    flags = [os.path.relpath(f, ROOT) if os.path.isabs(f) else f for f in B.FLAGS]
+    h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
 
