@@ -88,6 +88,7 @@ int layout(sc::RowParams& P, int kind) {
   P.ke = P.k + 2;
   P.off_lval = take((size_t)P.ke * N * 4);
   P.off_lvec = take((size_t)P.ke * 4);
+  P.off_lslot = take((size_t)P.ke * N * 2);   // recorded-id slot of each listed element
   P.lds_bytes = off;
   return off <= kMaxLds ? SC_OK : SC_ERR_UNSUPPORTED;
 }

@@ -73,7 +73,7 @@ struct RowParams {
   // LDS layout (bytes into dynamic shared memory)
   int hs, hshift, bm_wpt, ke;
   int off_bitmap, off_hkey, off_hval, off_headz, off_headp, off_headlp, off_hout;
-  int off_lval, off_lvec;
+  int off_lval, off_lvec, off_lslot;
   size_t lds_bytes;
 };
 

@@ -28,7 +28,8 @@
 //   pass 2    (optional) the row streamed again to write one output element
 //             per vocabulary id: off-head ids get alpha * p_v from one exp2 of
 //             an exactly formed exponent; the listed vectors are written from
-//             the list, one 16-byte store each.
+//             the list, one 16-byte store each (in the fused kind before the
+//             stream, their values formed element-parallel).
 #include "sc_device.h"
 #include "sc_internal.h"
 
@@ -95,6 +96,7 @@ void k_row(RowParams P) {
   float* hout = reinterpret_cast<float*>(lds + P.off_hout);       // output value at H
   float* lval = reinterpret_cast<float*>(lds + P.off_lval);       // listed vectors' values
   int* lvec = reinterpret_cast<int*>(lds + P.off_lvec);           // listed vectors' indices
+  int16_t* lslot = reinterpret_cast<int16_t*>(lds + P.off_lslot); // listed elements' slots in H
 
   __shared__ float redf[NW];
   __shared__ int redi[NW];
@@ -443,6 +445,7 @@ void k_row(RowParams P) {
         if (id >= V) continue;
         const float z = lval[i];
         const int slot = idset_find(hkey, hval, hmask, hshift, id);
+        lslot[i] = (int16_t)slot;   // kept for the listed vectors' output values
         if (slot >= 0) {
           headz[slot] = z;
         } else {
@@ -704,15 +707,48 @@ void k_row(RowParams P) {
         put(j, false, o);
       }
     };
+    if (KIND == KIND_CORRECT) {
+      // The listed vectors first, while the stream below keeps the memory
+      // busy: each listed element's value (recorded ids take hout, the
+      // sampled id outside H the float64 value alpha p_a + scale, every other
+      // element the streamed value) computed element-parallel from the slot
+      // the finalize found, in place of its logit; then one store per vector.
+      const float va = (a_ok && a_slot < 0)
+                           ? (float)(alpha * exp2((double)sh_za * c64 - F) + scale) : 0.f;
+      for (int i = t; i < n_ent * N; i += B) {
+        const int e = i / N;
+        const int id = lvec[e] * N + (i - e * N);
+        float val = 0.f;
+        if (id < V) {
+          const int slot = lslot[i];
+          if (slot >= 0) val = hout[slot];
+          else if (id == a) val = va;
+          else val = p2_value<true>(lval[i], Q);
+        }
+        lval[i] = val;
+      }
+      __syncthreads();
+      for (int e = t; e < n_ent; e += B) {
+        const int n = lvec[e];
+        float o[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) o[i] = lval[e * N + i];
+        if (n < n_full) {
+          RowOut<TO, N>::store(orow, n, o);
+        } else {
+          for (int i = 0; i < rem; ++i) store_elem(orow, (int64_t)n * N + i, o[i]);
+        }
+      }
+    }
     if (careful) stream2(std::true_type{});
     else stream2(std::false_type{});
     if (KIND == KIND_CENTER) {
       if (rem_owner) capture_partial();
       __syncthreads();
     }
-    // Listed vectors: recorded ids take hout, the sampled id outside H the
-    // float64 value alpha p_a + scale, every other element the streamed
-    // value; one thread per listed vector, one store per vector.
+    // sc_center lists its vectors as its stream meets them: their values
+    // and stores come after the stream, one thread per listed vector.
+    if (KIND == KIND_CENTER)
     for (int e = t; e < n_ent; e += B) {
       const int n = lvec[e];
       float o[N];

@@ -15,7 +15,7 @@ import sys
 # extent of each named row-kernel LDS array, in elements
 EXTENTS = {"bitmap": "(long)P.bm_wpt * B", "hkey": "P.hs", "hval": "P.hs", "headz": "P.k",
            "headp": "P.k", "headlp": "P.k", "hout": "P.k", "lval": "(long)P.ke * N",
-           "lvec": "P.ke"}
+           "lvec": "P.ke", "lslot": "(long)P.ke * N"}
 
 
 def transform(src):
