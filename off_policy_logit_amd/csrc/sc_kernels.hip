@@ -106,6 +106,7 @@ void k_row(RowParams P) {
   __shared__ uint32_t sh_status;
   __shared__ int sh_ninf;
   __shared__ int sh_am;
+  __shared__ int lbase[B];   // each thread's first list entry
 
   const uint32_t hmask = (uint32_t)P.hs - 1;
   const int hshift = P.hshift;
@@ -158,6 +159,11 @@ void k_row(RowParams P) {
                               : nullptr;
     const bool a_ok = a >= 0 && a < V;
     const bool need_stage = (KIND != KIND_CENTER) || has_out;
+  // The list slots of the recorded ids are mapped once in the stage for the
+  // kinds that write an output row; the statistics-only kind, whose one
+  // list pass resolves them by lookup, keeps its registers (it runs at four
+  // waves per SIMD on 128 VGPRs, where extra state spills).
+  constexpr bool kSlotMap = KIND != KIND_LOGPROBS;
 
     // Vector j of this thread is row vector j * B + t.  Every thread owns at
     // least Jmin vectors, so tiles of kU vectors below Jt are loaded with the
@@ -234,6 +240,8 @@ void k_row(RowParams P) {
       for (int w = 0; w < P.bm_wpt; ++w) bitmap[w * B + t] = 0u;
       for (int i = t; i < P.hs; i += B) hkey[i] = -1;
       for (int k = t; k < K; k += B) headz[k] = qnan;
+      if (kSlotMap)
+        for (int i = t; i < P.ke * N; i += B) lslot[i] = -1;
     }
     if (t == 0) { sh_flags = 0; sh_za = qnan; sh_ninf = 0; }
     __syncthreads();
@@ -264,6 +272,30 @@ void k_row(RowParams P) {
       int cnt = rem_owner ? 1 : 0;
       for (int w = 0; w < P.bm_wpt; ++w) cnt += __builtin_popcount(bitmap[w * B + t]);
       lpos = block_excl_scan<B>(cnt, redi, n_ent);
+      // The list slot of every recorded id, without a lookup per listed
+      // element later: thread tt lists its marked vectors in stream order
+      // (j ascending) from lbase[tt] on, then the partial last vector if it
+      // owns it, so the entry of vector n = j B + tt is lbase[tt] plus the
+      // marked vectors of tt below j.  Other listed elements keep -1.
+      if constexpr (kSlotMap) {
+        lbase[t] = lpos;
+        __syncthreads();
+        for (int k = t; k < K; k += B) {
+          const int32_t id = k == t ? my_id : P.head_ids[row * K + k];
+          if (id < 0 || id >= V) continue;
+          const int n = id / N;
+          const int tt = n % B;
+          int entry = lbase[tt];
+          if (n < n_full) {
+            const int j = n / B;
+            for (int w = 0; w < (j >> 5); ++w) entry += __builtin_popcount(bitmap[w * B + tt]);
+            entry += __builtin_popcount(bitmap[(j >> 5) * B + tt] & ((1u << (j & 31)) - 1u));
+          } else {
+            for (int w = 0; w < P.bm_wpt; ++w) entry += __builtin_popcount(bitmap[w * B + tt]);
+          }
+          lslot[entry * N + (id - n * N)] = (int16_t)k;
+        }
+      }
     }
 
     float m = 0.f;          // row max of raw logits
@@ -444,8 +476,7 @@ void k_row(RowParams P) {
         const int id = lvec[e] * N + (i - e * N);
         if (id >= V) continue;
         const float z = lval[i];
-        const int slot = idset_find(hkey, hval, hmask, hshift, id);
-        lslot[i] = (int16_t)slot;   // kept for the listed vectors' output values
+        const int slot = kSlotMap ? (int)lslot[i] : idset_find(hkey, hval, hmask, hshift, id);
         if (slot >= 0) {
           headz[slot] = z;
         } else {
@@ -758,7 +789,7 @@ void k_row(RowParams P) {
         const float z = lval[e * N + i];
         float val = 0.f;
         if (id < V) {
-          const int slot = idset_find(hkey, hval, hmask, hshift, id);
+          const int slot = lslot[e * N + i];
           if (slot >= 0) val = hout[slot];
           else if (id == a) val = (float)(alpha * exp2((double)z * c64 - F) + scale);
           else val = p2_value<true>(z, Q);
