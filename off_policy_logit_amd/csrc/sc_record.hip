@@ -169,14 +169,19 @@ void k_record(RecParams P) {
     // bins finds the bin.
     constexpr int kGB = 32;                      // bins per group
     auto refresh = [&]() {
-      const int cnt = (int)__atomic_load_n(&wcnt[w], __ATOMIC_RELAXED);
+      // The count once for the wave (the branches below are the wave's),
+      // after every lane's pushes of the tiles before: the wave runs in
+      // lockstep, and the barrier (no instruction) keeps the compiler from
+      // moving the read above them.
+      __builtin_amdgcn_wave_barrier();
+      const int cnt = __builtin_amdgcn_readfirstlane((int)__atomic_load_n(&wcnt[w], __ATOMIC_RELAXED));
       if (cnt > cap) return;                     // overflowed: the row takes the fallback
       int total = 0, found = -1;
       // start at the highest bin any wave has reported (this wave's max
       // included); missing a higher count only lowers the bound
       const float wm = wave_max(m_t);
       if (lane == 0) atomicMax(&sh_u[4], (unsigned)bin_of(okey(wm)));
-      const int top0 = (int)__atomic_load_n(&sh_u[4], __ATOMIC_RELAXED);
+      const int top0 = __builtin_amdgcn_readfirstlane((int)__atomic_load_n(&sh_u[4], __ATOMIC_RELAXED));
       const int gw = b_w / kGB;
       for (int g0 = top0 / kGB; g0 >= gw && found < 0; g0 -= kWave) {
         const int g = g0 - lane;
@@ -312,7 +317,8 @@ void k_record(RecParams P) {
       for (int u = 0; u < kRU; ++u) r[u] = nx[u];
       if (j0 + B * kRU < n_full) load_tile(nx, j0 + B * kRU);
       if (iter > 0 && ((iter & (iter + 1)) == 0 ||
-                       (int)__atomic_load_n(&wcnt[w], __ATOMIC_RELAXED) > cap / 2))
+                       __builtin_amdgcn_readfirstlane(
+                           (int)__atomic_load_n(&wcnt[w], __ATOMIC_RELAXED)) > cap / 2))
         refresh();                             // tiles 1, 3, 7, 15, ... or a filling buffer
       if (iter == 0 && K <= B) {
         // Initial bound: the k-th largest of the B per-thread maxima of this

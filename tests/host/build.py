@@ -34,7 +34,7 @@ def build(out_dir=None):
     out_dir = out_dir or os.path.join(ROOT, "_build", "host")
     os.makedirs(out_dir, exist_ok=True)
     units = []
-    for name in ("sc_kernels.hip", "sc_lmhead.hip"):
+    for name in ("sc_kernels.hip", "sc_lmhead.hip", "sc_record.hip"):
         dst = os.path.join(out_dir, name.replace(".hip", "_host.cpp"))
         with open(os.path.join(CSRC, name)) as f:
             text = xform.transform(f.read())

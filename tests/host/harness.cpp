@@ -9,6 +9,8 @@
 //   harness lmhead OUT N V D K CHUNK the LM-head entry points on one seeded
 //                                    problem; inputs and outputs written to OUT
 //                                    for a comparison with the oracle
+//   harness record OUT CASES SEED    seeded random shapes through sc_record;
+//                                    inputs and outputs written to OUT
 //   harness replay N V D CHUNK       sc_lmhead_backward alone (bounds only)
 //
 // Every mode ends with "HARNESS OK" when no entry point failed and no buffer
@@ -16,17 +18,13 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <numeric>
 #include <random>
 #include <string>
 
 #include "sc.h"
 #include "sc_internal.h"
-
-namespace sc {  // the recorder is not part of the emulated build
-hipError_t launch_record(RecParams, hipStream_t) { return 1; }
-size_t record_lds_bytes(int) { return 0; }
-}  // namespace sc
 
 static int failures = 0;
 
@@ -237,6 +235,63 @@ static void rows(int cases, uint64_t seed0, const char* out = nullptr) {
 }
 
 // ---------------------------------------------------------------------------
+// Rollout-side record: seeded random shapes (ties, equal rows that take the
+// exact fallback, masks, a NaN row, K past 256, strides), each case's inputs
+// and outputs written to `out` for a comparison with the oracle.
+// ---------------------------------------------------------------------------
+static void record(int cases, uint64_t seed0, const char* out) {
+  FILE* rec = fopen(out, "wb");
+  if (!rec) { ++failures; return; }
+  for (int c = 0; c < cases; ++c) {
+    std::mt19937_64 g(seed0 * 7919 + c);
+    auto U = [&](int lo, int hi) { return lo + (int)(g() % (uint64_t)(hi - lo + 1)); };
+    const int n = U(1, 4);
+    const int V = (g() % 5 == 0) ? U(1, 40) : (g() % 4 == 0 ? U(9000, 20000) : U(41, 9000));
+    const int K = std::min(V, (g() % 4 == 0) ? U(257, 1024) : U(1, 200));
+    const int dtype = g() % 2 ? SC_BF16 : SC_F32;
+    const int pad = g() % 3 == 0 ? U(1, 9) : 0;
+    const int64_t stride = V + pad;
+    const float T = (g() % 3 == 0) ? 0.7f : ((g() % 2) ? 1.3f : 1.f);
+    const int with_sampled = g() % 4 != 0;
+    const float scales[5] = {0.1f, 1.f, 3.f, 8.f, 30.f};
+    std::vector<float> zf((size_t)n * stride, 0.f);
+    std::vector<int32_t> sampled(n);
+    for (int r = 0; r < n; ++r) {
+      float* z = zf.data() + (size_t)r * stride;
+      std::normal_distribution<float> nd(U(0, 3) == 0 ? 2.f : 0.f, scales[U(0, 4)]);
+      for (int v = 0; v < V; ++v) z[v] = nd(g);
+      const int kind = U(0, 9);
+      if (kind == 0) for (int v = 0; v < V; ++v) z[v] = 0.5f;                      // all equal
+      if (kind == 1) for (int v = 0; v < V; ++v) z[v] = std::round(z[v] * 4.f) / 4.f;   // ties
+      if (kind == 2) for (int v = 0; v < V; v += 3) z[v] = -INFINITY;              // masked
+      if (kind == 3) z[U(0, V - 1)] = NAN;                                         // flagged
+      if (kind == 4) for (int v = 0; v < V; ++v) z[v] = (v % 7 == 0) ? 1.f : -1.f;  // two levels
+      sampled[r] = (int)(g() % V);
+    }
+    std::vector<uint16_t> zb(zf.size());
+    for (size_t i = 0; i < zf.size(); ++i) zb[i] = to_bf16(zf[i]);
+    const void* logits = dtype == SC_BF16 ? (const void*)zb.data() : (const void*)zf.data();
+    std::vector<int32_t> ids((size_t)n * K, -7);
+    std::vector<float> probs((size_t)n * K, -7.f), lp(n, -7.f);
+    uint32_t status = 0;
+    EXPECT(sc_record(logits, dtype, n, V, stride, T, K, with_sampled ? sampled.data() : nullptr,
+                     ids.data(), probs.data(), with_sampled ? lp.data() : nullptr, &status,
+                     nullptr), SC_OK);
+    const int32_t hdr[6] = {n, V, K, (int32_t)stride, dtype, with_sampled};
+    fwrite(hdr, 4, 6, rec);
+    fwrite(&T, 4, 1, rec);
+    fwrite(zf.data(), 4, zf.size(), rec);
+    fwrite(sampled.data(), 4, n, rec);
+    fwrite(ids.data(), 4, ids.size(), rec);
+    fwrite(probs.data(), 4, probs.size(), rec);
+    fwrite(lp.data(), 4, n, rec);
+    printf("record case %d: n=%d V=%d K=%d in=%d pad=%d T=%g sampled=%d status %u\n", c, n, V,
+           K, dtype, pad, T, with_sampled, status);
+  }
+  fclose(rec);
+}
+
+// ---------------------------------------------------------------------------
 // LM-head entry points on one seeded problem.
 // ---------------------------------------------------------------------------
 struct LmProblem {
@@ -358,6 +413,8 @@ int main(int argc, char** argv) {
     rows(atoi(argv[2]), (uint64_t)atoll(argv[3]), argc > 4 ? argv[4] : nullptr);
   } else if (mode == "lmhead" && argc > 7) {
     lmhead(argv[2], atoi(argv[3]), atoi(argv[4]), atoi(argv[5]), atoi(argv[6]), atoi(argv[7]));
+  } else if (mode == "record" && argc > 4) {
+    record(atoi(argv[3]), (uint64_t)atoll(argv[4]), argv[2]);
   } else if (mode == "replay" && argc > 5) {
     replay(atoi(argv[2]), atoi(argv[3]), atoi(argv[4]), atoi(argv[5]));
   } else {

@@ -113,6 +113,31 @@ template <class T> inline T emu_shfl(T v, int kind, int arg) {
   memcpy(&r, emu::shfl_buf[b][w][src], sizeof(T));
   return r;
 }
+// Ballot: every lane deposits its predicate, the wave meets, every lane
+// reads all 64 (lanes past a partial last wave read as false).
+inline unsigned long long __ballot(int pred) {
+  const int lane = emu::cur % 64, w = emu::cur / 64, b = emu_next_buffer();
+  emu::shfl_buf[b][w][lane][0] = pred ? 1 : 0;
+  emu::yield_wave();
+  const int wsize = emu::nthreads - w * 64 < 64 ? emu::nthreads - w * 64 : 64;
+  unsigned long long m = 0;
+  for (int l = 0; l < wsize; ++l) m |= (unsigned long long)(emu::shfl_buf[b][w][l][0] & 1) << l;
+  return m;
+}
+// Lane counts: src1 plus the bits of src0 that belong to lower lanes (the low
+// word covers lanes 0-31, the high word lanes 32-63).
+inline uint32_t emu_mbcnt_lo(uint32_t m, uint32_t acc) {
+  const int lane = emu::cur % 64;
+  const uint32_t below = lane >= 32 ? 0xffffffffu : ((1u << lane) - 1u);
+  return acc + (uint32_t)__builtin_popcount(m & below);
+}
+inline uint32_t emu_mbcnt_hi(uint32_t m, uint32_t acc) {
+  const int lane = emu::cur % 64;
+  const uint32_t below = lane < 32 ? 0u : ((1u << (lane - 32)) - 1u);
+  return acc + (uint32_t)__builtin_popcount(m & below);
+}
+#define __builtin_amdgcn_mbcnt_lo emu_mbcnt_lo
+#define __builtin_amdgcn_mbcnt_hi emu_mbcnt_hi
 template <class T> inline T __shfl_xor(T v, int m, int = 64) { return emu_shfl(v, 0, m); }
 template <class T> inline T __shfl(T v, int s, int = 64) { return emu_shfl(v, 1, s); }
 template <class T> inline T __shfl_up(T v, unsigned d, int = 64) { return emu_shfl(v, 2, (int)d); }
@@ -126,7 +151,20 @@ template <class T> inline T atomicAdd(T* p, T v) { T o = *p; *p = o + v; return 
 template <class T> inline T atomicSub(T* p, T v) { T o = *p; *p = o - v; return o; }
 
 #define __builtin_amdgcn_exp2f(x) exp2f(x)
-#define __builtin_amdgcn_readfirstlane(x) (x)
+// Lane 0's value for the whole wave (a wave collective: every lane of the
+// wave must call it).
+inline int emu_readfirstlane(int v) {
+  const int lane = emu::cur % 64, w = emu::cur / 64, b = emu_next_buffer();
+  memcpy(emu::shfl_buf[b][w][lane], &v, sizeof(int));
+  emu::yield_wave();
+  int r;
+  memcpy(&r, emu::shfl_buf[b][w][0], sizeof(int));
+  return r;
+}
+#define __builtin_amdgcn_readfirstlane(x) emu_readfirstlane(x)
+// The fibers of a wave do not run in lockstep: a wave barrier stands in for
+// it where the kernel relies on it.
+#define __builtin_amdgcn_wave_barrier() ::emu::yield_wave()
 #define __builtin_amdgcn_s_setprio(x) ((void)0)
 #define __builtin_amdgcn_iglp_opt(x) ((void)0)
 inline long long clock64() { return 0; }
@@ -137,6 +175,8 @@ inline uint32_t __float_as_uint(float f) { uint32_t u; memcpy(&u, &f, 4); return
 inline float __int_as_float(int u) { float f; memcpy(&f, &u, 4); return f; }
 inline int __float_as_int(float f) { int u; memcpy(&u, &f, 4); return u; }
 struct float4 { float x, y, z, w; };
+struct alignas(16) uint4 { unsigned int x, y, z, w; };
+struct alignas(16) ulonglong2 { unsigned long long x, y; };
 inline float4 make_float4(float a, float b, float c, float d) { return float4{a, b, c, d}; }
 
 // v_mfma_f32_32x32x16_bf16: D = C + A B^T over one wave.  Lane l holds

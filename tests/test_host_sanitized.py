@@ -8,6 +8,9 @@ buffer-resource accesses are bounds checked).
 * seeded random shapes through sc_logprobs, sc_correct and sc_center (data
   errors, -inf / NaN logits, ragged vectors, strided rows), sc_correct's
   outputs on every row compared with the oracle at the GPU tests' bar;
+* sc_record (the rollout-side top-k) on seeded random shapes, ties, equal
+  rows that take the exact fallback, masks and K past 256: ids exact,
+  probabilities and the sampled log-probability at the GPU tests' bars;
 * the LM-head entry points on one small ragged problem (two row tiles, two
   vocabulary tiles, a three-chunk backward), their outputs compared with the
   oracle: logits with the fp32 summation bound, statistics at the row
@@ -196,3 +199,62 @@ def test_lmhead_entry_points_match_oracle_under_sanitizers(harness, tmp_path):
     tol_w = 2.0 ** -8 * (np.abs(G).T @ np.abs(x)) + 1e-30
     assert np.all(np.abs(r["dh"] - rdX) <= tol_x), float(np.abs(r["dh"] - rdX).max())
     assert np.all(np.abs(r["dw"] - rdW) <= tol_w), float(np.abs(r["dw"] - rdW).max())
+
+
+def read_record(path):
+    b = open(path, "rb").read()
+    o = 0
+
+    def take(dt, n):
+        nonlocal o
+        a = np.frombuffer(b, dt, n, o)
+        o += a.nbytes
+        return a
+    cases = []
+    while o < len(b):
+        n, V, K, stride, dtype, with_sampled = (int(v) for v in take(np.int32, 6))
+        c = dict(n=n, V=V, K=K, with_sampled=bool(with_sampled), T=float(take(np.float32, 1)[0]))
+        z = take(np.float32, n * stride).reshape(n, stride)[:, :V]
+        if dtype == SC_BF16:
+            z = torch.from_numpy(z.copy()).to(torch.bfloat16).float().numpy()
+        c["z"] = z.astype(np.float64)
+        c["sampled"] = take(np.int32, n)
+        c["ids"] = take(np.int32, n * K).reshape(n, K)
+        c["probs"] = take(np.float32, n * K).reshape(n, K)
+        c["lp"] = take(np.float32, n)
+        cases.append(c)
+    return cases
+
+
+def test_record_matches_oracle_under_sanitizers(harness, tmp_path):
+    """sc_record on 24 seeded random cases in the emulated device
+    environment, every row against the oracle: ids exact, probabilities
+    within abs 1e-6 + rel 4e-6, the sampled log-probability within abs
+    1e-5 (or one fp32 spacing of it)."""
+    path = tmp_path / "record.bin"
+    out = run(harness, "record", path, 24, 5)
+    assert out.count("record case") == 24
+    cases = read_record(path)
+    assert len(cases) == 24
+    rows = flagged = big_k = 0
+    for ci, c in enumerate(cases):
+        for r in range(c["n"]):
+            a = int(c["sampled"][r]) if c["with_sampled"] else None
+            o = O.record_topk(c["z"][r], c["T"], c["K"], sampled=a)
+            tag = f"emulated record case {ci} row {r}"
+            if o["flags"]:
+                assert np.all(c["ids"][r] == -1) and np.all(np.isnan(c["probs"][r])), tag
+                flagged += 1
+                continue
+            np.testing.assert_array_equal(c["ids"][r], o["head_ids"], err_msg=tag)
+            err = np.abs(c["probs"][r] - o["head_probs"]) - (1e-6 + 4e-6 * o["head_probs"])
+            assert err.max() <= 0, (tag, float(np.abs(c["probs"][r] - o["head_probs"]).max()))
+            if a is not None:
+                tol = max(1e-5, float(np.spacing(np.float32(abs(o["sampled_logp"])))))
+                assert abs(c["lp"][r] - o["sampled_logp"]) <= tol, (tag, c["lp"][r],
+                                                                    o["sampled_logp"])
+            rows += 1
+            big_k += c["K"] > 256
+    print(f"[case] emulated record: {rows} rows checked, {flagged} flagged, "
+          f"{big_k} with K > 256", flush=True)
+    assert rows >= 30 and big_k >= 3, (rows, big_k)
