@@ -1,4 +1,4 @@
-"""The library's C ABI and its row and LM-head kernels on the CPU, under
+"""The library's C ABI and its row, LM-head and recorder kernels on the CPU, under
 AddressSanitizer and UndefinedBehaviorSanitizer (tests/host: the kernels are
 compiled for the host against an emulated device environment in which every
 GPU thread is a fiber, wave operations and barriers switch fibers, and
