@@ -100,6 +100,7 @@ void k_record(RecParams P) {
   unsigned long long* buf = reinterpret_cast<unsigned long long*>(lds + kNBins * 4) +
                             (size_t)w * cap;                               // [cap] per wave
   __shared__ float redf[4 * kRNW];
+  __shared__ double redd[kRNW];
   __shared__ int redi[kRNW];
   // 0: flags, 1: overflow, 2: sort count, 3: status, 4: highest counted bin
   __shared__ unsigned int sh_u[5];
@@ -154,6 +155,11 @@ void k_record(RecParams P) {
       above_out = sh_i[1];
     };
     // -------------------------------------------------------------- stream
+    // The sum in two levels: each tile's kRU N terms in fp32 first, then the
+    // tile sums into s_t.  A flat row gives a thread ~1,000 comparable
+    // terms; added one by one to a running fp32 sum they would lose ~1e-5 of
+    // it, ~30 tile sums lose a few 1e-7.  The workgroup adds the threads'
+    // sums in float64.
     float m_t = -FLT_MAX, s_t = 0.f;
     int b_w = 0;            // wave-uniform lower bound on the k-th key's bin
     float thr = -INFINITY;  // bin_floor(b_w)
@@ -274,12 +280,14 @@ void k_record(RecParams P) {
         const bool act = j0 + u * B + t < n_full;
         cmask |= (act && vm >= thr) ? (1u << u) : 0u;
       }
-      s_t *= exp2_fast((m_t - m_run) * c);
+      s_t *= exp2_fast((m_t - m_run) * c);   // exactly 1 unless the max rose
       m_t = m_run;
+      float ts = 0.f;   // the tile's terms (kRU N of them) in fp32 first
 #pragma unroll
       for (int u = 0; u < kRU; ++u)
 #pragma unroll
-        for (int i = 0; i < N; ++i) s_t += exp2_fast((v[u][i] - m_t) * c);
+        for (int i = 0; i < N; ++i) ts += exp2_fast((v[u][i] - m_t) * c);
+      s_t += ts;
       if (cmask) {
 #pragma unroll
         for (int u = 0; u < kRU; ++u) {
@@ -377,9 +385,9 @@ void k_record(RecParams P) {
     int dummy = 0;
     block_argmax<B>(mv, dummy, redf, redi);
     const float m = mv;
-    float part[1] = {s_t * exp2_fast((m_t - m) * c)};
-    block_sum<B, 1>(part, redf);
-    const float log2s = log2f(part[0]);
+    double part[1] = {(double)s_t * (double)exp2_fast((m_t - m) * c)};
+    block_sum<B, 1>(part, redd);
+    const float log2s = (float)log2(part[0]);
     // a NaN logit makes the sum NaN (exp2 propagates it), +inf makes the max
     // +inf, an all -inf row leaves the max at -FLT_MAX
     if (t == 0 && (!(m > -FLT_MAX) || !(m < INFINITY) || !(part[0] < INFINITY)))
@@ -515,7 +523,7 @@ void k_record(RecParams P) {
     if (t == 0) {
       // log p(a) in float64: the logit difference is exact there, and the
       // fp32 log-sum-exp of the row enters only through log2 of its sum
-      const double lpa = (((double)za - (double)m) * P.c64 - log2((double)part[0])) *
+      const double lpa = (((double)za - (double)m) * P.c64 - log2(part[0])) *
                          0.6931471805599453;
       if (P.sampled_logp) P.sampled_logp[row] = (flags || a < 0) ? qnan : (float)lpa;
       if (flags) sh_u[3] |= flags;
