@@ -21,12 +21,22 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 size_t esize(int dtype) { return dtype == SC_BF16 ? 2 : 4; }
 bool dtype_ok(int d) { return d == SC_F32 || d == SC_BF16; }
 
+// c = log2(e) / T (float64, > 0) as an fp32 pair hi + lo with hi < c, so
+// that lo > 0: the kernels form z c as fma(z, lo, fma(z, hi, -E)), and for a
+// masked logit z = -inf that is -inf only when both products are -inf (with
+// lo < 0 the inner -inf meets +inf: NaN).  Rounded to nearest, lo is negative
+// for T = 0.6 ... 0.9, for instance.
+void split_scale(double c64, float& hi, float& lo) {
+  hi = (float)c64;
+  if ((double)hi >= c64) hi = std::nextafter(hi, 0.f);
+  lo = (float)(c64 - (double)hi);
+}
+
 // log2(e) / T as fp32, as float64 and as an fp32 pair (hi + lo).
 void set_lm_temperature(sc::LmParams& P, float temperature) {
   P.c64 = 1.4426950408889634 / (double)temperature;
   P.c = (float)P.c64;
-  P.c_hi = P.c;
-  P.c_lo = (float)(P.c64 - (double)P.c_hi);
+  split_scale(P.c64, P.c_hi, P.c_lo);
 }
 
 // Shared row-kernel argument checks; fills the geometry part of RowParams.
@@ -56,8 +66,7 @@ int check_rows(sc::RowParams& P, const void* logits, bool logits_needed, int log
   P.sampled = sampled;
   P.temperature = temperature;
   P.c64 = 1.4426950408889634 / (double)temperature;
-  P.c_hi = (float)P.c64;
-  P.c_lo = (float)(P.c64 - (double)P.c_hi);
+  split_scale(P.c64, P.c_hi, P.c_lo);
   P.row_stats = row_stats;
   P.row_idx = row_idx;
   return SC_OK;

@@ -18,7 +18,7 @@ namespace sc {
 #define SC_STATS_TILE 4
 #endif
 #ifndef SC_STATS_WAVES
-#define SC_STATS_WAVES 4
+#define SC_STATS_WAVES 3
 #endif
 #ifndef SC_CENTER_BLOCK
 #define SC_CENTER_BLOCK 256

@@ -159,11 +159,6 @@ void k_row(RowParams P) {
                               : nullptr;
     const bool a_ok = a >= 0 && a < V;
     const bool need_stage = (KIND != KIND_CENTER) || has_out;
-  // The list slots of the recorded ids are mapped once in the stage for the
-  // kinds that write an output row; the statistics-only kind, whose one
-  // list pass resolves them by lookup, keeps its registers (it runs at four
-  // waves per SIMD on 128 VGPRs, where extra state spills).
-  constexpr bool kSlotMap = KIND != KIND_LOGPROBS;
 
     // Vector j of this thread is row vector j * B + t.  Every thread owns at
     // least Jmin vectors, so tiles of kU vectors below Jt are loaded with the
@@ -240,8 +235,7 @@ void k_row(RowParams P) {
       for (int w = 0; w < P.bm_wpt; ++w) bitmap[w * B + t] = 0u;
       for (int i = t; i < P.hs; i += B) hkey[i] = -1;
       for (int k = t; k < K; k += B) headz[k] = qnan;
-      if (kSlotMap)
-        for (int i = t; i < P.ke * N; i += B) lslot[i] = -1;
+      for (int i = t; i < P.ke * N; i += B) lslot[i] = -1;
     }
     if (t == 0) { sh_flags = 0; sh_za = qnan; sh_ninf = 0; }
     __syncthreads();
@@ -277,7 +271,7 @@ void k_row(RowParams P) {
       // (j ascending) from lbase[tt] on, then the partial last vector if it
       // owns it, so the entry of vector n = j B + tt is lbase[tt] plus the
       // marked vectors of tt below j.  Other listed elements keep -1.
-      if constexpr (kSlotMap) {
+      {
         lbase[t] = lpos;
         __syncthreads();
         for (int k = t; k < K; k += B) {
@@ -306,18 +300,18 @@ void k_row(RowParams P) {
 
     if (KIND != KIND_CENTER) {
       // ---------------------------------------------------------- pass 1
-      // m_t: running max of every vector (argmax; starts at -FLT_MAX so that
-      // all -inf vectors never count); am_vec: the thread's vector that last
-      // raised it (strictly, so the first of equal maxima is kept).
-      // E_t = ref_exp(m_t): the exponent reference of s_t = sum 2^(z c - E_t)
-      // (float64) and of h_t = sum 2^(z c - E_t) (z c - E_t) over unmarked
-      // vectors.  When E_t rises by D, s_t scales by 2^-D and h_t by 2^-D
-      // after subtracting D s_t, both exactly.
+      // m_t: running max of the unmarked vectors (argmax; starts at -FLT_MAX
+      // so that all -inf vectors never count; the marked vectors' elements
+      // are compared in the finalize, from the list); am_vec: the thread's
+      // vector that last raised it (strictly, so the first of equal maxima is
+      // kept).  E_t = ref_exp(m_t): the exponent reference of
+      // s_t = sum 2^(z c - E_t) (float64) and of h_t = sum 2^(z c - E_t)
+      // (z c - E_t) over unmarked vectors.  When E_t rises by D, s_t scales by
+      // 2^-D and h_t by 2^-D after subtracting D s_t, both exactly.
       float m_t = -FLT_MAX, E_t = ref_exp(-FLT_MAX, c_hi);
       double s_t = 0.0;
       float h_t = 0.f;
       int am_vec = -1;
-      int am_direct = -1;
       auto rebase = [&](float E_new) {
         const float D = E_new - E_t;                 // >= 0
         const int kd = (int)fminf(D, 2048.f);
@@ -344,20 +338,27 @@ void k_row(RowParams P) {
           for (int i = 0; i + w < N; i += 2 * w) e[i] += e[i + w];
         acc = e[0];
       };
-      // One vector's maximum, its argmax bookkeeping and, when marked, its
-      // capture to the list.
+      // An unmarked vector's maximum and its argmax bookkeeping; a marked
+      // vector is captured to the list instead (its maximum is taken there).
       auto scan_vec = [&](const float (&v)[N], int j, bool marked, float& m_run) {
         float vm = v[0];
 #pragma unroll
         for (int i = 1; i < N; ++i) vm = fmaxf(vm, v[i]);
-        am_vec = vm > m_run ? j : am_vec;          // strictly: first of equal maxima
-        m_run = fmaxf(m_run, vm);
+        const float vu = marked ? -FLT_MAX : vm;
+        am_vec = vu > m_run ? j : am_vec;          // strictly: first of equal maxima
+        m_run = fmaxf(m_run, vu);
         if (marked) capture(j * B + t, v);
       };
       // Branch-free sums: marked vectors are summed too and the sum is
       // dropped (they are resolved element by element after the stream).
       // The maximum is raised once per group of kG vectors, so one rebase
       // serves kG vectors, and each group's sums are added in fp32 first.
+      // The exponent reference follows the largest unmarked logit, not the
+      // row maximum: where the maximum is a recorded id, the tail's largest
+      // terms, which make up tau, then have exponents near 0, and rounding
+      // each exponent to fp32 (relative 2^-24 of its size) costs them little.
+      // A marked vector above the reference may overflow its dropped sum;
+      // the selects keep that out.
       constexpr int kG = kU >= 4 ? 4 : kU;
       auto process = [&](const Raw (&r)[kU], int j0) {
         const uint32_t bits = tile_bits(j0);
@@ -422,32 +423,40 @@ void k_row(RowParams P) {
         }
         h_t = hh;
       }
-      // The partial last vector (vocab not a multiple of N) counts for the
-      // maximum here and goes to the list; its sums are taken with the list.
-      if (rem_owner) {
-        capture_partial();
-        for (int i = 0; i < rem; ++i) {
-          const float z = lval[(lpos - 1) * N + i];
-          if (z > m_t) { m_t = z; am_direct = n_full * N + i; }
-        }
+      // The partial last vector (vocab not a multiple of N) goes to the
+      // list: its maximum and its sums are taken with the list.
+      if (rem_owner) capture_partial();
+      // Argmax candidates, keyed by element index.  The stream's: the first
+      // element of the unmarked vector that holds the thread's maximum
+      // (vectors do not overlap, so among the threads holding the row maximum
+      // the lowest key is the vector of the row's first maximum; its owner
+      // finds the element below).  The list's: each listed element by its own
+      // index, the lower index first among equal values.
+      const int am_key = am_vec >= 0 ? (am_vec * B + t) * N : 0x7fffffff;
+      __syncthreads();   // every list entry is written
+      float lm = -FLT_MAX;
+      int lk = 0x7fffffff;
+      for (int i = t; i < n_ent * N; i += B) {
+        const int e = i / N;
+        const int id = lvec[e] * N + (i - e * N);
+        const float z = lval[i];
+        if (id < V && (z > lm || (z == lm && id < lk))) { lm = z; lk = id; }
       }
-      // Argmax key: the first element index of the vector that holds the
-      // thread's maximum (for the partial vector, the element itself).
-      // Vectors do not overlap, so among the threads holding the row maximum
-      // the lowest key is the vector of the row's first maximum.
-      int am_key = 0x7fffffff;
-      if (am_direct >= 0) am_key = am_direct;
-      else if (am_vec >= 0) am_key = (am_vec * B + t) * N;
+      const bool from_list = lm > m_t || (lm == m_t && lk < am_key);
 
       // ---------------------------------------------------------- finalize
-      float mv = m_t;
-      int mi = am_key;
+      float mv = from_list ? lm : m_t;
+      const int my_key = from_list ? lk : am_key;
+      int mi = my_key;
       block_argmax<B>(mv, mi, redf, redi);
       m = mv;
       argmax = mi;
-      // Only the thread owning that vector reads it again, to find the
-      // element (one load per workgroup, awaited after the list below).
-      const bool am_owner = mi < n_full * N && am_key == mi;
+      // Only the thread whose candidate won writes the row's argmax: a
+      // listed element as it is, a streamed vector after reading it again to
+      // find the element (one load per workgroup, awaited after the list
+      // below).
+      const bool am_owner = !from_list && mi < n_full * N && my_key == mi;
+      const bool am_listed = from_list && my_key == mi;
       Raw am_raw = IO::ninf();
       if (am_owner) am_raw = ld(am_vec, std::false_type{});
       E_row = ref_exp(m, c_hi);
@@ -458,35 +467,27 @@ void k_row(RowParams P) {
       const int kd = (int)fmin(Dd, 2048.0);
       double s_tail = ldexp(s_t, -kd);
       double h_sum = ldexp((double)h_t - Dd * s_t, -kd);
-      // Tail members of the list: 2^((z - m) c - G1), G1 = E_row - m c, by the
-      // exact fp32 exponent of pass 2 (relative error ~1e-7 per term).
-      Pass2 Q1;
-      {
-        const double G1 = fmin(fmax((double)E_row - (double)m * c64, -2.0), 2.0);
-        const double gi = ceil(G1);
-        const double gq = ceil((G1 - gi) * 16384.0) / 16384.0;
-        Q1.m = m; Q1.c_hi = c_hi; Q1.c_lo = c_lo;
-        Q1.gq = (float)gq;
-        Q1.nglo = (float)(-((G1 - gi) - gq) * kLn2d);
-        Q1.scl = ldexpf(1.f, -(int)gi);
-        Q1.scl_lo = ldexpf(1.f, -(int)gi - 64);
-      }
+      // Tail members of the list (the marked vectors' other elements):
+      // 2^(z c - E_row) in float64.  They are few (at most (K + 2) N per row)
+      // and can carry much of the tail mass where the recorded ids cluster,
+      // so they are formed to float64 accuracy.
       for (int i = t; i < n_ent * N; i += B) {
         const int e = i / N;
         const int id = lvec[e] * N + (i - e * N);
         if (id >= V) continue;
         const float z = lval[i];
-        const int slot = kSlotMap ? (int)lslot[i] : idset_find(hkey, hval, hmask, hshift, id);
+        const int slot = lslot[i];
         if (slot >= 0) {
           headz[slot] = z;
         } else {
-          const float ez = p2_value<true>(z, Q1);
-          const float y = fmaf(z, c_lo, fmaf(z, c_hi, -E_row));
-          s_tail += (double)ez;
-          h_sum += ez > 0.f ? (double)(ez * y) : 0.0;
+          const double y = (double)z * c64 - (double)E_row;
+          const double ez = exp2(y);
+          s_tail += ez;
+          h_sum += ez > 0.0 ? ez * y : 0.0;
         }
         if (id == a) sh_za = z;
       }
+      if (am_listed) sh_am = mi;
       if (am_owner) {   // the first element equal to the row maximum
         int i0 = 0;
 #pragma unroll
@@ -533,16 +534,31 @@ void k_row(RowParams P) {
       // sc_center: pass-1 results come from memory (the log-sum-exp as its
       // fp32 value plus the fp32 remainder in column C_LSE_LO); the row max
       // is read back at the recorded argmax when the row is streamed again.
+      // With the logits at hand, log p and p at H and log p(a) are formed in
+      // float64 from the logits and that log-sum-exp, as in the fused
+      // kernel: rho p_k reaches 1e5 and more where the tail mass is clamped,
+      // and p_k from its stored fp32 log would carry |log p_k| 2^-24 of
+      // relative error into c_k.  Without the logits the stored logs serve.
       lse = (double)stats[C_LSE] + (double)stats[C_LSE_LO];
-      logp_a = stats[C_LOGP_A];
+      const double F = lse * kLog2ed;
+      const bool zin = P.logits != nullptr;
+      logp_a = (zin && a >= 0 && a < V) ? ((double)load_elem(zrow, a) * c64 - F) * kLn2d
+                                        : (double)stats[C_LOGP_A];
       tau = stats[C_TAIL];
       a_slot = ridx[1];
       argmax = ridx[0];
       double ph = 0.0;
       for (int k = t; k < K; k += B) {
-        const float lp = P.head_logp[row * K + k];
-        headlp[k] = lp;
-        headp[k] = expf(lp);   // p_k from its stored fp32 log
+        const int32_t id = P.head_ids[row * K + k];
+        if (zin && id >= 0 && id < V) {
+          const double y = (double)load_elem(zrow, id) * c64 - F;
+          headlp[k] = y * kLn2d;
+          headp[k] = exp2(y);
+        } else {
+          const double lp = P.head_logp[row * K + k];
+          headlp[k] = lp;
+          headp[k] = exp(lp);    // p_k from its stored fp32 log, in float64
+        }
         ph += headp[k];
       }
       double sums[1] = {ph};

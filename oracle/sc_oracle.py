@@ -261,6 +261,62 @@ def sc_row(z, temperature, head_ids, head_probs, sampled, rollout_logp=None,
                 entropy=entropy, w=w, weight=weight, rev_kl=rev_kl, row=row)
 
 
+def sc_center_row(logp_a, tau, head_logp, head_probs, rollout_logp=None,
+                  advantage=1.0, is_mode=IS_NONE, is_lo=0.5, is_hi=None,
+                  centering=True):
+    """The centering step of one valid row from the statistics it is handed,
+    in float64: what a second call computes when it has the first call's
+    log p(a), tail mass tau and log p at H but not the logits.
+
+    Same definitions as sc_row (Score Centering page, section "Score
+    Centering": rho with both 1e-6 clamps, c = q - rho p on H, the token loss;
+    the tail of mu_hat is rho p), with every sum over the tail taken in closed
+    form from tau: S = Q_H + rho tau, the tail's share of TV is
+    |rho - 1| tau / 2, of KL(mu_hat || p) rho tau log rho and of KL(p ||
+    mu_hat) -tau log rho.  p at H is exp(head_logp).
+
+    Returns dict(P_H, Q_H, rho, S, coef, loss, tv, kl, rev_kl, k3, w, weight).
+    """
+    lp = np.asarray(head_logp, dtype=np.float64)
+    q = np.asarray(head_probs, dtype=np.float64)
+    logp_a = float(logp_a)
+    tau = float(tau)
+    p_H = np.exp(lp)
+    P_H = float(np.sum(p_H))
+    Q_H = float(np.sum(q))
+    rho = max(1.0 - Q_H, CLAMP) / max(tau, CLAMP)
+
+    if rollout_logp is None:
+        if is_mode != IS_NONE:
+            raise ValueError("importance weighting needs rollout_logp")
+        w = float("nan")
+        k3 = float("nan")
+    else:
+        d = logp_a - float(rollout_logp)
+        w = math.exp(d)
+        k3 = math.expm1(d) - d
+    if is_hi is None:
+        is_hi = 5.0 if is_mode == IS_MIS else 2.0
+    weight = is_weight(w, is_mode, is_lo, is_hi)
+
+    coef = q - rho * p_H
+    centered = float(np.sum(coef * lp)) if centering else 0.0
+    loss = -float(advantage) * weight * (logp_a - centered)
+    S = Q_H + rho * tau
+
+    log_rho = math.log(rho)
+    tv = 0.5 * (float(np.sum(np.abs(q - p_H))) + abs(rho - 1.0) * tau)
+    qpos = q > 0
+    kl = float(np.sum(q[qpos] * (np.log(q[qpos]) - lp[qpos]))) + rho * tau * log_rho
+    ppos = p_H > 0
+    if np.any(ppos & ~qpos):
+        rev_kl = float("inf")
+    else:
+        rev_kl = float(np.sum(p_H[ppos] * (lp[ppos] - np.log(q[ppos])))) - tau * log_rho
+    return dict(P_H=P_H, Q_H=Q_H, rho=rho, S=S, coef=coef, loss=loss, tv=tv,
+                kl=kl, rev_kl=rev_kl, k3=k3, w=w, weight=weight)
+
+
 def masked_row(V, K):
     """Outputs of a padding row: nothing read, zero loss and gradient."""
     return dict(flags=0, lse=0.0, logp_a=0.0, argmax=-1, a_slot=-1,

@@ -7,10 +7,12 @@ oracle, per row):
 * log-probabilities (lse, log p(a), log p at H): abs 1e-5.
 * masses tau, P_H, Q_H, S and TV: abs 1e-6.
 * rho: rel 1e-5.
-* c_k = q_k - rho p_k: abs 1e-6.
+* c_k = q_k - rho p_k: abs 1e-6, plus p_k times an error of rho of 2^-21
+  relative (RHO_REL, below).
 * K3: abs 1e-6.
 * KL(mu_hat || p): abs 1e-6 + rel 1e-5.
-* loss per row: abs 1e-4.
+* loss per row: abs 1e-4, plus |A wt| sum_k p_k |log p_k| times the same
+  error of rho (the centering sum of c_k log p_k).
 * full-vocabulary rows in fp32 (the score g, the correction mu_hat - p, or
   dLogits = -A wt / (T N_valid) g): abs 1e-6 per entry, scaled by the factor
   in front of g (|A wt| / (T N_valid) for dLogits, |wt| for the score).
@@ -21,13 +23,34 @@ oracle, per row):
   are [k = a] - q_k - (1 - S) p_k (or q_k - p_k), and where q_k equals p_k to
   within 1e-15 that difference cancels to the size of the float64 rounding
   of S, a 128-term sum, in the oracle as in the kernel (~1e-16), so no
-  implementation fixes its bits.
+  implementation fixes its bits.  The floor is |scale| |lse| 2^-47 where that
+  is larger: the two-call path hands lse over as an fp32 pair (48 bits), so
+  each p_v it forms carries |lse| 2^-48 of relative error, and where the
+  sampled entry 1 - p_a cancels to (nearly) zero, as in a one-id vocabulary or
+  a row whose p_a is within 1e-13 of 1, that error is what is left.  And it
+  adds |scale| p_v 2^-22 per entry where the row's p is at hand: p_v =
+  2^(z c - E) / s with s the row's sum of V exponentials evaluated in fp32,
+  whose relative error is a few 2^-24, so an entry carries that times p_v; it
+  is far below one bf16 step of any entry that does not cancel, and decides
+  only entries such as a recorded q_k within ~1e-7 of p_k.
 
 Every output is an fp32 number, whose own spacing exceeds an absolute bound
 once the value is large (2^-23 |x| > 1e-6 for |x| >= 16): an absolute
 tolerance is therefore read as "abs tol, or one fp32 spacing of the exact
 value where that is larger" (``f32_tol``); below |x| = 8 this is the
-absolute tolerance itself.
+absolute tolerance itself.  For the log-probabilities (abs 1e-5) the spacing
+takes over at |x| >= 128, e.g. log p of a recorded id far below the row
+maximum at a low temperature.
+
+rho = (1 - Q_H) / tau is ill-conditioned where tau is small under a large
+leftover mass 1 - Q_H (the stated bar itself checks rho relative to 1e-5 only
+while min(1 - Q_H, tau) >= 1e-4).  tau is a sum of exponentials evaluated in
+fp32, each term within about two fp32 units of its value and the partial sums
+in fp32, and the two-call path hands it over as an fp32 number: its relative
+error is a few 2^-24, and rho carries it.  Where rho p_k is large, c_k and the
+loss carry that error times rho p_k, beyond what abs 1e-6 and abs 1e-4 allow;
+their bars add it at RHO_REL = 2^-21.  Where rho p_k <= 2 (every row whose
+tail is not far smaller than 1 - Q_H) the added term is below 1e-6.
 
 Extra signals, beyond the stated bar: entropy abs 1e-5 + rel 1e-6; the
 importance ratio w and the weight rel 1e-6, or one fp32 spacing of the value
@@ -49,6 +72,7 @@ from oracle import sc_oracle as O
 STAT_COLS = dict(lse=0, logp_a=1, tau=2, P_H=3, Q_H=4, rho=5, S=6, loss=7,
                  tv=8, kl=9, k3=10, entropy=11, w=12, weight=13, rev_kl=14)
 REL_W = 1e-6
+RHO_REL = 2.0 ** -21
 MIN_BF16_EQUAL = 0.9999
 
 # Largest error seen per quantity, in units of its tolerance (printed by the
@@ -135,7 +159,7 @@ def _gpu_weight(o, got_w, is_mode, is_lo, is_hi):
 def check_row(tag, g, o, A=1.0, T=1.0, n_valid=1, mode=O.MODE_DLOGITS,
               row_dtype=None, bf16_stats=None, stats_only=False, rlp=None,
               is_mode=O.IS_NONE, is_lo=0.5, is_hi=2.0, centering=True,
-              rerun=None):
+              rerun=None, p_row=None):
     """Assert one row's GPU outputs against the oracle dict ``o``.
 
     g: dict with numpy arrays: stats [16], idx [2], head_logp [K] and, unless
@@ -143,7 +167,9 @@ def check_row(tag, g, o, A=1.0, T=1.0, n_valid=1, mode=O.MODE_DLOGITS,
     bits).  bf16_stats: list collecting (max_dist, equal_fraction, entries).
     The weighting arguments are the ones the oracle row was computed with;
     rerun(**overrides) recomputes the oracle row with other weighting
-    arguments (needed only for a masked-IS decision at a boundary).
+    arguments (needed only for a masked-IS decision at a boundary).  p_row:
+    the row's trainer probabilities (float64), for the bf16 floor of entries
+    that cancel (see the module docstring).
     """
     st = g["stats"]
     if o["flags"]:
@@ -162,18 +188,20 @@ def check_row(tag, g, o, A=1.0, T=1.0, n_valid=1, mode=O.MODE_DLOGITS,
             WORST[name] = max(WORST.get(name, 0.0), ratio)
         assert np.all(err <= tol), (tag, name, float(np.max(err)), ratio)
 
-    close("lse", st[0], o["lse"], 1e-5)
-    close("logp_a", st[1], o["logp_a"], 1e-5)
+    close("lse", st[0], o["lse"], f32_tol(o["lse"], 1e-5))
+    close("logp_a", st[1], o["logp_a"], f32_tol(o["logp_a"], 1e-5))
     close("tau", st[2], o["tau"], 1e-6)
     close("P_H", st[3], o["P_H"], 1e-6)
-    close("head_logp", g["head_logp"], o["head_logp"], 1e-5)
+    close("head_logp", g["head_logp"], o["head_logp"], f32_tol(o["head_logp"], 1e-5))
     close("entropy", st[11], o["entropy"], 1e-5 + 1e-6 * abs(o["entropy"]))
     if stats_only:
         return
     close("Q_H", st[4], o["Q_H"], 1e-6)
     close("rho", st[5], o["rho"], 1e-5 * abs(o["rho"]))
     close("S", st[6], o["S"], 1e-6)
-    close("coef", g["coef"], o["coef"], f32_tol(o["coef"], 1e-6))
+    p_h = np.exp(np.asarray(o["head_logp"], np.float64))
+    close("coef", g["coef"], o["coef"],
+          f32_tol(o["coef"], 1e-6) + RHO_REL * np.abs(o["rho"] * p_h))
     if rlp is not None:
         close("w", st[12], o["w"], f32_rel(o["w"], REL_W))
     wt, boundary = _gpu_weight(o, st[12], is_mode, is_lo, is_hi)
@@ -181,7 +209,9 @@ def check_row(tag, g, o, A=1.0, T=1.0, n_valid=1, mode=O.MODE_DLOGITS,
     close("weight", st[13], wt, f32_rel(wt, rel_wt) if rel_wt else 0.0)
     bracket = o["logp_a"] - (float(np.sum(o["coef"] * o["head_logp"])) if centering else 0.0)
     loss = -A * wt * bracket
-    close("loss", st[7], loss, f32_tol(loss, 1e-4))
+    rho_loss = (abs(A * wt) * RHO_REL * abs(o["rho"]) *
+                float(np.sum(p_h * np.abs(o["head_logp"]))) if centering else 0.0)
+    close("loss", st[7], loss, f32_tol(loss, 1e-4) + rho_loss)
     close("tv", st[8], o["tv"], 1e-6)
     close("kl", st[9], o["kl"], 1e-6 + 1e-5 * abs(o["kl"]))
     if math.isinf(o["rev_kl"]):
@@ -208,7 +238,10 @@ def check_row(tag, g, o, A=1.0, T=1.0, n_valid=1, mode=O.MODE_DLOGITS,
     if row_dtype == "f32":
         close("row", g["row"], ref_row, f32_tol(ref_row, 1e-6 * scale))
     else:
-        dist, eq = compare_bf16(g["row"], ref_row, floor=2.0 ** -45 * scale)
+        floor = scale * max(2.0 ** -45, abs(float(o["lse"])) * 2.0 ** -47)
+        if p_row is not None:
+            floor = floor + scale * 2.0 ** -22 * p_row
+        dist, eq = compare_bf16(g["row"], ref_row, floor=floor)
         assert dist <= 1, (tag, "bf16 row step distance", dist)
         if bf16_stats is not None:
             bf16_stats.append((dist, eq, ref_row.size))

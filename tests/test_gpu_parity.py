@@ -117,9 +117,11 @@ def check_rows(tag, d, out, rows, adv_h, n_valid, T, mode, out_dtype,
                             **dict(weighting, **over))
         o = rerun()
         st = []
+        p_row = (np.exp(z[j].astype(np.float64) / T - o["lse"])
+                 if out_dtype == "bf16" else None)
         check_row(f"{tag} row {r}", gj, o, A=A, T=T, n_valid=n_valid, mode=mode,
                   row_dtype=out_dtype, bf16_stats=st, rlp=rlp[j], rerun=rerun,
-                  **weighting)
+                  p_row=p_row, **weighting)
         o.pop("row")
         return int(r), o, st
 
@@ -682,13 +684,74 @@ def test_clamp_corners(kind, dtype):
     bf16_bar(stats, f"clamp corner {kind} {dtype}")
 
 
+@pytest.mark.parametrize("kind", ["tiny_tau", "q_ge_1"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_masked_vocabulary_rows(dtype):
+def test_clamp_corners_two_call(kind, dtype):
+    """Both clamp corners through sc_logprobs, then sc_center.  With the
+    logits, the second call forms p and log p at H in float64 from them, and
+    every output (and the fp32 dLogits row) matches the oracle on the logits.
+    Without them (the path after the fused LM-head), its inputs are the
+    first call's fp32 log p(a), tail mass and log p at H: those are checked
+    against the oracle on the logits, and the centering outputs against the
+    oracle's centering from exactly those inputs (sc_center_row), at the same
+    bars.  Where rho p_k reaches 1e5 the fp32 logs alone move c_k by many fp32
+    steps, so the two are told apart."""
+    n, V, K = 32, 4099, 64
+    d, z = clamp_corner_rows(kind, n, V, K, seed=73 if kind == "tiny_tau" else 74, dtype=dtype)
+    adv = torch.linspace(-1.0, 1.0, n // 4, device=DEV)
+    adv_h = adv.cpu().numpy()
+    n_valid = sc.count_valid(d["resp_idx"])
+    status = [torch.zeros(1, dtype=torch.int32, device=DEV) for _ in range(3)]
+    st = sc.logprobs(d["logits"], d["head_ids"], d["sampled"], d["resp_idx"],
+                     dev_status=status[0])
+    args = (d["head_ids"], d["head_probs"], d["sampled"], d["resp_idx"], adv)
+    with_z = {k: v.clone() for k, v in st.items()}
+    row_out = torch.empty(n, V, device=DEV)
+    sc.center(with_z, *args, n_valid=n_valid, rollout_logp=d["rollout_logp"],
+              logits=d["logits"], row_out=row_out, row_mode=O.MODE_DLOGITS,
+              dev_status=status[1])
+    with_z["row"] = row_out
+    no_z = {k: v.clone() for k, v in st.items()}
+    sc.center(no_z, *args, n_valid=n_valid, rollout_logp=d["rollout_logp"], vocab=V,
+              dev_status=status[2])
+    torch.cuda.synchronize()
+    assert [int(s.item()) for s in status] == [0, 0, 0]
+    say(f"two-call clamp corner {kind} {dtype}, with the logits")
+    found = check_rows(f"two-call clamp {kind} {dtype} with logits", d, with_z, np.arange(n),
+                       adv_h, n, 1.0, O.MODE_DLOGITS, "f32", logits_h=z)
+    assert len(found) == n
+    if kind == "tiny_tau":
+        assert all(o["tau"] < 1e-6 and o["rho"] > 1e4 for o in found.values())
+    say(f"two-call clamp corner {kind} {dtype}, without the logits")
+    g = gather(no_z, np.arange(n), None)
+    q = host_rows(d["head_probs"], np.arange(n))
+    rlp = host_rows(d["rollout_logp"], np.arange(n))
+    resp = host_rows(d["resp_idx"], np.arange(n))
+    for r in range(n):
+        o = found[r]
+        gr = {key: val[r] for key, val in g.items()}
+        check_row(f"two-call clamp {kind} {dtype} first call row {r}", gr, o, stats_only=True)
+        A = float(adv_h[resp[r]])
+        lp = gr["head_logp"].astype(np.float64)
+        c = O.sc_center_row(float(gr["stats"][1]), float(gr["stats"][2]), lp, q[r],
+                            rollout_logp=float(rlp[r]), advantage=A)
+        handed = dict(o, logp_a=float(gr["stats"][1]), head_logp=lp, **c)
+        check_row(f"two-call clamp {kind} {dtype} centering row {r}", gr, handed, A=A,
+                  T=1.0, n_valid=n, rlp=rlp[r])
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_masked_vocabulary_rows(dtype, T):
     """Rows with a masked (-inf) share of the vocabulary: the statistics
     stream drops those terms from the entropy sum through its recompute path
-    (every thread of these rows meets a -inf)."""
+    (every thread of these rows meets a -inf).  Fused, statistics-only and
+    two-call paths, every row against the oracle.  At T = 0.7, log2(e)/T
+    rounded to the nearest fp32 leaves a negative remainder, so these rows
+    also test how the library splits that scale into an fp32 pair: a -inf
+    logit times the pair must stay -inf in every exponent."""
     n, V, K = 24, 50_000, 64
-    say(f"masked-vocabulary rows n={n} V={V} K={K} {dtype}")
+    say(f"masked-vocabulary rows n={n} V={V} K={K} {dtype} T={T}")
     d, z = crafted(n, V, K, seed=9, dtype=dtype)
     rng = np.random.default_rng(10)
     ids = d["head_ids"].cpu().numpy()
@@ -703,17 +766,31 @@ def test_masked_vocabulary_rows(dtype):
     d["logits"] = logits.to(torch.bfloat16) if dtype == "bf16" else logits
     adv = torch.linspace(-1.0, 1.0, 6, device=DEV)
     n_valid = sc.count_valid(d["resp_idx"])
-    out = run_correct(d, adv, n_valid, 1.0, O.MODE_DLOGITS, "bf16")
-    st = sc.logprobs(d["logits"], d["head_ids"], d["sampled"], d["resp_idx"])
+    out = run_correct(d, adv, n_valid, T, O.MODE_DLOGITS, "bf16")
+    s1 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    st = sc.logprobs(d["logits"], d["head_ids"], d["sampled"], d["resp_idx"], temperature=T,
+                     dev_status=s1)
     torch.cuda.synchronize()
-    assert int(out["status"].item()) == 0
-    check_rows(f"masked {dtype}", d, out, np.arange(n), adv.cpu().numpy(), n, 1.0,
+    assert int(out["status"].item()) == 0 and int(s1.item()) == 0
+    check_rows(f"masked {dtype} T={T}", d, out, np.arange(n), adv.cpu().numpy(), n, T,
                O.MODE_DLOGITS, "bf16", logits_h=z)
-    ent = st["row_stats"][:, sc.STAT["entropy"]].cpu().numpy()
+    Tf = float(np.float32(T))
     for r in range(n):
-        o = O.sc_row(z[r].astype(np.float64), 1.0, ids[r], d["head_probs"][r].cpu().numpy(),
+        o = O.sc_row(z[r].astype(np.float64), Tf, ids[r], d["head_probs"][r].cpu().numpy(),
                      a[r])
-        assert abs(ent[r] - o["entropy"]) <= 1e-5 + 1e-5 * abs(o["entropy"]), (r, ent[r])
+        g = dict(stats=st["row_stats"][r].cpu().numpy(), idx=st["row_idx"][r].cpu().numpy(),
+                 head_logp=st["head_logp"][r].cpu().numpy())
+        check_row(f"masked logprobs {dtype} T={T} row {r}", g, o, stats_only=True)
+    row_out = torch.empty(n, V, device=DEV)
+    s2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    sc.center(st, d["head_ids"], d["head_probs"], d["sampled"], d["resp_idx"], adv,
+              temperature=T, n_valid=n_valid, rollout_logp=d["rollout_logp"],
+              logits=d["logits"], row_out=row_out, row_mode=O.MODE_DLOGITS, dev_status=s2)
+    st["row"] = row_out
+    torch.cuda.synchronize()
+    assert int(s2.item()) == 0
+    check_rows(f"masked two-call {dtype} T={T}", d, st, np.arange(n), adv.cpu().numpy(), n, T,
+               O.MODE_DLOGITS, "f32", logits_h=z)
 
 
 @pytest.mark.parametrize("dtype,K,T", [("f32", 128, 1.0), ("bf16", 1024, 0.6)])

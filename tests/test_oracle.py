@@ -521,6 +521,50 @@ def test_reverse_kl_closed_form_and_special_cases():
 # --------------------------------------------------------------------------
 # bf16 round-to-nearest-even
 # --------------------------------------------------------------------------
+def test_center_from_statistics_matches_the_full_row():
+    """sc_center_row, fed the log p(a), tau and log p at H of a row, gives
+    every centering output of sc_row on that row: the closed-form tail sums
+    (S, TV, both KL directions) against sc_row's sums over the whole
+    vocabulary, at the clamp corners, with masks, every weighting and
+    centering off."""
+    rng = np.random.default_rng(123)
+    cases = 0
+    for case in range(48):
+        V, K = 300, 40
+        z = rng.normal(0, 2, V)
+        ids = rng.choice(V, K, replace=False)
+        kind = case % 6
+        if kind == 1:
+            z[ids] += 20.0                                   # tau < 1e-6
+        if kind == 3:
+            mask = rng.random(V) < 0.3
+            mask[ids] = False
+            z[mask] = -np.inf
+        q = rng.dirichlet(np.ones(K)) * (rng.uniform(0.3, 0.95) if kind != 2 else 1.0 + 2.0 ** -20)
+        if kind == 4:
+            q[3] = 0.0                                       # reverse KL infinite
+        a = int(ids[5]) if case % 2 else int(rng.integers(0, V))
+        while a != ids[5] and np.isneginf(z[a]):
+            a = int(rng.integers(0, V))
+        rlp = float(np.log(rng.uniform(0.05, 1.0)))
+        wkw = [dict(), dict(is_mode=O.IS_TIS, is_hi=1.5), dict(is_mode=O.IS_MIS, is_lo=0.5, is_hi=3.0),
+               dict(centering=False)][case % 4]
+        T = (1.0, 0.7, 1.3)[case % 3]
+        o = O.sc_row(z, T, ids, q, a, rollout_logp=rlp, advantage=-0.8, **wkw)
+        c = O.sc_center_row(o["logp_a"], o["tau"], o["head_logp"], q, rollout_logp=rlp,
+                            advantage=-0.8, **wkw)
+        if kind == 1:
+            assert o["tau"] < 1e-6 and o["rho"] > 1e4
+        for key in ("P_H", "Q_H", "rho", "S", "coef", "loss", "tv", "kl", "k3", "w", "weight"):
+            np.testing.assert_allclose(c[key], o[key], rtol=1e-11, atol=1e-13, err_msg=f"{case} {key}")
+        if math.isinf(o["rev_kl"]):
+            assert c["rev_kl"] == o["rev_kl"]
+        else:
+            np.testing.assert_allclose(c["rev_kl"], o["rev_kl"], rtol=1e-11, atol=1e-13)
+        cases += 1
+    assert cases == 48
+
+
 def test_bf16_page_facts():
     with open(os.path.join(GOLDEN, "bf16_page_facts.json")) as f:
         facts = json.load(f)
