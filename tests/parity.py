@@ -50,7 +50,8 @@ in fp32, and the two-call path hands it over as an fp32 number: its relative
 error is a few 2^-24, and rho carries it.  Where rho p_k is large, c_k and the
 loss carry that error times rho p_k, beyond what abs 1e-6 and abs 1e-4 allow;
 their bars add it at RHO_REL = 2^-21.  Where rho p_k <= 2 (every row whose
-tail is not far smaller than 1 - Q_H) the added term is below 1e-6.
+tail is not far smaller than 1 - Q_H) the added term is below 1e-6, and below
+the clamp (tau < 1e-6) rho has no such error and nothing is added.
 
 Extra signals, beyond the stated bar: entropy abs 1e-5 + rel 1e-6; the
 importance ratio w and the weight rel 1e-6, or one fp32 spacing of the value
@@ -200,8 +201,11 @@ def check_row(tag, g, o, A=1.0, T=1.0, n_valid=1, mode=O.MODE_DLOGITS,
     close("rho", st[5], o["rho"], 1e-5 * abs(o["rho"]))
     close("S", st[6], o["S"], 1e-6)
     p_h = np.exp(np.asarray(o["head_logp"], np.float64))
+    # rho's error comes from tau's; below the clamp (tau < 1e-6, taken with a
+    # margin for tau's own error) rho = max(1 - Q_H, 1e-6) / 1e-6 has none
+    rho_rel = RHO_REL if o["tau"] >= 0.5e-6 else 0.0
     close("coef", g["coef"], o["coef"],
-          f32_tol(o["coef"], 1e-6) + RHO_REL * np.abs(o["rho"] * p_h))
+          f32_tol(o["coef"], 1e-6) + rho_rel * np.abs(o["rho"] * p_h))
     if rlp is not None:
         close("w", st[12], o["w"], f32_rel(o["w"], REL_W))
     wt, boundary = _gpu_weight(o, st[12], is_mode, is_lo, is_hi)
@@ -209,7 +213,7 @@ def check_row(tag, g, o, A=1.0, T=1.0, n_valid=1, mode=O.MODE_DLOGITS,
     close("weight", st[13], wt, f32_rel(wt, rel_wt) if rel_wt else 0.0)
     bracket = o["logp_a"] - (float(np.sum(o["coef"] * o["head_logp"])) if centering else 0.0)
     loss = -A * wt * bracket
-    rho_loss = (abs(A * wt) * RHO_REL * abs(o["rho"]) *
+    rho_loss = (abs(A * wt) * rho_rel * abs(o["rho"]) *
                 float(np.sum(p_h * np.abs(o["head_logp"]))) if centering else 0.0)
     close("loss", st[7], loss, f32_tol(loss, 1e-4) + rho_loss)
     close("tv", st[8], o["tv"], 1e-6)

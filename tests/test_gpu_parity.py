@@ -829,17 +829,35 @@ def test_many_rows_one_workgroup_each():
 @pytest.mark.parametrize("V", [1, 2, 7, 8, 9, 17])
 def test_tiny_vocabularies(V):
     """Degenerate row lengths: fewer elements than one 16-byte vector, exactly
-    one, one plus a partial one; K up to V (K = V makes the tail empty)."""
+    one, one plus a partial one; K up to V (K = V makes the tail empty).
+    Fused and two-call paths, fp32 and bf16 rows, T = 1 and 0.7.  With V = 1
+    the sampled entry e_a - p_a is exactly 0, and the two-call path's is the
+    rounding of the log-sum-exp it is handed."""
     for K in sorted({1, min(V, 3), V}):
-        say(f"tiny vocabulary V={V} K={K}")
-        d, z = crafted(16, V, K, seed=V * 7 + K, dtype="f32")
-        adv = torch.linspace(-1.0, 1.0, 4, device=DEV)
-        n_valid = sc.count_valid(d["resp_idx"])
-        out = run_correct(d, adv, n_valid, 1.0, O.MODE_SCORE, "f32")
-        torch.cuda.synchronize()
-        assert int(out["status"].item()) == 0
-        check_rows(f"tiny V={V} K={K}", d, out, np.arange(16), adv.cpu().numpy(), 16, 1.0,
-                   O.MODE_SCORE, "f32", logits_h=z)
+        for T, out_dtype, two_call in ((1.0, "f32", False), (0.7, "bf16", False),
+                                       (0.7, "bf16", True), (1.0, "f32", True)):
+            tag = f"tiny V={V} K={K} T={T} {out_dtype} two_call={two_call}"
+            say(tag)
+            d, z = crafted(16, V, K, seed=V * 7 + K, dtype="f32")
+            adv = torch.linspace(-1.0, 1.0, 4, device=DEV)
+            n_valid = sc.count_valid(d["resp_idx"])
+            if not two_call:
+                out = run_correct(d, adv, n_valid, T, O.MODE_SCORE, out_dtype)
+            else:
+                out = sc.logprobs(d["logits"], d["head_ids"], d["sampled"], d["resp_idx"],
+                                  temperature=T)
+                row_out = torch.empty(16, V, device=DEV,
+                                      dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32)
+                out["status"] = torch.zeros(1, dtype=torch.int32, device=DEV)
+                sc.center(out, d["head_ids"], d["head_probs"], d["sampled"], d["resp_idx"], adv,
+                          temperature=T, n_valid=n_valid, rollout_logp=d["rollout_logp"],
+                          logits=d["logits"], row_out=row_out, row_mode=O.MODE_SCORE,
+                          dev_status=out["status"])
+                out["row"] = row_out
+            torch.cuda.synchronize()
+            assert int(out["status"].item()) == 0
+            check_rows(tag, d, out, np.arange(16), adv.cpu().numpy(), 16, T, O.MODE_SCORE,
+                       out_dtype, logits_h=z)
 
 
 def test_seeded_random_shapes():

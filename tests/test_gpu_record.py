@@ -217,6 +217,29 @@ def test_record_tiny_vocabularies(V):
         check(f"tiny V={V} k={k}", z, 1.0, k, sampled, out)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_record_flat_rows_full_vocabulary(dtype):
+    """Near-flat rows over the full 248,320-id vocabulary (every logit 0.25,
+    one in fifty 1.0, padded rows): each thread of a row sums ~1,000
+    comparable terms, the case that asks most of the row sum's precision.
+    Ids exact (many ties: the exact fallback), probabilities and the sampled
+    log-probability at their bars, for k = 2 and k = 128."""
+    V, n = 248_320, 4
+    rng = np.random.default_rng(91)
+    z = np.full((n, V), 0.25, np.float32)
+    for r in range(n):
+        z[r, rng.integers(0, V, V // 50)] = 1.0
+    sampled = rng.integers(0, V, n).astype(np.int32)
+    buf = torch.zeros(n, V + 3, dtype=dtype, device=DEV)
+    buf[:, :V] = torch.from_numpy(z).to(DEV).to(dtype)
+    zt = buf[:, :V]
+    for k in (2, 128):
+        say(f"record flat rows V={V} k={k} {dtype}")
+        out = sc.record(zt, k, sampled=torch.from_numpy(sampled).to(DEV))
+        torch.cuda.synchronize()
+        check(f"flat V={V} k={k}", host(zt), 1.0, k, sampled, out)
+
+
 def test_record_seeded_random_shapes():
     """24 seeded draws of (rows, V, k, dtype, stride, T), every row against
     the oracle."""
