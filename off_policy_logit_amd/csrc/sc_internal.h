@@ -24,7 +24,7 @@ namespace sc {
 #define SC_CENTER_BLOCK 256
 #endif
 #ifndef SC_CENTER_TILE
-#define SC_CENTER_TILE 8
+#define SC_CENTER_TILE 4
 #endif
 #ifndef SC_CENTER_WAVES
 #define SC_CENTER_WAVES 3
