@@ -159,8 +159,13 @@ int sc_logprobs(const void* logits, int logits_dtype, int64_t n_rows,
  * generated-token reduction with padding masked; rollout_corr/k3_kl.
  * Reads row_stats columns LSE, LSE_LO, LOGP_A, TAIL and row_idx / head_logp as
  * written by sc_logprobs (or sc_logprobs_lmhead) on the same rows; writes
- * columns P_H .. K3 and W .. REV_KL.  With row_out, the row maximum is read
- * back from the logits at the recorded argmax.
+ * columns P_H .. K3 and W .. REV_KL.  When logits are given, log p and p at
+ * the recorded ids and log p(a) are formed in float64 from the logits at
+ * those ids and LSE + LSE_LO (head_logp and LOGP_A then serve only where an
+ * id is out of range); without logits they come from head_logp and LOGP_A,
+ * fp32 numbers, whose rounding c = q - rho p carries times rho p where rho is
+ * large.  With row_out, the row maximum is read back from the logits at the
+ * recorded argmax.
  * When row_out is not NULL the logits are streamed once more to write it.
  *
  *   logits, logits_dtype, row_stride   as for sc_logprobs; may be NULL when
