@@ -228,6 +228,16 @@ static void rows(int cases, uint64_t seed0, const char* out = nullptr) {
                      rlp.data(), resp.data(), adv.data(), n, T, &nv, stats.data(), idx.data(),
                      hl.data(), coef.data(), outp, out_dtype, stride, mode, SC_IS_NONE, 0.5f, 2.f,
                      1, &status, nullptr), SC_OK);
+    // the centering alone: with the logits (read at the recorded and sampled
+    // ids only) and without them
+    EXPECT(sc_center(logits, dtype, n, V, stride, ids.data(), q.data(), K, sampled.data(),
+                     rlp.data(), resp.data(), adv.data(), n, T, &nv, stats.data(), idx.data(),
+                     hl.data(), coef.data(), nullptr, out_dtype, stride, mode, SC_IS_NONE, 0.5f,
+                     2.f, 1, &status, nullptr), SC_OK);
+    EXPECT(sc_center(nullptr, dtype, n, V, stride, ids.data(), q.data(), K, sampled.data(),
+                     rlp.data(), resp.data(), adv.data(), n, T, &nv, stats.data(), idx.data(),
+                     hl.data(), coef.data(), nullptr, out_dtype, stride, mode, SC_IS_NONE, 0.5f,
+                     2.f, 1, &status, nullptr), SC_OK);
     printf("rows case %d: n=%d V=%d K=%d in=%d out=%d mode=%d pad=%d T=%g status %u\n", c, n, V,
            K, dtype, out_dtype, mode, pad, T, status);
   }
