@@ -1,5 +1,5 @@
 """Builds the host harness (tests/host/harness.cpp): the library's C ABI and
-its row and LM-head kernels compiled for the CPU against the emulated device
+its row, LM-head and recorder kernels compiled for the CPU against the emulated device
 environment in tests/host/hip, with AddressSanitizer and
 UndefinedBehaviorSanitizer (host code only: no GPU code is built here).
 
