@@ -43,6 +43,9 @@ namespace {
 #ifndef SC_RECORD_TILE
 #define SC_RECORD_TILE 4
 #endif
+#ifndef SC_RECORD_WAVES
+#define SC_RECORD_WAVES 4
+#endif
 constexpr int kRB = SC_RECORD_BLOCK;     // threads per workgroup
 constexpr int kRNW = kRB / kWave;        // waves
 constexpr int kHBits = 12;               // histogram bits of the key
@@ -81,7 +84,7 @@ SC_DEV int lane_rank(unsigned long long bal) {
 // At most 128 VGPRs (four waves per SIMD): the row stream, the hot loop,
 // stays free of spills; the rare paths (fallback passes, sort) may spill.
 template <typename T, bool VECTOR>
-__global__ __launch_bounds__(kRB) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(kRB) __attribute__((amdgpu_waves_per_eu(SC_RECORD_WAVES)))
 void k_record(RecParams P) {
   using IO = RowIO<T, VECTOR>;
   using Raw = typename IO::raw;
