@@ -211,28 +211,24 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
   const int V = (int)P.vocab;
 
   // Loader: thread t moves 16 bytes of rows (t >> 3) + 64 j, j < 4, of each
-  // operand per stage.  Rows past the end read row 0 of the tile (valid
-  // memory); their results are masked or never written.
+  // operand per stage, through one buffer resource per operand tile, the
+  // whole offset in the per-lane operand (the range check covers it; a
+  // scalar offset would not be checked).  Rows past the end lie beyond the
+  // resource and read zeros; their results are masked or never written.
+  // (The host keeps 256 rows of either operand below 2^31 bytes.)
   constexpr int kLJ = kTV * kKB * 2 / 16 / kB;  // 16-byte loads per operand
   constexpr int kRS = kB / 8;                    // rows covered by one load round
   const int lrow = t >> 3, lcol = t & 7;
-  const char* xb = reinterpret_cast<const char*>(P.x) + p0 * P.xs * 2;
-  uint32_t xoff[kLJ];
-#pragma unroll
-  for (int j = 0; j < kLJ; ++j) {
-    const int r = lrow + kRS * j;
-    xoff[j] = (uint32_t)(((p0 + r < P.n_rows) ? r : 0) * P.xs * 2 + lcol * 16);
-  }
-  uint32_t woff[kLJ];
-  const char* wb = nullptr;
+  const uint32_t xlane = (uint32_t)(lrow * P.xs * 2 + lcol * 16);
+  const uint32_t wlane = (uint32_t)(lrow * P.ws * 2 + lcol * 16);
+  const uint32_t xstep = (uint32_t)(kRS * P.xs * 2), wstep = (uint32_t)(kRS * P.ws * 2);
+  const int64_t xrows = P.n_rows - p0 < kTP ? P.n_rows - p0 : kTP;
+  const rsrc_t rx = make_rsrc(P.x + p0 * P.xs, (uint32_t)(xrows * P.xs * 2));
+  rsrc_t rw = make_rsrc(P.w, 0u);
   auto set_chunk_rows = [&](int ck) {
     const int64_t v0 = (int64_t)ck * kTV;
-    wb = reinterpret_cast<const char*>(P.w) + v0 * P.ws * 2;
-#pragma unroll
-    for (int j = 0; j < kLJ; ++j) {
-      const int r = lrow + kRS * j;
-      woff[j] = (uint32_t)(((v0 + r < V) ? r : 0) * P.ws * 2 + lcol * 16);
-    }
+    const int64_t rows = V - v0 < kTV ? V - v0 : kTV;
+    rw = make_rsrc(P.w + v0 * P.ws, (uint32_t)(rows * P.ws * 2));
   };
 
   u32x4 ra[kLJ], rb[kLJ];
@@ -240,11 +236,11 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
     const int ks = g % ST;
     const int ck = c_begin + g / ST;
     if (ks == 0) set_chunk_rows(ck);
-    const int kb = ks * kKB * 2;
+    const uint32_t kb = (uint32_t)(ks * kKB * 2);
 #pragma unroll
     for (int j = 0; j < kLJ; ++j) {
-      ra[j] = *reinterpret_cast<const u32x4*>(wb + woff[j] + kb);
-      rb[j] = *reinterpret_cast<const u32x4*>(xb + xoff[j] + kb);
+      ra[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, wlane + j * wstep + kb, 0, 0);
+      rb[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xlane + j * xstep + kb, 0, 0);
     }
   };
   auto store = [&](int buf) {
