@@ -81,8 +81,9 @@ SC_DEV int lane_rank(unsigned long long bal) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
 }
 
-// At most 128 VGPRs (four waves per SIMD): the row stream, the hot loop,
-// stays free of spills; the rare paths (fallback passes, sort) may spill.
+// At four waves per SIMD (the default), at most 128 VGPRs: the row stream,
+// the hot loop, stays free of spills; the rare paths (fallback passes, sort)
+// may spill.
 template <typename T, bool VECTOR>
 __global__ __launch_bounds__(kRB) __attribute__((amdgpu_waves_per_eu(SC_RECORD_WAVES)))
 void k_record(RecParams P) {
