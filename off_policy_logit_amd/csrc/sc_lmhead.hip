@@ -503,15 +503,18 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
           word |= nv <= 0 ? 0xffffffffu : (nv >= 32 ? 0u : ~((1u << nv) - 1u));
         }
         const uint32_t wh = word >> (4 * h);
-        // 2^(z c - E), z c = z c_hi + z c_lo; summed pairwise
+        // 2^(z c - E), z c = z c_hi + z c_lo; summed pairwise.  A recorded
+        // id's exponent is replaced by -2^100 first, which makes its term and
+        // its entropy product exactly 0 (one select instead of two).
         float e16[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float y = fmaf(acc[bi][j][i], c_lo, fmaf(acc[bi][j][i], c_hi, -E));
-          const float e = exp2_fast(y);
           const bool ex = (wh >> (8 * (i >> 2) + (i & 3))) & 1u;
-          e16[i] = ex ? 0.f : e;
-          h_acc += ex ? 0.f : e * y;
+          const float y0 = fmaf(acc[bi][j][i], c_lo, fmaf(acc[bi][j][i], c_hi, -E));
+          const float y = ex ? -0x1p100f : y0;
+          const float e = exp2_fast(y);
+          e16[i] = e;
+          h_acc = fmaf(e, y, h_acc);
         }
 #pragma unroll
         for (int w = 1; w < 16; w <<= 1)
