@@ -360,31 +360,17 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
   auto epilogue = [&](int ck) {
     const int v0 = ck * kTV;
     if (MODE == 2) {
-      if (P.dzt) {
-        // transposed copy: dzt[v][p]; lanes hold consecutive rows p, so each
-        // store instruction writes 64 contiguous bytes per id; rows past
-        // n_rows (up to dzt_cols) are written as 0
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int64_t p = p0 + wp * kWR + j * 32 + lc;
-          if (p >= P.dzt_cols) continue;
-          const bool live = p < P.n_rows;
-#pragma unroll
-          for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int v = v0 + wv * 128 + bi * 32 + lm_row(i, h);
-              if (v >= V) continue;
-              const float y = p2_value<true>(acc[bi][j][i], dzq[j]);
-              P.dzt[(int64_t)v * P.dzts + p] = live ? (uint16_t)f32_to_bf16(y) : (uint16_t)0;
-            }
-        }
-      }
+      // each value is formed and rounded to bf16 once, then stored to the
+      // row-major dLogits and, when asked, to the transposed copy dzt[v][p]
+      // (lanes hold consecutive rows p, so each transposed store instruction
+      // writes 64 contiguous bytes per id; rows past n_rows, up to dzt_cols,
+      // are written there as 0)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int64_t p = p0 + wp * kWR + j * 32 + lc;
-        if (p >= P.n_rows) continue;
-        uint16_t* orow = P.dz + p * P.dzs;
+        const bool live = p < P.n_rows;
+        const bool tcol = P.dzt != nullptr && p < P.dzt_cols;
+        if (!live && !tcol) continue;
 #pragma unroll
         for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
@@ -394,15 +380,23 @@ __global__ __launch_bounds__(kB) void k_lm_main(LmParams P) {
             float x[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = p2_value<true>(acc[bi][j][4 * g4 + e], dzq[j]);
+            u32x2 wv2;
+            wv2[0] = live ? pack_bf16x2(x[0], x[1]) : 0u;
+            wv2[1] = live ? pack_bf16x2(x[2], x[3]) : 0u;
+            if (tcol) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (v + e < V)
+                  P.dzt[(int64_t)(v + e) * P.dzts + p] = (uint16_t)(wv2[e >> 1] >> (16 * (e & 1)));
+            }
+            if (!live) continue;
+            uint16_t* orow = P.dz + p * P.dzs;
             if (v + 3 < V) {
-              u32x2 wv2;
-              wv2[0] = pack_bf16x2(x[0], x[1]);
-              wv2[1] = pack_bf16x2(x[2], x[3]);
               *reinterpret_cast<u32x2*>(orow + v) = wv2;
             } else {
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                if (v + e < V) orow[v + e] = (uint16_t)f32_to_bf16(x[e]);
+                if (v + e < V) orow[v + e] = (uint16_t)(wv2[e >> 1] >> (16 * (e & 1)));
                 else if (v + e < P.dz_cols) orow[v + e] = 0;
               }
             }
